@@ -1,0 +1,86 @@
+"""Byte-level model of the static ring-buffer KV cache.
+
+Test infrastructure (see ``oracle/__init__``).
+
+Reference: "Reflex: Real-Time VLA Control through Streaming Inference" paper
+review:
+* §3 Architecture, ring-buffer diagram and Eq. 1 text: a pinned instruction
+  prefix computed once at t = 0, then a sliding FIFO window where each frame
+  enqueues the newest frame and evicts the oldest;
+* §3 component table: buffer_k is num_layers x max_seq_len x num_heads x
+  head_dim in BF16, allocated statically so no allocation happens later;
+* §5 Code analysis: the buffers are created zeroed next to a write pointer
+  ``ptr = 0``; ``add_new_prefix`` adds the new observation and reports the
+  eviction; ``evict_source_prefix`` removes the oldest frame from all layers.
+
+Readings taken:
+* the pin occupies tokens [0, P) of the same buffer, so max_seq_len = P + W*F;
+* ``ptr`` is a slot index that advances by one per frame, modulo W;
+* a push overwrites slot ``head`` in every layer (that overwrite *is* the
+  eviction of the frame pushed W frames earlier) and nothing else moves.
+
+The model stores raw words (``uint16`` for bf16 bits, ``uint32`` for fp32
+bits) so that device buffers can be compared with ``array_equal``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+class RingModel:
+    """Expected contents and metadata of the ring after each call."""
+
+    def __init__(self, num_layers, num_kv_heads, head_dim, pin_capacity, num_slots,
+                 tokens_per_frame, word_dtype=np.uint16):
+        if min(num_layers, num_kv_heads, head_dim, num_slots, tokens_per_frame) <= 0 or pin_capacity < 0:
+            raise ValueError("ring dimensions must be positive (pin capacity >= 0)")
+        self.L, self.Hkv, self.D = num_layers, num_kv_heads, head_dim
+        self.P, self.W, self.F = pin_capacity, num_slots, tokens_per_frame
+        self.max_seq_len = self.P + self.W * self.F
+        shape = (self.L, self.max_seq_len, self.Hkv, self.D)
+        self.k = np.zeros(shape, dtype=word_dtype)   # zeroed at creation (§5 code)
+        self.v = np.zeros(shape, dtype=word_dtype)
+        self.head = 0          # next slot to write (the page's ``ptr``)
+        self.count = 0         # valid slots, saturates at W
+        self.pinned = 0        # pinned prefix tokens
+        self.frames_pushed = 0
+        self.slot_frame = [-1] * self.W   # which frame id sits in each slot
+
+    # -- the pinned prefix: written once, at t = 0 ---------------------------
+    def pin(self, k_words: np.ndarray, v_words: np.ndarray) -> None:
+        """Write ``[L][n][Hkv][D]`` into tokens [0, n) of every layer, once."""
+        n = k_words.shape[1]
+        if self.pinned:
+            raise RuntimeError("prefix already pinned")
+        if n > self.P:
+            raise ValueError("prefix longer than the pin capacity")
+        self.k[:, :n] = k_words
+        self.v[:, :n] = v_words
+        self.pinned = n
+
+    # -- one frame: enqueue newest, evict oldest ------------------------------
+    def push(self, k_words: np.ndarray, v_words: np.ndarray) -> int:
+        """Overwrite slot ``head``; return the evicted frame id or -1."""
+        slot = self.head
+        lo = self.P + slot * self.F
+        self.k[:, lo:lo + self.F] = k_words
+        self.v[:, lo:lo + self.F] = v_words
+        evicted = self.slot_frame[slot]
+        self.slot_frame[slot] = self.frames_pushed
+        self.frames_pushed += 1
+        self.head = (self.head + 1) % self.W
+        self.count = min(self.count + 1, self.W)
+        return evicted
+
+    # -- views used by the attention oracle -----------------------------------
+    def window_frames(self) -> list[int]:
+        """Frame ids in the window, oldest first (FIFO order)."""
+        return [f for f in range(max(0, self.frames_pushed - self.W), self.frames_pushed)]
+
+    def slot_of(self, frame_id: int) -> int:
+        return frame_id % self.W
+
+    def state(self) -> dict:
+        return {"head": self.head, "count": self.count, "pinned": self.pinned,
+                "frames_pushed": self.frames_pushed}
