@@ -1,0 +1,246 @@
+/*
+ * pattn.h -- C ABI of the partitioned-attention library for MI355X (gfx950).
+ *
+ * One operation sits at the centre: the dynamic-suffix queries of a
+ * flow-matching denoising step attend over three KV regions, a pinned
+ * instruction prefix, a sliding window of visual frames held in a static ring
+ * buffer, and the step's own freshly computed suffix KV ("Reflex: Real-Time
+ * VLA Control through Streaming Inference" paper review, §3 Architecture,
+ * Eq. 1). Around it: the ring buffer itself (§3 component table; §5 Code
+ * analysis), AdaRMSNorm with its conditioning MLP (§3 Eq. 2; §5 module), the
+ * packed QKV projection it feeds (§2/§4: a packed-QKV kernel is one of the
+ * fused operators), and the shared-KV decode readers of the OxyGen review
+ * ("OxyGen: Unified KV Cache Management for Vision-Language-Action Models
+ * under Multi-Task Parallelism", core method and method details).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a caller-owned DEVICE pointer, dense, in the
+ *   row-major layout written next to it ([a][b][c] means c is contiguous).
+ *   It must stay valid until the work queued on `stream` has finished.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every call only enqueues work; nothing synchronises the device.
+ * - bf16 tensors hold raw bfloat16 words; "f32" tensors IEEE binary32.
+ * - No entry point allocates device memory. Scratch space is passed in as
+ *   `workspace` (device, 256-byte aligned) and sized by the matching
+ *   *_workspace_bytes query; its contents need no initialisation.
+ * - Arguments are validated before any launch. On failure nothing is
+ *   enqueued, a status other than PA_OK is returned and pa_last_error()
+ *   describes it. No C++ exception ever crosses this boundary.
+ * - Handles are not thread-safe: one host thread per rb_ring at a time.
+ */
+#ifndef PATTN_H
+#define PATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_EINVAL = 1,     /* null pointer, bad enum, negative size, bad scale */
+    PA_ESHAPE = 2,     /* sizes inconsistent with the ring or each other   */
+    PA_ESTATE = 3,     /* call not allowed in the ring's current state     */
+    PA_EDEVICE = 4,    /* a HIP runtime call failed                        */
+    PA_ERANGE = 5      /* workspace too small, or a limit exceeded         */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/* ========================================================================
+ * Ring buffer (Reflex review §3 ring-buffer diagram and component table,
+ * §5 ring-buffer initialisation): two zero-initialised static buffers
+ *     K, V : [num_layers][P + W*F][num_kv_heads][head_dim]
+ * Tokens [0, P) hold the pinned prefix; slot s (0 <= s < W) holds tokens
+ * [P + s*F, P + (s+1)*F). Frame f is written to slot f mod W, so a push
+ * overwrites the frame pushed W frames earlier: that overwrite is the
+ * eviction. The library never reallocates or moves the buffers.
+ * ====================================================================== */
+typedef struct {
+    int32_t num_layers;        /* L  > 0 */
+    int32_t num_kv_heads;      /* Hkv > 0 */
+    int32_t head_dim;          /* D, a multiple of 8, <= 256 */
+    int32_t pin_capacity;      /* P >= 0 */
+    int32_t num_slots;         /* W > 0: frames in the sliding window */
+    int32_t tokens_per_frame;  /* F > 0 */
+    int32_t dtype;             /* pa_dtype of the K/V words */
+} rb_config;
+
+typedef struct {
+    int32_t head;              /* slot the next push writes */
+    int32_t count;             /* valid slots, min(frames_pushed, W) */
+    int32_t pinned;            /* pinned prefix tokens (0 until rb_pin_prefix) */
+    int32_t reserved;
+    int64_t frames_pushed;
+} rb_state;
+
+typedef struct rb_ring rb_ring;   /* opaque; host-side metadata only */
+
+/* Bind two caller-owned, zeroed device buffers of the layout above.
+ * The handle borrows the buffers; rb_destroy frees only the handle.
+ * PA_EINVAL: null argument or bad dtype; PA_ESHAPE: non-positive sizes. */
+pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, rb_ring** out);
+pa_status rb_destroy(rb_ring* ring);
+
+/* Copy the prefix K/V, [L][n_tokens][Hkv][D], into tokens [0, n_tokens) of
+ * every layer. Allowed once (PA_ESTATE on a second call); n_tokens <= P
+ * (PA_ESHAPE otherwise). The prefix is computed once, at t = 0 (Eq. 1 text). */
+pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, int32_t n_tokens, void* stream);
+
+/* Enqueue one frame, K/V [L][F][Hkv][D]: one strided device copy into slot
+ * `head` of every layer, then head = (head+1) mod W and count = min(count+1, W)
+ * on the host. O(1) in the window length; no allocation.
+ * *evicted_frame (nullable) receives the id of the frame overwritten, or -1. */
+pa_status rb_push_frame(rb_ring* ring, const void* k, const void* v, void* stream,
+                        int64_t* evicted_frame);
+
+pa_status rb_get_state(const rb_ring* ring, rb_state* out);
+
+/* ========================================================================
+ * Partitioned attention (Reflex review §3 Eq. 1; Prop. A.1):
+ *     out = softmax(scale * Q [K_pin; K_slide; K_dyn]^T) [V_pin; V_slide; V_dyn]
+ * for every dynamic-suffix token and query head, for layers
+ * [layer_begin, layer_begin + num_layers) of the ring.
+ * The cached regions are read in place: tokens [0, pinned) and the valid
+ * slots [P, P + count*F) in physical slot order (softmax does not depend on
+ * the order of its keys, Prop. A.1). Query head h reads KV head
+ * floor(h / (n_q_heads / num_kv_heads)). The cached keys are split across
+ * workgroups; each split yields a partial (max, sum, acc) that a
+ * log-sum-exp combine merges in FP32. bf16 rings use bf16 MFMA with FP32
+ * accumulation; f32 rings use FP32 vector arithmetic throughout.
+ * ====================================================================== */
+typedef struct {
+    int32_t layer_begin;
+    int32_t num_layers;        /* Lb >= 1 */
+    int32_t n_q_heads;         /* Hq, a multiple of Hkv */
+    int32_t n_dyn;             /* N >= 1 dynamic-suffix tokens */
+    float   scale;             /* the 1/sqrt(d) of Eq. 1, applied once */
+    int32_t out_dtype;         /* PA_F32 or PA_BF16 */
+    int32_t num_splits;        /* KV splits per layer; 0 = library's choice */
+} pattn_args;
+
+/* Workspace needed by pattn_step for these arguments (0 on invalid input). */
+size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* args);
+
+/* q     [Lb][N][Hq][D]    ring dtype
+ * k_dyn [Lb][N][Hkv][D]   ring dtype: K_dyn(k) of this step
+ * v_dyn [Lb][N][Hkv][D]   ring dtype
+ * out   [Lb][N][Hq][D]    args->out_dtype
+ * PA_ESTATE: the ring holds no cached token yet and n_dyn keys alone are
+ * allowed, so this is only raised for an unpinned ring with P > 0 and no frame.
+ * PA_ERANGE: ws_bytes < pattn_workspace_bytes(). */
+pa_status pattn_step(const rb_ring* ring, const pattn_args* args, const void* q,
+                     const void* k_dyn, const void* v_dyn, void* out,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ========================================================================
+ * Shared-KV decode readers (OxyGen review, core method and method
+ * details): G decode streams, one query token each, read the same cached
+ * regions as the action suffix plus a private tail of their own appended
+ * tokens, which no other reader sees.
+ *   tail_k, tail_v : [Lb][G][tail_capacity][Hkv][D]   ring dtype
+ *   tail_len       : [G] int32 (device): valid tail tokens per stream
+ * ====================================================================== */
+typedef struct {
+    int32_t layer_begin;
+    int32_t num_layers;
+    int32_t n_q_heads;
+    int32_t n_streams;         /* G >= 1 */
+    int32_t tail_capacity;     /* >= 1 */
+    float   scale;
+    int32_t out_dtype;
+    int32_t num_splits;        /* 0 = library's choice */
+} pattn_decode_args;
+
+/* Append one token per stream, k_new/v_new [Lb][G][Hkv][D], at index
+ * tail_len[g] of every layer, then tail_len[g] += 1 (on the device).
+ * A stream whose tail is full is left unchanged and its bit is set in
+ * *overflow_mask (device uint32, nullable; bit g%32). Retire a stream by
+ * setting its tail_len to 0. */
+pa_status pattn_append_private(const rb_ring* ring, const pattn_decode_args* args,
+                               void* tail_k, void* tail_v, int32_t* tail_len,
+                               const void* k_new, const void* v_new,
+                               uint32_t* overflow_mask, void* stream);
+
+size_t pattn_decode_workspace_bytes(const rb_ring* ring, const pattn_decode_args* args);
+
+/* q [Lb][G][Hq][D]; out [Lb][G][Hq][D]. Each stream attends over
+ * [pin; window; its own tail[0, tail_len[g])]. */
+pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* args, const void* q,
+                       const void* tail_k, const void* tail_v, const int32_t* tail_len,
+                       void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ========================================================================
+ * AdaRMSNorm (Reflex review §3 Eq. 2 and component table; §5 module):
+ *     y = x / sqrt(mean(x^2) + eps) * gamma,   gamma = 1 + MLP(c),
+ *     c = [emb(t); state],  MLP = Linear(cond->hidden), SiLU, Linear(hidden->model)
+ * emb(t) is the 128-wide sinusoid [sin(t w_i)] ++ [cos(t w_i)],
+ * w_i = 10000^(-i/64). The mean of squares is taken in FP32. The MLP runs on
+ * bf16 weights with c and the hidden activation rounded to bf16 and FP32
+ * accumulation; gamma is kept in FP32.
+ * ====================================================================== */
+typedef struct {
+    const void* w1;            /* bf16 [L][hidden][cond_emb + state_dim] */
+    const void* b1;            /* bf16 [L][hidden] */
+    const void* w2;            /* bf16 [L][model][hidden] */
+    const void* b2;            /* bf16 [L][model] */
+    int32_t num_layers;        /* L stacked MLPs (one per layer) */
+    int32_t cond_emb;          /* 128 */
+    int32_t state_dim;         /* s, 0 <= s <= 128 */
+    int32_t hidden_dim;        /* multiple of 64 */
+    int32_t model_dim;         /* multiple of 64 */
+} ada_mlp;
+
+size_t ada_gamma_workspace_bytes(const ada_mlp* mlp, int32_t n_t);
+
+/* gamma[l][i][:] = 1 + MLP_l([emb(t[i]); state]) for every layer l and
+ * timestep i (a frame's ten steps in one call). t: HOST array [n_t];
+ * state: device bf16 [state_dim]; gamma: device f32 [L][n_t][model_dim]. */
+pa_status ada_gamma(const ada_mlp* mlp, const float* t, int32_t n_t, const void* state,
+                    float* gamma, void* workspace, size_t ws_bytes, void* stream);
+
+/* The whole of Eq. 2 for one layer's MLP (layer index `layer` of mlp) and one t:
+ * x bf16 [rows][model_dim] -> y [rows][model_dim] in y_dtype. `workspace`
+ * as sized by ada_rmsnorm_workspace_bytes. *nonfinite (device, nullable)
+ * gets bit 0 set if any output is NaN or Inf. */
+size_t ada_rmsnorm_workspace_bytes(const ada_mlp* mlp);
+pa_status ada_rmsnorm(const void* x, int32_t rows, const ada_mlp* mlp, int32_t layer, float t,
+                      const void* state, float eps, void* y, int32_t y_dtype,
+                      uint32_t* nonfinite, void* workspace, size_t ws_bytes, void* stream);
+
+/* AdaRMSNorm with a precomputed gamma (f32 [model_dim]) fused into the
+ * packed QKV projection:
+ *     y = bf16(x / sqrt(mean(x^2)+eps) * gamma);  [q|k|v] = y W_qkv^T
+ * x bf16 [rows][model_dim]; w_qkv bf16 [(Hq + 2 Hkv) * D][model_dim]
+ * (nn.Linear layout: q heads, then k heads, then v heads);
+ * q bf16 [rows][Hq][D], k_dyn and v_dyn bf16 [rows][Hkv][D].
+ * rows <= 64; model_dim a multiple of 256; D a multiple of 32. */
+size_t ada_rmsnorm_qkv_workspace_bytes(int32_t rows, int32_t model_dim);
+pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const float* gamma,
+                          float eps, const void* w_qkv, int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, void* q, void* k_dyn, void* v_dyn,
+                          uint32_t* nonfinite, void* workspace, size_t ws_bytes, void* stream);
+
+/* ========================================================================
+ * Layer glue of the denoising stack (not on the pages; see the header of
+ * each reading in the design notes of the library):
+ *     h <- bf16(h + o W_o^T)                      (residual out-projection)
+ * and, when x is not NULL, the Euler update of the flow state
+ *     x <- bf16(x - dt * h)                       (v = last layer's stream)
+ * o bf16 [rows][in_dim]; w_o bf16 [model_dim][in_dim]; h, x bf16 [rows][model_dim].
+ * rows <= 64; in_dim a multiple of 256; model_dim a multiple of 32.
+ * ====================================================================== */
+pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, int32_t in_dim,
+                         int32_t model_dim, void* x, float dt, uint32_t* nonfinite, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATTN_H */

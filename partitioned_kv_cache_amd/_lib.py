@@ -1,0 +1,245 @@
+"""ctypes binding of libpattn.so: the C ABI of include/pattn.h, same names.
+
+Argument marshalling only: tensors become device pointers, the stream is
+torch's current stream unless one is given, and a non-OK status raises
+``PattnError`` with the library's message. Every computation runs in the
+HIP library. If the library is missing this module raises at import time;
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m partitioned_kv_cache_amd.build` "
+                      "(or __graft_entry__.build()); there is no CPU fallback")
+
+_lib = C.CDLL(LIB_PATH)
+
+PA_OK, PA_EINVAL, PA_ESHAPE, PA_ESTATE, PA_EDEVICE, PA_ERANGE = range(6)
+PA_F32, PA_BF16 = 0, 1
+STATUS_NAMES = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_ESHAPE", 3: "PA_ESTATE", 4: "PA_EDEVICE", 5: "PA_ERANGE"}
+
+# every symbol the header declares
+EXPORTS = (
+    "pa_last_error", "rb_create", "rb_destroy", "rb_pin_prefix", "rb_push_frame", "rb_get_state",
+    "pattn_workspace_bytes", "pattn_step", "pattn_append_private", "pattn_decode_workspace_bytes",
+    "pattn_decode", "ada_gamma_workspace_bytes", "ada_gamma", "ada_rmsnorm_workspace_bytes", "ada_rmsnorm",
+    "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual",
+)
+
+
+class PattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.pa_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+class RbConfig(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("pin_capacity", C.c_int32), ("num_slots", C.c_int32), ("tokens_per_frame", C.c_int32),
+                ("dtype", C.c_int32)]
+
+
+class RbState(C.Structure):
+    _fields_ = [("head", C.c_int32), ("count", C.c_int32), ("pinned", C.c_int32), ("reserved", C.c_int32),
+                ("frames_pushed", C.c_int64)]
+
+
+class PattnArgs(C.Structure):
+    _fields_ = [("layer_begin", C.c_int32), ("num_layers", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_dyn", C.c_int32), ("scale", C.c_float), ("out_dtype", C.c_int32), ("num_splits", C.c_int32)]
+
+
+class PattnDecodeArgs(C.Structure):
+    _fields_ = [("layer_begin", C.c_int32), ("num_layers", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_streams", C.c_int32), ("tail_capacity", C.c_int32), ("scale", C.c_float),
+                ("out_dtype", C.c_int32), ("num_splits", C.c_int32)]
+
+
+class AdaMlp(C.Structure):
+    _fields_ = [("w1", C.c_void_p), ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
+                ("num_layers", C.c_int32), ("cond_emb", C.c_int32), ("state_dim", C.c_int32),
+                ("hidden_dim", C.c_int32), ("model_dim", C.c_int32)]
+
+
+_vp, _i32, _f32, _sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype, f.argtypes = res, list(args)
+    return f
+
+
+_sig("pa_last_error", C.c_char_p)
+_sig("rb_create", _i32, C.POINTER(RbConfig), _vp, _vp, C.POINTER(_vp))
+_sig("rb_destroy", _i32, _vp)
+_sig("rb_pin_prefix", _i32, _vp, _vp, _vp, _i32, _vp)
+_sig("rb_push_frame", _i32, _vp, _vp, _vp, _vp, C.POINTER(C.c_int64))
+_sig("rb_get_state", _i32, _vp, C.POINTER(RbState))
+_sig("pattn_workspace_bytes", _sz, _vp, C.POINTER(PattnArgs))
+_sig("pattn_step", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("pattn_append_private", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp)
+_sig("pattn_decode_workspace_bytes", _sz, _vp, C.POINTER(PattnDecodeArgs))
+_sig("pattn_decode", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("ada_gamma_workspace_bytes", _sz, C.POINTER(AdaMlp), _i32)
+_sig("ada_gamma", _i32, C.POINTER(AdaMlp), C.POINTER(C.c_float), _i32, _vp, _vp, _vp, _sz, _vp)
+_sig("ada_rmsnorm_workspace_bytes", _sz, C.POINTER(AdaMlp))
+_sig("ada_rmsnorm", _i32, _vp, _i32, C.POINTER(AdaMlp), _i32, _f32, _vp, _f32, _vp, _i32, _vp, _vp, _sz, _vp)
+_sig("ada_rmsnorm_qkv_workspace_bytes", _sz, _i32, _i32)
+_sig("ada_rmsnorm_qkv", _i32, _vp, _i32, _i32, _vp, _f32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("oproj_residual", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _f32, _vp, _vp)
+
+
+def _check(st: int, where: str):
+    if st != PA_OK:
+        raise PattnError(st, where)
+
+
+def ptr(t) -> int | None:
+    """Device pointer of a tensor (or an int / None passed through)."""
+    if t is None or isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ----------------------------------------------------------------- ring ------
+
+class Ring:
+    """Handle over caller-owned K/V buffers [L][P + W*F][Hkv][D] (rb_*)."""
+
+    def __init__(self, cfg: RbConfig, k_buf, v_buf):
+        self.cfg = cfg
+        self.k_buf, self.v_buf = k_buf, v_buf        # keep the tensors alive
+        h = _vp()
+        _check(_lib.rb_create(C.byref(cfg), ptr(k_buf), ptr(v_buf), C.byref(h)), "rb_create")
+        self.handle = h.value
+
+    def close(self):
+        if self.handle:
+            _lib.rb_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pin_prefix(self, k, v, n_tokens: int, stream=None):
+        _check(_lib.rb_pin_prefix(self.handle, ptr(k), ptr(v), n_tokens, _stream(stream)), "rb_pin_prefix")
+
+    def push_frame(self, k, v, stream=None) -> int:
+        ev = C.c_int64(0)
+        _check(_lib.rb_push_frame(self.handle, ptr(k), ptr(v), _stream(stream), C.byref(ev)), "rb_push_frame")
+        return ev.value
+
+    def state(self) -> dict:
+        s = RbState()
+        _check(_lib.rb_get_state(self.handle, C.byref(s)), "rb_get_state")
+        return {"head": s.head, "count": s.count, "pinned": s.pinned, "frames_pushed": s.frames_pushed}
+
+
+def rb_config(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype) -> RbConfig:
+    return RbConfig(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype)
+
+
+# ------------------------------------------------------------ attention ------
+
+def pattn_args(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype=PA_F32, num_splits=0) -> PattnArgs:
+    return PattnArgs(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype, num_splits)
+
+
+def pattn_workspace_bytes(ring: Ring, args: PattnArgs) -> int:
+    return _lib.pattn_workspace_bytes(ring.handle, C.byref(args))
+
+
+def pattn_step(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, workspace, ws_bytes: int, stream=None):
+    _check(_lib.pattn_step(ring.handle, C.byref(args), ptr(q), ptr(k_dyn), ptr(v_dyn), ptr(out), ptr(workspace),
+                           ws_bytes, _stream(stream)), "pattn_step")
+
+
+def decode_args(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype=PA_F32,
+                num_splits=0) -> PattnDecodeArgs:
+    return PattnDecodeArgs(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype, num_splits)
+
+
+def pattn_append_private(ring: Ring, args: PattnDecodeArgs, tail_k, tail_v, tail_len, k_new, v_new,
+                         overflow=None, stream=None):
+    _check(_lib.pattn_append_private(ring.handle, C.byref(args), ptr(tail_k), ptr(tail_v), ptr(tail_len),
+                                     ptr(k_new), ptr(v_new), ptr(overflow), _stream(stream)), "pattn_append_private")
+
+
+def pattn_decode_workspace_bytes(ring: Ring, args: PattnDecodeArgs) -> int:
+    return _lib.pattn_decode_workspace_bytes(ring.handle, C.byref(args))
+
+
+def pattn_decode(ring: Ring, args: PattnDecodeArgs, q, tail_k, tail_v, tail_len, out, workspace, ws_bytes: int,
+                 stream=None):
+    _check(_lib.pattn_decode(ring.handle, C.byref(args), ptr(q), ptr(tail_k), ptr(tail_v), ptr(tail_len), ptr(out),
+                             ptr(workspace), ws_bytes, _stream(stream)), "pattn_decode")
+
+
+# ------------------------------------------------------------- adanorm -------
+
+def ada_mlp(w1, b1, w2, b2, num_layers, cond_emb, state_dim, hidden_dim, model_dim) -> AdaMlp:
+    m = AdaMlp(ptr(w1), ptr(b1), ptr(w2), ptr(b2), num_layers, cond_emb, state_dim, hidden_dim, model_dim)
+    m._keep = (w1, b1, w2, b2)
+    return m
+
+
+def ada_gamma_workspace_bytes(mlp: AdaMlp, n_t: int) -> int:
+    return _lib.ada_gamma_workspace_bytes(C.byref(mlp), n_t)
+
+
+def ada_gamma(mlp: AdaMlp, t: list[float], state, gamma, workspace, ws_bytes: int, stream=None):
+    arr = (C.c_float * len(t))(*t)
+    _check(_lib.ada_gamma(C.byref(mlp), arr, len(t), ptr(state), ptr(gamma), ptr(workspace), ws_bytes,
+                          _stream(stream)), "ada_gamma")
+
+
+def ada_rmsnorm_workspace_bytes(mlp: AdaMlp) -> int:
+    return _lib.ada_rmsnorm_workspace_bytes(C.byref(mlp))
+
+
+def ada_rmsnorm(x, rows: int, mlp: AdaMlp, layer: int, t: float, state, eps: float, y, y_dtype: int,
+                nonfinite, workspace, ws_bytes: int, stream=None):
+    _check(_lib.ada_rmsnorm(ptr(x), rows, C.byref(mlp), layer, t, ptr(state), eps, ptr(y), y_dtype,
+                            ptr(nonfinite), ptr(workspace), ws_bytes, _stream(stream)), "ada_rmsnorm")
+
+
+def ada_rmsnorm_qkv_workspace_bytes(rows: int, model_dim: int) -> int:
+    return _lib.ada_rmsnorm_qkv_workspace_bytes(rows, model_dim)
+
+
+def ada_rmsnorm_qkv(x, rows, model_dim, gamma, eps, w_qkv, n_q_heads, n_kv_heads, head_dim, q, k_dyn, v_dyn,
+                    nonfinite, workspace, ws_bytes, stream=None):
+    _check(_lib.ada_rmsnorm_qkv(ptr(x), rows, model_dim, ptr(gamma), eps, ptr(w_qkv), n_q_heads, n_kv_heads,
+                                head_dim, ptr(q), ptr(k_dyn), ptr(v_dyn), ptr(nonfinite), ptr(workspace), ws_bytes,
+                                _stream(stream)), "ada_rmsnorm_qkv")
+
+
+def oproj_residual(o, w_o, h, rows, in_dim, model_dim, x=None, dt=0.1, nonfinite=None, stream=None):
+    _check(_lib.oproj_residual(ptr(o), ptr(w_o), ptr(h), rows, in_dim, model_dim, ptr(x), dt, ptr(nonfinite),
+                               _stream(stream)), "oproj_residual")
+
+
+def raw():
+    """The ctypes CDLL itself (for the symbol-export test)."""
+    return _lib

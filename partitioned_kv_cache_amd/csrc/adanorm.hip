@@ -1,0 +1,388 @@
+// AdaRMSNorm, its conditioning MLP, and the two projections around attention.
+//
+// "Reflex: Real-Time VLA Control through Streaming Inference" paper review:
+// §3 Architecture, Eq. 2 -- AdaRMSNorm(x, c) = x / RMS(x) * gamma(c),
+// gamma(c) = 1 + MLP(c), RMS(x) = sqrt(mean(x^2) + eps), c = [sinusoidal
+// t_k; robot state]; the RMS is computed in FP32 and the gating MLP runs in
+// BF16. §3 component table -- MLP = Linear(cond -> hidden) -> SiLU ->
+// Linear(hidden -> model). §5 Code analysis -- the module squares x.float(),
+// averages over the last axis, scales by rsqrt(ms + eps), multiplies by
+// 1 + dense(cond). §2 / §4 -- a packed QKV kernel is one of the fused ops.
+//
+// Readings (the pages are silent): the embedding is the 128-wide sinusoid
+// [sin(t w_i)] ++ [cos(t w_i)], w_i = 10000^(-i/64); the Linear layers have
+// biases; c and the hidden activation are rounded to bf16 (the inputs of
+// bf16 Linear layers) and accumulation is FP32; gamma stays FP32; the
+// normalised row is rounded to bf16 once, as the input of the projection.
+//
+// gamma depends only on (t_k, state), so a frame's ten gammas per layer are
+// produced by one batched call before its denoising loop, and the per-step
+// kernels only read them.
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace pa {
+
+constexpr int MAX_T = 16;            // timesteps per ada_gamma call
+struct TArr { float t[MAX_T]; };
+
+__device__ __forceinline__ float wsum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ float bf_round(float v) { return bf2f(f2bf(v)); }
+
+// ------------------------------------------------------------- gamma MLP ----
+// Hidden layer: a[l][i][j] = bf16(SiLU(W1[l][j] . c_i + b1[l][j])), with
+// c_i = bf16([emb(t_i); state]).
+// grid (ceil(hidden / 256), L), block 256, dynamic LDS n_t * cond floats.
+__global__ __launch_bounds__(256) void gamma_hidden(const uint16_t* w1, const uint16_t* b1, const uint16_t* state,
+                                                    TArr ts, int n_t, int cond_emb, int state_dim, int hidden,
+                                                    uint16_t* a_out) {
+    extern __shared__ float cs[];
+    const int cond = cond_emb + state_dim, half = cond_emb / 2;
+    const int l = blockIdx.y;
+    const float log2_base = 13.287712379549449f;   // log2(10000)
+    for (int idx = threadIdx.x; idx < n_t * cond; idx += blockDim.x) {
+        const int i = idx / cond, k = idx % cond;
+        float v;
+        if (k < cond_emb) {
+            const int f = k < half ? k : k - half;
+            const float w = exp2f(-(float)f / (float)half * log2_base);
+            v = k < half ? sinf(ts.t[i] * w) : cosf(ts.t[i] * w);
+        } else {
+            v = bf2f(state[k - cond_emb]);
+        }
+        cs[idx] = bf_round(v);
+    }
+    __syncthreads();
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= hidden) return;
+    float acc[MAX_T];
+#pragma unroll
+    for (int i = 0; i < MAX_T; ++i) acc[i] = 0.f;
+    const uint16_t* wr = w1 + ((long long)l * hidden + j) * cond;
+    for (int k = 0; k < cond; k += 8) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(wr + k);
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = bf2f(e[u]);
+#pragma unroll
+            for (int i = 0; i < MAX_T; ++i)
+                if (i < n_t) acc[i] += w * cs[i * cond + k + u];
+        }
+    }
+    const float bias = bf2f(b1[(long long)l * hidden + j]);
+#pragma unroll
+    for (int i = 0; i < MAX_T; ++i) {
+        if (i < n_t) {
+            const float h = acc[i] + bias;
+            const float s = h / (1.f + expf(-h));
+            a_out[((long long)l * n_t + i) * hidden + j] = f2bf(s);
+        }
+    }
+}
+
+// Output layer: gamma[l][i][m] = 1 + b2[l][m] + W2[l][m] . a[l][i].
+// One wave per 4 outputs; grid (model / 16, L), block 256, dynamic LDS n_t * hidden bf16.
+__global__ __launch_bounds__(256) void gamma_out(const uint16_t* w2, const uint16_t* b2, const uint16_t* a_in, int n_t,
+                                                 int hidden, int model, float* gamma) {
+    extern __shared__ uint16_t as[];
+    const int l = blockIdx.y;
+    const uint16_t* a_l = a_in + (long long)l * n_t * hidden;
+    for (int idx = threadIdx.x * 8; idx < n_t * hidden; idx += blockDim.x * 8)
+        *reinterpret_cast<uint4*>(&as[idx]) = *reinterpret_cast<const uint4*>(a_l + idx);
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int o = 0; o < 4; ++o) {
+        const int m = blockIdx.x * 16 + wave * 4 + o;
+        if (m >= model) break;
+        float acc[MAX_T];
+#pragma unroll
+        for (int i = 0; i < MAX_T; ++i) acc[i] = 0.f;
+        const uint16_t* wr = w2 + ((long long)l * model + m) * hidden;
+        for (int k = lane * 8; k < hidden; k += 512) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(wr + k);
+            const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float w = bf2f(e[u]);
+#pragma unroll
+                for (int i = 0; i < MAX_T; ++i)
+                    if (i < n_t) acc[i] += w * bf2f(as[i * hidden + k + u]);
+            }
+        }
+        const float bias = bf2f(b2[(long long)l * model + m]);
+#pragma unroll
+        for (int i = 0; i < MAX_T; ++i) {
+            if (i < n_t) {
+                const float s = wsum(acc[i]);
+                if (lane == 0) gamma[((long long)l * n_t + i) * model + m] = 1.f + bias + s;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- RMS norm -----
+// y[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * gamma, FP32 arithmetic.
+// grid (rows), block 256.
+template <typename TO> __device__ __forceinline__ void store_y(TO* p, float v);
+template <> __device__ __forceinline__ void store_y<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_y<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
+
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_rows(const uint16_t* x, const float* gamma, int model, float eps, TO* y,
+                                                    uint32_t* nonfinite) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    const uint16_t* xr = x + (long long)r * model;
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < model; k += blockDim.x) {
+        const float v = bf2f(xr[k]);
+        ss += v * v;
+    }
+    ss = wsum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float ms = (red[0] + red[1] + red[2] + red[3]) / (float)model;
+    const float rinv = 1.f / sqrtf(ms + eps);
+    bool bad = false;
+    for (int k = threadIdx.x; k < model; k += blockDim.x) {
+        const float v = bf2f(xr[k]) * rinv * gamma[k];
+        bad |= !finite_f(v);
+        store_y(y + (long long)r * model + k, v);
+    }
+    if (nonfinite && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(nonfinite, 1u);
+}
+
+// ------------------------------------------------- skinny GEMM, A W^T -------
+// C[m][n] = sum_k A[m][k] W[n][k] for m < rows <= 64, bf16 in, FP32 accumulate,
+// with W in nn.Linear layout [N][K]. A workgroup owns 32 output columns; its
+// four waves split K and reduce through LDS. Weight-streaming bound: every
+// W element is read once, by one lane.
+//   A operand (32 rows x 16 k): lane row l32, k 8hi..8hi+7 -> 16 B of A's row
+//   B operand (16 k x 32 cols): lane col l32, k 8hi..8hi+7 -> 16 B of W's row
+enum GemmMode { GEMM_QKV = 0, GEMM_OPROJ = 1 };
+
+struct GemmOut {
+    // GEMM_QKV: columns [0, nq) -> q, [nq, nq+nk) -> k, [nq+nk, nq+2nk) -> v
+    uint16_t* q; uint16_t* k; uint16_t* v; int nq; int nk;
+    // GEMM_OPROJ: h += C (rounded to bf16); x -= dt * h when x != null
+    uint16_t* h; uint16_t* x; float dt;
+    uint32_t* nonfinite;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_awt(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w, int rows,
+                                                int K, int N, GemmOut out) {
+    __shared__ float red[4][2][16][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int n0 = blockIdx.x * 32;
+    const int kw = K / 4, k0 = wave * kw;
+    const bool two = rows > 32;
+    f32x16 c0 = f32x16{}, c1 = f32x16{};
+    const uint16_t* wp = w + (long long)(n0 + l32) * K + 8 * hi;
+    const uint16_t* ap0 = a + (long long)l32 * K + 8 * hi;
+    const uint16_t* ap1 = a + (long long)(32 + l32) * K + 8 * hi;
+    const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+    for (int k = k0; k < k0 + kw; k += 16) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(wp + k);
+        const bf16x8 x0 = r0 ? *reinterpret_cast<const bf16x8*>(ap0 + k) : bf16x8{};
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, b, c0, 0, 0, 0);
+        if (two) {
+            const bf16x8 x1 = r1 ? *reinterpret_cast<const bf16x8*>(ap1 + k) : bf16x8{};
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, b, c1, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        red[wave][0][r][lane] = c0[r];
+        red[wave][1][r][lane] = c1[r];
+    }
+    __syncthreads();
+    // wave w finishes registers r = 4w .. 4w+3 of both row blocks
+    bool bad = false;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = wave * 4 + rr;
+            const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const int n = n0 + l32;
+            if (m >= rows || n >= N) continue;
+            const float v = red[0][blk][r][lane] + red[1][blk][r][lane] + red[2][blk][r][lane] + red[3][blk][r][lane];
+            if (MODE == GEMM_QKV) {
+                if (n < out.nq)
+                    out.q[(long long)m * out.nq + n] = f2bf(v);
+                else if (n < out.nq + out.nk)
+                    out.k[(long long)m * out.nk + (n - out.nq)] = f2bf(v);
+                else
+                    out.v[(long long)m * out.nk + (n - out.nq - out.nk)] = f2bf(v);
+            } else {
+                uint16_t* hp = out.h + (long long)m * N + n;
+                const float hn = bf2f(f2bf(bf2f(*hp) + v));
+                *hp = f2bf(hn);
+                bad |= !finite_f(hn);
+                if (out.x) {
+                    uint16_t* xp = out.x + (long long)m * N + n;
+                    const float xn = bf2f(*xp) - out.dt * hn;
+                    bad |= !finite_f(xn);
+                    *xp = f2bf(xn);
+                }
+            }
+        }
+    }
+    if (MODE == GEMM_OPROJ && out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
+}
+
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static pa_status check_mlp(const ada_mlp* m) {
+    PA_CHECK_ARG(m && m->w1 && m->b1 && m->w2 && m->b2, PA_EINVAL, "ada: null MLP pointer");
+    PA_CHECK_ARG(al16(m->w1) && al16(m->w2), PA_EINVAL, "ada: MLP weights must be 16-byte aligned");
+    PA_CHECK_ARG(m->num_layers >= 1, PA_ESHAPE, "ada: num_layers must be >= 1");
+    PA_CHECK_ARG(m->cond_emb >= 2 && m->cond_emb % 2 == 0 && m->state_dim >= 0 && m->state_dim <= 128 &&
+                     (m->cond_emb + m->state_dim) % 8 == 0 && m->cond_emb + m->state_dim <= 512,
+                 PA_ESHAPE, "ada: cond_emb must be even, state_dim <= 128, cond_emb + state_dim a multiple of 8 (<= 512)");
+    PA_CHECK_ARG(m->hidden_dim >= 64 && m->hidden_dim % 64 == 0 && m->hidden_dim <= 4096, PA_ESHAPE,
+                 "ada: hidden_dim must be a multiple of 64 in [64, 4096]");
+    PA_CHECK_ARG(m->model_dim >= 64 && m->model_dim % 64 == 0, PA_ESHAPE, "ada: model_dim must be a multiple of 64");
+    return PA_OK;
+}
+
+static pa_status launch_gamma(const ada_mlp* m, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
+                              const uint16_t* b2, int n_layers, const float* t, int n_t, const uint16_t* state,
+                              float* gamma, uint16_t* a_ws, hipStream_t s) {
+    TArr ts{};
+    for (int i = 0; i < n_t; ++i) ts.t[i] = t[i];
+    const int cond = m->cond_emb + m->state_dim;
+    gamma_hidden<<<dim3((m->hidden_dim + 255) / 256, n_layers), 256, n_t * cond * sizeof(float), s>>>(
+        w1, b1, state, ts, n_t, m->cond_emb, m->state_dim, m->hidden_dim, a_ws);
+    PA_LAUNCHED();
+    gamma_out<<<dim3((m->model_dim + 15) / 16, n_layers), 256, n_t * m->hidden_dim * sizeof(uint16_t), s>>>(
+        w2, b2, a_ws, n_t, m->hidden_dim, m->model_dim, gamma);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" size_t ada_gamma_workspace_bytes(const ada_mlp* m, int32_t n_t) {
+    if (check_mlp(m) != PA_OK || n_t < 1 || n_t > MAX_T) return 0;
+    return align_up((size_t)m->num_layers * n_t * m->hidden_dim * sizeof(uint16_t), 256);
+}
+
+extern "C" pa_status ada_gamma(const ada_mlp* m, const float* t, int32_t n_t, const void* state, float* gamma,
+                               void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    pa_status st = check_mlp(m);
+    if (st != PA_OK) return st;
+    PA_CHECK_ARG(t && gamma && ws && (state || m->state_dim == 0), PA_EINVAL, "ada_gamma: null argument");
+    PA_CHECK_ARG(n_t >= 1 && n_t <= MAX_T, PA_ESHAPE, "ada_gamma: n_t %d not in [1, %d]", n_t, MAX_T);
+    PA_CHECK_ARG(n_t * m->hidden_dim * 2 <= 65536, PA_ESHAPE, "ada_gamma: n_t * hidden_dim too large for one call");
+    const size_t need = ada_gamma_workspace_bytes(m, n_t);
+    PA_CHECK_ARG(ws_bytes >= need, PA_ERANGE, "ada_gamma: workspace %zu < %zu bytes", ws_bytes, need);
+    for (int i = 0; i < n_t; ++i) PA_CHECK_ARG(isfinite(t[i]), PA_EINVAL, "ada_gamma: t[%d] is not finite", i);
+    return launch_gamma(m, static_cast<const uint16_t*>(m->w1), static_cast<const uint16_t*>(m->b1),
+                        static_cast<const uint16_t*>(m->w2), static_cast<const uint16_t*>(m->b2), m->num_layers, t,
+                        n_t, static_cast<const uint16_t*>(state), gamma, static_cast<uint16_t*>(ws),
+                        static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t ada_rmsnorm_workspace_bytes(const ada_mlp* m) {
+    if (check_mlp(m) != PA_OK) return 0;
+    return align_up((size_t)m->hidden_dim * sizeof(uint16_t), 256) + align_up((size_t)m->model_dim * sizeof(float), 256);
+}
+
+extern "C" pa_status ada_rmsnorm(const void* x, int32_t rows, const ada_mlp* m, int32_t layer, float t,
+                                 const void* state, float eps, void* y, int32_t y_dtype, uint32_t* nonfinite, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    clear_error();
+    pa_status st = check_mlp(m);
+    if (st != PA_OK) return st;
+    PA_CHECK_ARG(x && y && ws && (state || m->state_dim == 0), PA_EINVAL, "ada_rmsnorm: null argument");
+    PA_CHECK_ARG(y_dtype == PA_F32 || y_dtype == PA_BF16, PA_EINVAL, "ada_rmsnorm: bad y_dtype");
+    PA_CHECK_ARG(rows >= 1, PA_ESHAPE, "ada_rmsnorm: rows must be >= 1");
+    PA_CHECK_ARG(layer >= 0 && layer < m->num_layers, PA_ESHAPE, "ada_rmsnorm: layer %d outside [0, %d)", layer,
+                 m->num_layers);
+    PA_CHECK_ARG(eps >= 0.f && isfinite(t), PA_EINVAL, "ada_rmsnorm: eps must be >= 0 and t finite");
+    PA_CHECK_ARG(ws_bytes >= ada_rmsnorm_workspace_bytes(m), PA_ERANGE, "ada_rmsnorm: workspace too small");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int cond = m->cond_emb + m->state_dim;
+    const uint16_t* w1 = static_cast<const uint16_t*>(m->w1) + (long long)layer * m->hidden_dim * cond;
+    const uint16_t* b1 = static_cast<const uint16_t*>(m->b1) + (long long)layer * m->hidden_dim;
+    const uint16_t* w2 = static_cast<const uint16_t*>(m->w2) + (long long)layer * m->model_dim * m->hidden_dim;
+    const uint16_t* b2 = static_cast<const uint16_t*>(m->b2) + (long long)layer * m->model_dim;
+    uint16_t* a_ws = static_cast<uint16_t*>(ws);
+    float* g = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)m->hidden_dim * 2, 256));
+    st = launch_gamma(m, w1, b1, w2, b2, 1, &t, 1, static_cast<const uint16_t*>(state), g, a_ws, s);
+    if (st != PA_OK) return st;
+    if (y_dtype == PA_F32)
+        rmsnorm_rows<float><<<rows, 256, 0, s>>>(static_cast<const uint16_t*>(x), g, m->model_dim, eps,
+                                                 static_cast<float*>(y), nonfinite);
+    else
+        rmsnorm_rows<uint16_t><<<rows, 256, 0, s>>>(static_cast<const uint16_t*>(x), g, m->model_dim, eps,
+                                                    static_cast<uint16_t*>(y), nonfinite);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
+extern "C" size_t ada_rmsnorm_qkv_workspace_bytes(int32_t rows, int32_t model_dim) {
+    if (rows < 1 || model_dim < 1) return 0;
+    return align_up((size_t)rows * model_dim * sizeof(uint16_t), 256);
+}
+
+extern "C" pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const float* gamma, float eps,
+                                     const void* w_qkv, int32_t hq, int32_t hkv, int32_t d, void* q, void* k_dyn,
+                                     void* v_dyn, uint32_t* nonfinite, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    PA_CHECK_ARG(x && gamma && w_qkv && q && k_dyn && v_dyn && ws, PA_EINVAL, "ada_rmsnorm_qkv: null argument");
+    PA_CHECK_ARG(al16(x) && al16(w_qkv) && al16(ws), PA_EINVAL, "ada_rmsnorm_qkv: x, w_qkv, workspace must be 16-byte aligned");
+    PA_CHECK_ARG(rows >= 1 && rows <= 64, PA_ESHAPE, "ada_rmsnorm_qkv: rows %d not in [1, 64]", rows);
+    PA_CHECK_ARG(model_dim >= 64 && model_dim % 64 == 0, PA_ESHAPE, "ada_rmsnorm_qkv: model_dim must be a multiple of 64");
+    PA_CHECK_ARG(hq >= 1 && hkv >= 1 && hq % hkv == 0 && d >= 32 && d % 32 == 0, PA_ESHAPE,
+                 "ada_rmsnorm_qkv: need Hq a multiple of Hkv and D a multiple of 32");
+    PA_CHECK_ARG(eps >= 0.f, PA_EINVAL, "ada_rmsnorm_qkv: eps must be >= 0");
+    PA_CHECK_ARG(ws_bytes >= ada_rmsnorm_qkv_workspace_bytes(rows, model_dim), PA_ERANGE,
+                 "ada_rmsnorm_qkv: workspace too small");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t* y = static_cast<uint16_t*>(ws);
+    rmsnorm_rows<uint16_t><<<rows, 256, 0, s>>>(static_cast<const uint16_t*>(x), gamma, model_dim, eps, y, nonfinite);
+    PA_LAUNCHED();
+    GemmOut o{};
+    o.q = static_cast<uint16_t*>(q);
+    o.k = static_cast<uint16_t*>(k_dyn);
+    o.v = static_cast<uint16_t*>(v_dyn);
+    o.nq = hq * d;
+    o.nk = hkv * d;
+    const int n = (hq + 2 * hkv) * d;
+    gemm_awt<GEMM_QKV><<<n / 32, 256, 0, s>>>(y, static_cast<const uint16_t*>(w_qkv), rows, model_dim, n, o);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
+extern "C" pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, int32_t in_dim,
+                                    int32_t model_dim, void* x, float dt, uint32_t* nonfinite, void* stream) {
+    clear_error();
+    PA_CHECK_ARG(o && w_o && h, PA_EINVAL, "oproj_residual: null argument");
+    PA_CHECK_ARG(al16(o) && al16(w_o), PA_EINVAL, "oproj_residual: o and w_o must be 16-byte aligned");
+    PA_CHECK_ARG(rows >= 1 && rows <= 64, PA_ESHAPE, "oproj_residual: rows %d not in [1, 64]", rows);
+    PA_CHECK_ARG(in_dim >= 64 && in_dim % 64 == 0, PA_ESHAPE, "oproj_residual: in_dim must be a multiple of 64");
+    PA_CHECK_ARG(model_dim >= 32 && model_dim % 32 == 0, PA_ESHAPE, "oproj_residual: model_dim must be a multiple of 32");
+    PA_CHECK_ARG(isfinite(dt), PA_EINVAL, "oproj_residual: dt must be finite");
+    GemmOut g{};
+    g.h = static_cast<uint16_t*>(h);
+    g.x = static_cast<uint16_t*>(x);
+    g.dt = dt;
+    g.nonfinite = nonfinite;
+    gemm_awt<GEMM_OPROJ><<<model_dim / 32, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(w_o), rows, in_dim, model_dim, g);
+    PA_LAUNCHED();
+    return PA_OK;
+}

@@ -1,0 +1,102 @@
+// Internal helpers shared by the library's translation units: status and
+// error text, bf16 words, MFMA operand vector types, the KV-source descriptor
+// used by every attention kernel, and the ring handle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pattn.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------- errors --
+pa_status fail(pa_status st, const char* fmt, ...);
+void clear_error();
+
+#define PA_CHECK_ARG(cond, st, ...)            \
+    do {                                       \
+        if (!(cond)) return ::pa::fail(st, __VA_ARGS__); \
+    } while (0)
+
+#define PA_HIP(call)                                                          \
+    do {                                                                      \
+        hipError_t e_ = (call);                                               \
+        if (e_ != hipSuccess)                                                 \
+            return ::pa::fail(PA_EDEVICE, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// After a launch: report a launch failure as PA_EDEVICE.
+#define PA_LAUNCHED()                                                         \
+    do {                                                                      \
+        hipError_t e_ = hipGetLastError();                                    \
+        if (e_ != hipSuccess)                                                 \
+            return ::pa::fail(PA_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e_)); \
+    } while (0)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------- ring handle --
+struct Ring {
+    rb_config cfg;
+    void* k;              // device [L][P + W*F][Hkv][D]
+    void* v;
+    int32_t head = 0;
+    int32_t count = 0;
+    int32_t pinned = 0;
+    int64_t frames_pushed = 0;
+    int64_t elem_bytes() const { return cfg.dtype == PA_F32 ? 4 : 2; }
+    int64_t seq_len() const { return (int64_t)cfg.pin_capacity + (int64_t)cfg.num_slots * cfg.tokens_per_frame; }
+    int64_t layer_elems() const { return seq_len() * cfg.num_kv_heads * cfg.head_dim; }
+    int32_t cached_tokens() const { return pinned + count * cfg.tokens_per_frame; }
+};
+
+// ------------------------------------------------------------ device types --
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// float -> bf16 word, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ bool finite_f(float x) { return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u; }
+
+// Where the keys of one (layer, kv-head) live. Logical key j of the context
+// [pin | window | dyn] maps to
+//   j <  pinned                     ring token j
+//   j <  pinned + n_slide           ring token P + (j - pinned)   (physical slot order)
+//   otherwise                       dyn token j - pinned - n_slide
+// n_slide = count * F: the valid slots are always the leading `count` slots,
+// because slot f mod W is written by frame f and slots fill from 0.
+struct KvSource {
+    const void* ring_k;        // element 0 of layer `layer_begin`
+    const void* ring_v;
+    long long ring_layer;      // elements per ring layer
+    const void* dyn_k;         // element 0 of call-layer 0, may be null if n_dyn == 0
+    const void* dyn_v;
+    long long dyn_layer;       // elements per dyn layer (N * Hkv * D)
+    int pinned, pin_cap, n_slide, n_dyn;
+    int hkv, d;
+
+    __device__ __forceinline__ int total() const { return pinned + n_slide + n_dyn; }
+
+    // element offset of (call-layer lb, kv head g, logical key j) and which buffer
+    __device__ __forceinline__ long long offset(int lb, int g, int j, bool& is_dyn) const {
+        if (j < pinned + n_slide) {
+            int tok = j < pinned ? j : pin_cap + (j - pinned);
+            is_dyn = false;
+            return (long long)lb * ring_layer + ((long long)tok * hkv + g) * d;
+        }
+        is_dyn = true;
+        return (long long)lb * dyn_layer + ((long long)(j - pinned - n_slide) * hkv + g) * d;
+    }
+};
+
+}  // namespace pa

@@ -1,0 +1,121 @@
+// Static ring-buffer KV cache: handle, pinned prefix, frame push.
+//
+// "Reflex: Real-Time VLA Control through Streaming Inference" paper review,
+// §3 Architecture (ring-buffer diagram: a pinned prefix, then a FIFO window
+// where every frame enqueues the newest frame and evicts the oldest; the
+// component table gives buffer_k as num_layers x max_seq_len x num_heads x
+// head_dim) and §5 Code analysis (the buffers are allocated zeroed, once,
+// beside a write pointer that starts at 0).
+//
+// The buffers are the caller's. A push is one strided device-to-device copy
+// of the frame's [L][F][Hkv][D] block into slot `head` of every layer; only
+// host metadata changes otherwise. Nothing is ever allocated or moved, so a
+// captured graph that reads the ring stays valid across pushes.
+
+#include <stdarg.h>
+
+#include <new>
+
+#include "internal.h"
+
+namespace pa {
+
+static thread_local char g_err[512] = "";
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+}  // namespace pa
+
+using pa::Ring;
+
+extern "C" const char* pa_last_error(void) { return pa::g_err; }
+
+extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, rb_ring** out) {
+    pa::clear_error();
+    PA_CHECK_ARG(cfg && k_buf && v_buf && out, PA_EINVAL, "rb_create: null argument");
+    PA_CHECK_ARG(cfg->dtype == PA_F32 || cfg->dtype == PA_BF16, PA_EINVAL, "rb_create: bad dtype %d", cfg->dtype);
+    PA_CHECK_ARG(cfg->num_layers > 0 && cfg->num_kv_heads > 0 && cfg->head_dim > 0 && cfg->num_slots > 0 &&
+                     cfg->tokens_per_frame > 0 && cfg->pin_capacity >= 0,
+                 PA_ESHAPE, "rb_create: sizes must be positive (pin capacity >= 0)");
+    PA_CHECK_ARG(cfg->head_dim % 8 == 0 && cfg->head_dim <= 256, PA_ESHAPE,
+                 "rb_create: head_dim %d must be a multiple of 8 and <= 256", cfg->head_dim);
+    int64_t seq = (int64_t)cfg->pin_capacity + (int64_t)cfg->num_slots * cfg->tokens_per_frame;
+    PA_CHECK_ARG(seq < (1LL << 31), PA_ESHAPE, "rb_create: P + W*F too large");
+    Ring* r = new (std::nothrow) Ring();
+    PA_CHECK_ARG(r, PA_EINVAL, "rb_create: out of host memory");
+    r->cfg = *cfg;
+    r->k = k_buf;
+    r->v = v_buf;
+    *out = reinterpret_cast<rb_ring*>(r);
+    return PA_OK;
+}
+
+extern "C" pa_status rb_destroy(rb_ring* ring) {
+    pa::clear_error();
+    delete reinterpret_cast<Ring*>(ring);
+    return PA_OK;
+}
+
+// Copy [L][n][Hkv][D] (contiguous) into tokens [tok0, tok0 + n) of every layer.
+static pa_status copy_tokens(Ring* r, void* dst_base, const void* src, int64_t tok0, int64_t n, hipStream_t s) {
+    const int64_t tok_bytes = (int64_t)r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes();
+    const size_t width = (size_t)(n * tok_bytes);
+    const size_t dpitch = (size_t)(r->seq_len() * tok_bytes);
+    char* dst = static_cast<char*>(dst_base) + tok0 * tok_bytes;
+    PA_HIP(hipMemcpy2DAsync(dst, dpitch, src, width, width, (size_t)r->cfg.num_layers, hipMemcpyDeviceToDevice, s));
+    return PA_OK;
+}
+
+extern "C" pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, int32_t n_tokens, void* stream) {
+    pa::clear_error();
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_pin_prefix: null argument");
+    PA_CHECK_ARG(r->pinned == 0, PA_ESTATE, "rb_pin_prefix: prefix already pinned (%d tokens)", r->pinned);
+    PA_CHECK_ARG(n_tokens > 0 && n_tokens <= r->cfg.pin_capacity, PA_ESHAPE,
+                 "rb_pin_prefix: n_tokens %d not in [1, %d]", n_tokens, r->cfg.pin_capacity);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pa_status st = copy_tokens(r, r->k, k, 0, n_tokens, s);
+    if (st != PA_OK) return st;
+    st = copy_tokens(r, r->v, v, 0, n_tokens, s);
+    if (st != PA_OK) return st;
+    r->pinned = n_tokens;
+    return PA_OK;
+}
+
+extern "C" pa_status rb_push_frame(rb_ring* ring, const void* k, const void* v, void* stream, int64_t* evicted) {
+    pa::clear_error();
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_push_frame: null argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t tok0 = (int64_t)r->cfg.pin_capacity + (int64_t)r->head * r->cfg.tokens_per_frame;
+    pa_status st = copy_tokens(r, r->k, k, tok0, r->cfg.tokens_per_frame, s);
+    if (st != PA_OK) return st;
+    st = copy_tokens(r, r->v, v, tok0, r->cfg.tokens_per_frame, s);
+    if (st != PA_OK) return st;
+    const int64_t ev = r->frames_pushed >= r->cfg.num_slots ? r->frames_pushed - r->cfg.num_slots : -1;
+    r->frames_pushed += 1;
+    r->head = (r->head + 1) % r->cfg.num_slots;
+    r->count = r->count < r->cfg.num_slots ? r->count + 1 : r->cfg.num_slots;
+    if (evicted) *evicted = ev;
+    return PA_OK;
+}
+
+extern "C" pa_status rb_get_state(const rb_ring* ring, rb_state* out) {
+    pa::clear_error();
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    PA_CHECK_ARG(r && out, PA_EINVAL, "rb_get_state: null argument");
+    out->head = r->head;
+    out->count = r->count;
+    out->pinned = r->pinned;
+    out->reserved = 0;
+    out->frames_pushed = r->frames_pushed;
+    return PA_OK;
+}

@@ -1,0 +1,127 @@
+"""The C-ABI library loads and exports every entry point include/pattn.h
+declares; host-side argument validation returns the documented status codes
+without touching a device (no compute call runs here)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pattn.h")
+LIB = os.path.join(ROOT, "partitioned_kv_cache_amd", "libpattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:pa_status|size_t|const char\*|char\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ("rb_create", "rb_pin_prefix", "rb_push_frame", "rb_get_state", "pattn_step", "ada_rmsnorm",
+              "ada_gamma", "ada_rmsnorm_qkv", "pattn_decode", "pattn_append_private", "oproj_residual",
+              "pa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    from partitioned_kv_cache_amd import _lib
+    assert sorted(_lib.EXPORTS) == declared_functions()
+
+
+def _fake(n):
+    return 0x10000 * n      # non-null, never dereferenced on these paths
+
+
+def test_rb_create_validation_and_state_without_device():
+    from partitioned_kv_cache_amd import _lib as L
+    bad = L.rb_config(1, 1, 64, 16, 4, 16, 7)
+    with pytest.raises(L.PattnError) as e:
+        L.Ring(bad, _fake(1), _fake(2))
+    assert e.value.status == L.PA_EINVAL and "dtype" in str(e.value)
+    with pytest.raises(L.PattnError) as e:
+        L.Ring(L.rb_config(1, 1, 60, 16, 4, 16, L.PA_F32), _fake(1), _fake(2))
+    assert e.value.status == L.PA_ESHAPE
+    with pytest.raises(L.PattnError) as e:
+        L.Ring(L.rb_config(0, 1, 64, 16, 4, 16, L.PA_F32), _fake(1), _fake(2))
+    assert e.value.status == L.PA_ESHAPE
+    r = L.Ring(L.rb_config(1, 1, 64, 16, 4, 16, L.PA_F32), _fake(1), _fake(2))
+    assert r.state() == {"head": 0, "count": 0, "pinned": 0, "frames_pushed": 0}
+    with pytest.raises(L.PattnError) as e:
+        r.pin_prefix(_fake(3), _fake(4), 17, stream=0)       # > P
+    assert e.value.status == L.PA_ESHAPE
+    with pytest.raises(L.PattnError) as e:
+        r.pin_prefix(None, _fake(4), 4, stream=0)
+    assert e.value.status == L.PA_EINVAL
+    r.close()
+
+
+def test_pattn_step_validation_without_device():
+    from partitioned_kv_cache_amd import _lib as L
+    r = L.Ring(L.rb_config(2, 1, 256, 48, 2, 768, L.PA_BF16), _fake(1), _fake(2))
+    a = L.pattn_args(0, 2, 8, 51, 1 / 16, L.PA_F32)
+    ws = L.pattn_workspace_bytes(r, a)
+    assert ws > 0 and ws % 256 == 0
+    # not pinned yet, P > 0: state error, raised before any launch
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r, a, _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), ws, stream=0)
+    assert e.value.status == L.PA_ESTATE
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r, L.pattn_args(1, 2, 8, 51, 1 / 16), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), ws, 0)
+    assert e.value.status == L.PA_ESHAPE                      # layers [1, 3) outside 2 layers
+    r2 = L.Ring(L.rb_config(1, 2, 64, 0, 2, 8, L.PA_BF16), _fake(1), _fake(2))
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r2, L.pattn_args(0, 1, 7, 5, 1 / 8), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), ws, 0)
+    assert e.value.status == L.PA_ESHAPE                      # 7 query heads over 2 KV heads
+    r2.close()
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r, L.pattn_args(0, 2, 8, 0, 1 / 16), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), ws, 0)
+    assert e.value.status == L.PA_ESHAPE                      # n_dyn = 0
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r, L.pattn_args(0, 2, 8, 51, -1.0), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), ws, 0)
+    assert e.value.status == L.PA_EINVAL
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r, a, 0x10001, _fake(4), _fake(5), _fake(6), _fake(7), ws, 0)
+    assert e.value.status == L.PA_EINVAL and "aligned" in str(e.value)
+    assert L.pattn_workspace_bytes(r, L.pattn_args(0, 3, 8, 51, 1.0)) == 0
+    r.close()
+
+
+def test_workspace_grows_with_splits():
+    from partitioned_kv_cache_amd import _lib as L
+    r = L.Ring(L.rb_config(18, 1, 256, 256, 8, 768, L.PA_BF16), _fake(1), _fake(2))
+    w4 = L.pattn_workspace_bytes(r, L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_F32, 4))
+    w8 = L.pattn_workspace_bytes(r, L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_F32, 8))
+    assert w8 > w4 > 0
+    # 408 rows pad to 416; 8 splits x 18 layers x 416 rows x 256 dims x 4 bytes, plus (m, l)
+    assert w8 == 8 * 18 * 416 * 256 * 4 + ((8 * 18 * 416 * 8 + 255) // 256) * 256
+    r.close()
+
+
+def test_ada_validation_without_device():
+    from partitioned_kv_cache_amd import _lib as L
+    m = L.ada_mlp(_fake(1), _fake(2), _fake(3), _fake(4), 18, 128, 32, 1024, 1024)
+    assert L.ada_gamma_workspace_bytes(m, 10) == 18 * 10 * 1024 * 2
+    assert L.ada_gamma_workspace_bytes(m, 17) == 0
+    with pytest.raises(L.PattnError) as e:
+        L.ada_gamma(m, [0.5] * 17, _fake(5), _fake(6), _fake(7), 1 << 30, stream=0)
+    assert e.value.status == L.PA_ESHAPE
+    with pytest.raises(L.PattnError) as e:
+        L.ada_rmsnorm_qkv(_fake(1), 65, 1024, _fake(2), 1e-6, _fake(3), 8, 1, 256, _fake(4), _fake(5), _fake(6),
+                          None, _fake(7), 1 << 20, stream=0)
+    assert e.value.status == L.PA_ESHAPE
+    with pytest.raises(L.PattnError) as e:
+        L.oproj_residual(_fake(1), _fake(2), _fake(3), 51, 2000, 1024, stream=0)
+    assert e.value.status == L.PA_ESHAPE

@@ -1,0 +1,192 @@
+"""GPU parity of the ring buffer and partitioned attention against the oracle.
+
+Bars (written in each test): ring bytes bit-exact; fp32 attention max-abs
+<= 1e-5; bf16 attention max|gpu - ref| / max|ref| <= 2e-2 per layer output.
+The oracle attends over the chronological [pin; window; suffix] context in
+float64; the kernels read the ring in physical slot order.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import full_attention
+from partitioned_kv_cache_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_helpers import Scenario, dev, host, lib, max_abs, rel_err  # noqa: E402
+
+F32_ATOL = 1e-5
+BF16_REL = 2e-2
+
+
+def _banner(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ ring ----
+
+@pytest.mark.parametrize("shape,frames", [(configs.TINY, 10), (configs.PI05_1L, 5), (configs.LONG_18L, 10)])
+def test_ring_bytes_bit_exact(shape, frames):
+    _banner(f"ring bytes {shape.name} frames={frames}")
+    sc = Scenario(shape)
+    sc.check_bytes()
+    for f in range(frames):
+        sc.push(f)
+        sc.check_bytes()
+
+
+def test_ring_500_frames_wraps_and_counts():
+    """500 pushes on the Pi0.5-like ring; frames are cheap device patterns."""
+    _banner("ring 500 frames")
+    s = configs.PI05_1L
+    shp = (s.num_layers, s.tokens_per_frame, s.n_kv_heads, s.head_dim)
+    base = np.arange(np.prod(shp), dtype=np.int64).reshape(shp)
+
+    def frame(f):
+        return ((base * 3 + f * 7919) % 65521).astype(np.uint16), ((base * 5 + f * 104729) % 65519).astype(np.uint16)
+
+    sc = Scenario(s, frame_fn=frame)
+    for f in range(500):
+        ev = sc.push(f)
+        assert ev == (f - s.num_slots if f >= s.num_slots else -1)
+    sc.check_bytes()
+    assert sc.ring.state() == {"head": 500 % s.num_slots, "count": s.num_slots, "pinned": s.pin_tokens,
+                               "frames_pushed": 500}
+
+
+# ------------------------------------------------------------- attention ----
+
+def test_attention_tiny_fp32_every_frame_and_step():
+    s = configs.TINY
+    _banner(f"attention {s.name}")
+    sc = Scenario(s)
+    worst = 0.0
+    for f in range(s.frames):
+        sc.push(f)
+        for k in range(s.steps_per_frame):
+            q, kd, vd = synth.suffix_qkv(s, f, k)
+            for splits in (0, 1, 2, 3):
+                out = sc.run_step(q, kd, vd, num_splits=splits)
+                ref = sc.oracle_step(q, kd, vd, 0)
+                worst = max(worst, max_abs(out[0], ref))
+    _banner(f"tiny fp32 worst max-abs {worst:.3e}")
+    assert worst <= F32_ATOL
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_attention_pi05_single_layer(splits):
+    s = configs.PI05_1L
+    _banner(f"attention {s.name} splits={splits}")
+    sc = Scenario(s)
+    worst = 0.0
+    checked = {0: (0, 9), 1: (0,), 2: (5,), 7: (9,), 30: (0, 9)}
+    for f in range(max(checked) + 1):
+        sc.push(f)
+        for k in checked.get(f, ()):
+            q, kd, vd = synth.suffix_qkv(s, f, k)
+            out = sc.run_step(q, kd, vd, num_splits=splits)
+            worst = max(worst, rel_err(out[0], sc.oracle_step(q, kd, vd, 0)))
+    _banner(f"pi05 1L worst rel {worst:.3e}")
+    assert worst <= BF16_REL
+
+
+def test_attention_long_history_18_layers_bench_launch():
+    """Full long-history shape, default splits (the launch the benchmark times)."""
+    s = configs.LONG_18L
+    _banner(f"attention {s.name}")
+    sc = Scenario(s)
+    worst = 0.0
+    for f in range(10):
+        sc.push(f)
+        if f in (0, 7, 9):               # partly filled, just full, wrapped once
+            for k in (0, 9):
+                q, kd, vd = synth.suffix_qkv(s, f, k)
+                out = sc.run_step(q, kd, vd)
+                for l in (0, 5, 17):
+                    worst = max(worst, rel_err(out[l], sc.oracle_step(q, kd, vd, l)))
+    _banner(f"long 18L worst rel {worst:.3e}")
+    assert worst <= BF16_REL
+
+
+def test_attention_bf16_output_dtype():
+    s = configs.PI05_1L
+    sc = Scenario(s)
+    for f in range(3):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s, 2, 4)
+    out32 = sc.run_step(q, kd, vd)
+    out16 = sc.run_step(q, kd, vd, out_dtype=lib().PA_BF16)
+    ref = sc.oracle_step(q, kd, vd, 0)
+    assert rel_err(out16[0], ref) <= BF16_REL
+    # the bf16 output is the fp32 result rounded once
+    assert np.max(np.abs(out16 - out32)) <= np.max(np.abs(out32)) * 2 ** -8
+
+
+EDGE = [
+    # (D, Hq, Hkv, P, pinned, W, F, N, frames, splits)
+    (64, 1, 1, 0, 0, 3, 5, 1, 4, 0),          # no pin, a single suffix token
+    (128, 4, 2, 7, 3, 2, 33, 5, 3, 0),         # grouped heads, pin gap, ragged tiles
+    (256, 8, 1, 1, 1, 1, 1, 51, 2, 0),         # one-token window, one-slot ring
+    (256, 2, 1, 40, 40, 4, 100, 3, 9, 7),      # ragged split tails
+    (64, 6, 3, 5, 5, 5, 7, 17, 1, 3),          # one frame only (partly filled ring)
+    (128, 8, 1, 300, 300, 2, 64, 51, 0, 0),    # nothing pushed yet: pin + suffix only
+]
+
+
+@pytest.mark.parametrize("D,hq,hkv,P,pinned,W,F,N,frames,splits", EDGE)
+def test_attention_edge_cases(D, hq, hkv, P, pinned, W, F, N, frames, splits):
+    _banner(f"edge D={D} hq={hq} hkv={hkv} P={P}/{pinned} W={W} F={F} N={N} frames={frames} splits={splits}")
+    s = configs.PI05_1L.with_(name="edge", cfg_id=40 + D + hq, num_layers=2, n_q_heads=hq, n_kv_heads=hkv,
+                              head_dim=D, pin_tokens=P, num_slots=W, tokens_per_frame=F, n_dyn=N,
+                              scale=1 / math.sqrt(D))
+    sc = Scenario(s, pin_tokens=pinned)
+    for f in range(frames):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s, frames, 3)
+    out = sc.run_step(q, kd, vd, num_splits=splits)
+    for l in range(2):
+        assert rel_err(out[l], sc.oracle_step(q, kd, vd, l)) <= BF16_REL
+
+
+def test_attention_layer_subrange():
+    s = configs.LONG_18L.with_(name="sub", cfg_id=47, num_layers=4, num_slots=2, tokens_per_frame=96)
+    sc = Scenario(s)
+    for f in range(3):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s.with_(num_layers=2), 3, 1)
+    out = sc.run_step(q, kd, vd, layer_begin=2, num_layers=2)
+    for lb in range(2):
+        ck, cv = sc.cached_context(2 + lb)
+        ref = full_attention(synth.widen(q[lb]), np.concatenate([ck, synth.widen(kd[lb])]),
+                             np.concatenate([cv, synth.widen(vd[lb])]), s.scale)
+        assert rel_err(out[lb], ref) <= BF16_REL
+
+
+def test_naive_cache_fails_parity():
+    """Negative control (Table 4 of the Reflex review: the naive cache is wrong):
+    reusing step 0's suffix K/V at step 9 must miss the oracle by far more than the bar."""
+    s = configs.PI05_1L
+    sc = Scenario(s)
+    for f in range(2):
+        sc.push(f)
+    q9, kd9, vd9 = synth.suffix_qkv(s, 1, 9)
+    _, kd0, vd0 = synth.suffix_qkv(s, 1, 0)
+    ref = sc.oracle_step(q9, kd9, vd9, 0)
+    good = sc.run_step(q9, kd9, vd9)
+    naive = sc.run_step(q9, kd0, vd0)
+    assert rel_err(good[0], ref) <= BF16_REL
+    assert rel_err(naive[0], ref) > 5 * BF16_REL
+
+
+def test_repeat_calls_are_deterministic():
+    s = configs.PI05_1L
+    sc = Scenario(s)
+    sc.push(0)
+    q, kd, vd = synth.suffix_qkv(s, 0, 0)
+    a = sc.run_step(q, kd, vd)
+    b = sc.run_step(q, kd, vd)
+    assert np.array_equal(a, b)
