@@ -132,12 +132,22 @@ size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* args);
  * k_dyn [Lb][N][Hkv][D]   ring dtype: K_dyn(k) of this step
  * v_dyn [Lb][N][Hkv][D]   ring dtype
  * out   [Lb][N][Hq][D]    args->out_dtype
- * PA_ESTATE: the ring holds no cached token yet and n_dyn keys alone are
- * allowed, so this is only raised for an unpinned ring with P > 0 and no frame.
+ * PA_ESTATE: P > 0 and the prefix has not been pinned (the prefix is
+ * computed once, before streaming starts). With nothing pushed yet the
+ * context is [pin; suffix].
  * PA_ERANGE: ws_bytes < pattn_workspace_bytes(). */
 pa_status pattn_step(const rb_ring* ring, const pattn_args* args, const void* q,
                      const void* k_dyn, const void* v_dyn, void* out,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/* pattn_step that also records ev_begin / ev_end (hipEvent_t as void*,
+ * either may be NULL) on `stream` immediately before and after its split-KV
+ * partial kernel, so that kernel can be timed alone while the whole step
+ * runs. Same arguments, results and errors as pattn_step. */
+pa_status pattn_step_timed(const rb_ring* ring, const pattn_args* args, const void* q,
+                           const void* k_dyn, const void* v_dyn, void* out,
+                           void* workspace, size_t ws_bytes, void* stream,
+                           void* ev_begin, void* ev_end);
 
 /* ========================================================================
  * Shared-KV decode readers (OxyGen review, core method and method
@@ -228,8 +238,9 @@ pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const 
                           uint32_t* nonfinite, void* workspace, size_t ws_bytes, void* stream);
 
 /* ========================================================================
- * Layer glue of the denoising stack (not on the pages; see the header of
- * each reading in the design notes of the library):
+ * Layer glue of the denoising stack. The pages give none; this is a reading:
+ * a residual out-projection with no bias and no FFN, the velocity taken as
+ * the last layer's stream, and an Euler step of size dt:
  *     h <- bf16(h + o W_o^T)                      (residual out-projection)
  * and, when x is not NULL, the Euler update of the flow state
  *     x <- bf16(x - dt * h)                       (v = last layer's stream)
@@ -238,6 +249,36 @@ pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const 
  * ====================================================================== */
 pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, int32_t in_dim,
                          int32_t model_dim, void* x, float dt, uint32_t* nonfinite, void* stream);
+
+/* ========================================================================
+ * One denoising step of the stack, all layers (the chain the pages'
+ * denoising loop runs ten times per frame; Reflex review §6 Table 7):
+ *   h = x
+ *   for l in layers:  [q|k|v] = ada_rmsnorm_qkv(h, gamma[l])      (Eq. 2)
+ *                     o = partitioned attention, layer l           (Eq. 1)
+ *                     h = bf16(h + o W_o[l]^T)
+ *   x = bf16(x - dt * h)
+ * gamma: f32, gamma[l] at gamma + l * gamma_layer_stride, [model_dim] each.
+ * x: bf16 [rows][model_dim], updated in place. Layers [0, num_layers) of
+ * the ring; the ring's head_dim and KV heads define D and Hkv.
+ * ====================================================================== */
+typedef struct {
+    int32_t num_layers;
+    int32_t rows;              /* N suffix tokens, <= 64 */
+    int32_t model_dim;         /* multiple of 256 */
+    int32_t n_q_heads;
+    const void* w_qkv;         /* bf16 [L][(Hq + 2 Hkv) * D][model_dim] */
+    const void* w_o;           /* bf16 [L][model_dim][Hq * D] */
+    float eps;
+    float scale;               /* attention scale, applied once */
+    float dt;                  /* Euler step */
+    int32_t num_splits;        /* attention KV splits; 0 = library's choice */
+} pa_stack;
+
+size_t pa_denoise_step_workspace_bytes(const rb_ring* ring, const pa_stack* stack);
+pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* stack, void* x, const float* gamma,
+                          int64_t gamma_layer_stride, uint32_t* nonfinite, void* workspace,
+                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,8 @@ EXPORTS = (
     "pa_last_error", "rb_create", "rb_destroy", "rb_pin_prefix", "rb_push_frame", "rb_get_state",
     "pattn_workspace_bytes", "pattn_step", "pattn_append_private", "pattn_decode_workspace_bytes",
     "pattn_decode", "ada_gamma_workspace_bytes", "ada_gamma", "ada_rmsnorm_workspace_bytes", "ada_rmsnorm",
-    "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual",
+    "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
+    "pa_denoise_step_workspace_bytes", "pa_denoise_step",
 )
 
 
@@ -69,6 +70,12 @@ class AdaMlp(C.Structure):
                 ("hidden_dim", C.c_int32), ("model_dim", C.c_int32)]
 
 
+class PaStack(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("rows", C.c_int32), ("model_dim", C.c_int32), ("n_q_heads", C.c_int32),
+                ("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("eps", C.c_float), ("scale", C.c_float),
+                ("dt", C.c_float), ("num_splits", C.c_int32)]
+
+
 _vp, _i32, _f32, _sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
 
 
@@ -86,6 +93,9 @@ _sig("rb_push_frame", _i32, _vp, _vp, _vp, _vp, C.POINTER(C.c_int64))
 _sig("rb_get_state", _i32, _vp, C.POINTER(RbState))
 _sig("pattn_workspace_bytes", _sz, _vp, C.POINTER(PattnArgs))
 _sig("pattn_step", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("pattn_step_timed", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp)
+_sig("pa_denoise_step_workspace_bytes", _sz, _vp, C.POINTER(PaStack))
+_sig("pa_denoise_step", _i32, _vp, C.POINTER(PaStack), _vp, _vp, C.c_int64, _vp, _vp, _sz, _vp)
 _sig("pattn_append_private", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _sig("pattn_decode_workspace_bytes", _sz, _vp, C.POINTER(PattnDecodeArgs))
 _sig("pattn_decode", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
@@ -175,6 +185,13 @@ def pattn_step(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, workspace, ws_
                            ws_bytes, _stream(stream)), "pattn_step")
 
 
+def pattn_step_timed(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, workspace, ws_bytes: int, stream=None,
+                     ev_begin=None, ev_end=None):
+    """pattn_step plus HIP events recorded around its split-KV partial kernel (raw hipEvent_t ints)."""
+    _check(_lib.pattn_step_timed(ring.handle, C.byref(args), ptr(q), ptr(k_dyn), ptr(v_dyn), ptr(out),
+                                 ptr(workspace), ws_bytes, _stream(stream), ev_begin, ev_end), "pattn_step_timed")
+
+
 def decode_args(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype=PA_F32,
                 num_splits=0) -> PattnDecodeArgs:
     return PattnDecodeArgs(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype, num_splits)
@@ -238,6 +255,24 @@ def ada_rmsnorm_qkv(x, rows, model_dim, gamma, eps, w_qkv, n_q_heads, n_kv_heads
 def oproj_residual(o, w_o, h, rows, in_dim, model_dim, x=None, dt=0.1, nonfinite=None, stream=None):
     _check(_lib.oproj_residual(ptr(o), ptr(w_o), ptr(h), rows, in_dim, model_dim, ptr(x), dt, ptr(nonfinite),
                                _stream(stream)), "oproj_residual")
+
+
+# ----------------------------------------------------------- denoise step ----
+
+def pa_stack(num_layers, rows, model_dim, n_q_heads, w_qkv, w_o, eps, scale, dt, num_splits=0) -> PaStack:
+    st = PaStack(num_layers, rows, model_dim, n_q_heads, ptr(w_qkv), ptr(w_o), eps, scale, dt, num_splits)
+    st._keep = (w_qkv, w_o)
+    return st
+
+
+def pa_denoise_step_workspace_bytes(ring: Ring, st: PaStack) -> int:
+    return _lib.pa_denoise_step_workspace_bytes(ring.handle, C.byref(st))
+
+
+def pa_denoise_step(ring: Ring, st: PaStack, x, gamma, gamma_layer_stride: int, nonfinite, workspace, ws_bytes: int,
+                    stream=None):
+    _check(_lib.pa_denoise_step(ring.handle, C.byref(st), ptr(x), ptr(gamma), gamma_layer_stride, ptr(nonfinite),
+                                ptr(workspace), ws_bytes, _stream(stream)), "pa_denoise_step")
 
 
 def raw():

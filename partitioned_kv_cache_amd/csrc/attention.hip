@@ -519,8 +519,9 @@ extern "C" size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* a
     return partial_bytes(p, r->cfg.head_dim);
 }
 
-extern "C" pa_status pattn_step(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
-                                const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream) {
+static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
+                           const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream, void* ev_begin,
+                           void* ev_end) {
     clear_error();
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     PA_CHECK_ARG(r && a && q && k_dyn && v_dyn && out && ws, PA_EINVAL, "pattn_step: null argument");
@@ -541,9 +542,22 @@ extern "C" pa_status pattn_step(const rb_ring* ring, const pattn_args* a, const 
     const KvSource src = source_for(r, a->layer_begin, k_dyn, v_dyn, a->n_dyn);
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
     const long long q_layer = (long long)a->n_dyn * a->n_q_heads * r->cfg.head_dim;
+    if (ev_begin) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_begin), s));
     st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s);
     if (st != PA_OK) return st;
+    if (ev_end) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_end), s));
     return launch_combine(r, p, p.parts, a->n_q_heads, q_layer, out, a->out_dtype, part, s);
+}
+
+extern "C" pa_status pattn_step(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
+                                const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream) {
+    return step_impl(ring, a, q, k_dyn, v_dyn, out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" pa_status pattn_step_timed(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
+                                      const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream,
+                                      void* ev_begin, void* ev_end) {
+    return step_impl(ring, a, q, k_dyn, v_dyn, out, ws, ws_bytes, stream, ev_begin, ev_end);
 }
 
 // ------------------------------------------------------------ decode readers --

@@ -1,0 +1,124 @@
+// One denoising step of the whole stack, every layer, launched from C++.
+//
+// The pages time the denoising loop as one component -- ten steps per
+// action chunk ("Reflex: Real-Time VLA Control through Streaming Inference"
+// paper review, §6 Table 7) -- and describe each step's suffix as recomputed
+// while the cached regions are only read (§3 Eq. 1 text). Per layer the
+// chain is AdaRMSNorm fused into the packed QKV projection (§3 Eq. 2; §2/§4
+// fused operators), partitioned attention (Eq. 1), and a residual
+// out-projection; the Euler update of the flow state is fused into the last
+// out-projection. The out-projection, the velocity (last layer's stream) and
+// the Euler step are readings: the pages give no layer glue.
+//
+// Everything is enqueued on one stream with no host synchronisation and no
+// allocation, so a caller can capture the whole step in a graph and replay
+// it while frames are pushed into the ring between replays.
+
+#include "internal.h"
+
+namespace pa {
+
+struct StackWs {
+    size_t h, y, q, k, v, o, attn, total;
+};
+
+static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes) {
+    const size_t n = st->rows, m = st->model_dim, d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
+    StackWs w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += align_up(bytes, 256);
+        return at;
+    };
+    w.h = take(n * m * 2);
+    w.y = take(n * m * 2);
+    w.q = take(n * st->n_q_heads * d * 2);
+    w.k = take(n * hkv * d * 2);
+    w.v = take(n * hkv * d * 2);
+    w.o = take(n * st->n_q_heads * d * 2);
+    w.attn = take(attn_bytes);
+    w.total = off;
+    return w;
+}
+
+static pa_status check_stack(const Ring* r, const pa_stack* st) {
+    PA_CHECK_ARG(r && st && st->w_qkv && st->w_o, PA_EINVAL, "pa_denoise_step: null argument");
+    PA_CHECK_ARG(r->cfg.dtype == PA_BF16, PA_EINVAL, "pa_denoise_step: the stack runs on a bf16 ring");
+    PA_CHECK_ARG(st->num_layers >= 1 && st->num_layers <= r->cfg.num_layers, PA_ESHAPE,
+                 "pa_denoise_step: %d layers but the ring has %d", st->num_layers, r->cfg.num_layers);
+    PA_CHECK_ARG(st->rows >= 1 && st->rows <= 64, PA_ESHAPE, "pa_denoise_step: rows %d not in [1, 64]", st->rows);
+    PA_CHECK_ARG(st->model_dim >= 256 && st->model_dim % 256 == 0, PA_ESHAPE,
+                 "pa_denoise_step: model_dim must be a multiple of 256");
+    PA_CHECK_ARG(st->n_q_heads >= 1 && st->n_q_heads % r->cfg.num_kv_heads == 0, PA_ESHAPE,
+                 "pa_denoise_step: n_q_heads must be a multiple of num_kv_heads");
+    PA_CHECK_ARG((st->n_q_heads * r->cfg.head_dim) % 256 == 0, PA_ESHAPE,
+                 "pa_denoise_step: n_q_heads * head_dim must be a multiple of 256");
+    return PA_OK;
+}
+
+static pattn_args attn_args(const pa_stack* st, int layer) {
+    pattn_args a;
+    a.layer_begin = layer;
+    a.num_layers = 1;
+    a.n_q_heads = st->n_q_heads;
+    a.n_dyn = st->rows;
+    a.scale = st->scale;
+    a.out_dtype = PA_BF16;
+    a.num_splits = st->num_splits;
+    return a;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" size_t pa_denoise_step_workspace_bytes(const rb_ring* ring, const pa_stack* st) {
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    if (check_stack(r, st) != PA_OK) return 0;
+    const pattn_args a = attn_args(st, 0);
+    const size_t attn = pattn_workspace_bytes(ring, &a);
+    if (!attn) return 0;
+    return stack_layout(r, st, attn).total;
+}
+
+extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, void* x, const float* gamma,
+                                     int64_t gamma_layer_stride, uint32_t* nonfinite, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    clear_error();
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    pa_status s = check_stack(r, st);
+    if (s != PA_OK) return s;
+    PA_CHECK_ARG(x && gamma && ws, PA_EINVAL, "pa_denoise_step: null argument");
+    PA_CHECK_ARG(gamma_layer_stride >= st->model_dim, PA_ESHAPE, "pa_denoise_step: gamma stride below model_dim");
+    const pattn_args a0 = attn_args(st, 0);
+    const size_t attn = pattn_workspace_bytes(ring, &a0);
+    PA_CHECK_ARG(attn > 0, PA_ESHAPE, "pa_denoise_step: attention arguments rejected");
+    const StackWs w = stack_layout(r, st, attn);
+    PA_CHECK_ARG(ws_bytes >= w.total, PA_ERANGE, "pa_denoise_step: workspace %zu < %zu bytes", ws_bytes, w.total);
+    char* base = static_cast<char*>(ws);
+    void *h = base + w.h, *q = base + w.q, *k = base + w.k, *v = base + w.v, *o = base + w.o;
+    void* aws = base + w.attn;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    const size_t xbytes = (size_t)st->rows * st->model_dim * 2;
+    PA_HIP(hipMemcpyAsync(h, x, xbytes, hipMemcpyDeviceToDevice, strm));
+    const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
+    const int in_dim = st->n_q_heads * d;
+    const size_t wqkv_layer = (size_t)(st->n_q_heads + 2 * hkv) * d * st->model_dim;
+    const size_t wo_layer = (size_t)st->model_dim * in_dim;
+    const size_t y_bytes = align_up((size_t)st->rows * st->model_dim * 2, 256);
+    for (int l = 0; l < st->num_layers; ++l) {
+        const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
+        const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
+        s = ada_rmsnorm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq, st->n_q_heads,
+                            hkv, d, q, k, v, nonfinite, base + w.y, y_bytes, stream);
+        if (s != PA_OK) return s;
+        const pattn_args a = attn_args(st, l);
+        s = pattn_step(ring, &a, q, k, v, o, aws, attn, stream);
+        if (s != PA_OK) return s;
+        s = oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, l + 1 == st->num_layers ? x : nullptr, st->dt,
+                           nonfinite, stream);
+        if (s != PA_OK) return s;
+    }
+    return PA_OK;
+}

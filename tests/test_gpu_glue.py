@@ -1,0 +1,341 @@
+"""GPU parity of AdaRMSNorm (Eq. 2), its gamma MLP, the fused norm + packed
+QKV projection, the out-projection with the Euler update, the shared-KV
+decode readers, and the whole denoising step; plus the non-finite flag, graph
+replay and the 10^4-frame finiteness stress of the 18-layer stack.
+
+Bar: max|gpu - ref| / max|ref| <= 2e-2 per output tensor (bf16 storage,
+FP32 accumulation). Expected values come from the oracle only; where a GPU
+call needs a derived input (gamma for the fused kernel) the oracle's value is
+what it is fed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import adanorm, decode, stack
+from oracle.attention import full_attention
+from partitioned_kv_cache_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_helpers import Scenario, dev, host, lib, rel_err  # noqa: E402
+
+BAR = 2e-2
+S3 = configs.PI05_18L
+
+
+def _banner(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _mlp_host(s, layers):
+    ws = [synth.mlp_weights(s, l) for l in layers]
+    return [np.stack([w[i] for w in ws]) for i in range(4)]        # w1, b1, w2, b2 stacked
+
+
+def _mlp_dev(s, layers):
+    L = lib()
+    w1, b1, w2, b2 = (dev(a) for a in _mlp_host(s, layers))
+    return L.ada_mlp(w1, b1, w2, b2, len(layers), s.cond_emb, s.state_dim, s.hidden_dim, s.model_dim)
+
+
+def _oracle_gamma(s, layer, t, state_bits):
+    w1, b1, w2, b2 = (synth.widen(a) for a in synth.mlp_weights(s, layer))
+    return adanorm.gamma(w1, b1, w2, b2, t, synth.widen(state_bits))
+
+
+def test_ada_gamma_batched_over_layers_and_steps():
+    L = lib()
+    layers = list(range(S3.num_layers))
+    _banner("ada_gamma 18 layers x 10 steps")
+    mlp = _mlp_dev(S3, layers)
+    state = synth.robot_state(S3, 3)
+    ts = stack.timesteps(10)
+    gamma = torch.empty((len(layers), 10, S3.model_dim), dtype=torch.float32, device="cuda")
+    wsb = L.ada_gamma_workspace_bytes(mlp, 10)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    L.ada_gamma(mlp, ts, dev(state), gamma, ws, wsb)
+    g = host(gamma).astype(np.float64)
+    worst = 0.0
+    for l in (0, 7, 17):
+        for i in (0, 4, 9):
+            worst = max(worst, rel_err(g[l, i], _oracle_gamma(S3, l, ts[i], state)))
+    _banner(f"gamma worst rel {worst:.3e}")
+    assert worst <= BAR
+
+
+@pytest.mark.parametrize("y_dtype", ["f32", "bf16"])
+def test_ada_rmsnorm_full_eq2(y_dtype):
+    L = lib()
+    mlp = _mlp_dev(S3, [0, 1])
+    x = synth.flow_x(S3, 5)
+    state = synth.robot_state(S3, 5)
+    od = L.PA_F32 if y_dtype == "f32" else L.PA_BF16
+    y = torch.empty((S3.n_dyn, S3.model_dim), dtype=torch.float32 if od == L.PA_F32 else torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsb = L.ada_rmsnorm_workspace_bytes(mlp)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    L.ada_rmsnorm(dev(x), S3.n_dyn, mlp, 1, 0.7, dev(state), S3.eps, y, od, flag, ws, wsb)
+    w1, b1, w2, b2 = (synth.widen(a) for a in synth.mlp_weights(S3, 1))
+    ref = adanorm.ada_rmsnorm(synth.widen(x), w1, b1, w2, b2, 0.7, synth.widen(state), S3.eps)
+    err = rel_err(synth.widen(host(y)), ref)
+    _banner(f"ada_rmsnorm {y_dtype} rel {err:.3e}")
+    assert err <= BAR
+    assert int(host(flag)[0]) == 0
+
+
+@pytest.mark.parametrize("rows,model,hq,hkv,d", [(51, 1024, 8, 1, 256), (1, 256, 2, 1, 64), (64, 512, 4, 2, 32),
+                                                 (33, 768, 3, 1, 128)])
+def test_ada_rmsnorm_qkv_fused(rows, model, hq, hkv, d):
+    L = lib()
+    s = S3.with_(name="qkv", cfg_id=60 + rows, n_dyn=rows, model_dim=model, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                 hidden_dim=256)
+    x = synth.normal((rows, model), "bf16", s.cfg_id, synth.T_X, 9)
+    wq, _ = synth.proj_weights(s, 0)
+    gam = (1.0 + 0.2 * np.random.default_rng(rows).standard_normal(model)).astype(np.float32)
+    q = torch.empty((rows, hq, d), dtype=torch.int16, device="cuda")
+    k = torch.empty((rows, hkv, d), dtype=torch.int16, device="cuda")
+    v = torch.empty((rows, hkv, d), dtype=torch.int16, device="cuda")
+    wsb = L.ada_rmsnorm_qkv_workspace_bytes(rows, model)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    L.ada_rmsnorm_qkv(dev(x), rows, model, dev(gam), s.eps, dev(wq), hq, hkv, d, q, k, v, None, ws, wsb)
+    y = adanorm.round_bf16(adanorm.rmsnorm_scaled(synth.widen(x), gam.astype(np.float64), s.eps))
+    rq, rk, rv = stack.qkv_projection(y, synth.widen(wq), hq, hkv, d)
+    for got, ref in ((q, rq), (k, rk), (v, rv)):
+        assert rel_err(synth.widen(host(got)), ref) <= BAR
+
+
+@pytest.mark.parametrize("with_x", [False, True])
+def test_oproj_residual_and_euler(with_x):
+    L = lib()
+    s = S3
+    in_dim = s.n_q_heads * s.head_dim
+    o = synth.normal((s.n_dyn, in_dim), "bf16", 70, 1)
+    h = synth.normal((s.n_dyn, s.model_dim), "bf16", 70, 2)
+    x = synth.normal((s.n_dyn, s.model_dim), "bf16", 70, 3)
+    _, wo = synth.proj_weights(s, 4)
+    h_d, x_d = dev(h), dev(x)
+    L.oproj_residual(dev(o), dev(wo), h_d, s.n_dyn, in_dim, s.model_dim, x_d if with_x else None, 0.1)
+    ref_h = adanorm.round_bf16(stack.out_projection_residual(synth.widen(h), synth.widen(o), synth.widen(wo)))
+    assert rel_err(synth.widen(host(h_d)), ref_h) <= BAR
+    if with_x:
+        assert rel_err(synth.widen(host(x_d)), stack.euler(synth.widen(x), ref_h)) <= BAR
+    else:
+        assert np.array_equal(host(x_d), x)
+
+
+def test_nonfinite_flag_trips_on_injected_inf_and_nan():
+    L = lib()
+    mlp = _mlp_dev(S3, [0])
+    state = synth.robot_state(S3, 1)
+    wsb = L.ada_rmsnorm_workspace_bytes(mlp)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    for bad in (np.inf, np.nan, None):
+        x = synth.flow_x(S3, 1).copy()
+        if bad is not None:
+            x[7, 100] = synth.f32_to_bf16_bits(np.array([bad], np.float32))[0]
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y = torch.empty((S3.n_dyn, S3.model_dim), dtype=torch.int16, device="cuda")
+        L.ada_rmsnorm(dev(x), S3.n_dyn, mlp, 0, 0.5, dev(state), S3.eps, y, L.PA_BF16, flag, ws, wsb)
+        assert int(host(flag)[0]) == (0 if bad is None else 1), bad
+
+
+# ----------------------------------------------------------- decode readers --
+
+def test_decode_readers_private_tails():
+    """16 streams x 1 query token over the long-history cache plus private tails."""
+    L = lib()
+    s = configs.SHARED_KV
+    _banner("decode readers")
+    sc = Scenario(s)
+    for f in range(9):
+        sc.push(f)
+    G, cap, hkv, D = s.n_streams, s.tail_capacity, s.n_kv_heads, s.head_dim
+    lens0 = np.array([(2 * j) % cap for j in range(G)], dtype=np.int32)
+    lens0[3] = cap                        # a full tail: append must refuse it
+    tk = synth.normal((s.num_layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILK, 99)
+    tv = synth.normal((s.num_layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILV, 99)
+    tk_d, tv_d, len_d = dev(tk), dev(tv), dev(lens0)
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_F32)
+    kn, vn = synth.decode_kv(s, 9, 0)
+    L.pattn_append_private(sc.ring, a, tk_d, tv_d, len_d, dev(kn), dev(vn), ovf)
+    q = synth.decode_q(s, 9, 0)
+    wsb = L.pattn_decode_workspace_bytes(sc.ring, a)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.num_layers, G, s.n_q_heads, D), dtype=torch.float32, device="cuda")
+    L.pattn_decode(sc.ring, a, dev(q), tk_d, tv_d, len_d, out, ws, wsb)
+    torch.cuda.synchronize()
+    lens1 = host(len_d)
+    want_lens = np.minimum(lens0 + 1, cap)
+    assert np.array_equal(lens1, want_lens)
+    assert int(host(ovf)[0]) == 1 << 3
+    got = host(out).astype(np.float64)
+    worst = 0.0
+    for l in (0, 9, 17):
+        tails = decode.PrivateTails(G, cap, hkv, D)
+        for j in range(G):
+            for t in range(int(lens0[j])):
+                tails.append(j, synth.widen(tk[l, j, t]), synth.widen(tv[l, j, t]))
+            if lens0[j] < cap:
+                tails.append(j, synth.widen(kn[l, j]), synth.widen(vn[l, j]))
+        ck, cv = sc.cached_context(l)
+        ref = decode.decode_attention(synth.widen(q[l]), ck, cv, tails, s.scale)
+        worst = max(worst, rel_err(got[l], ref))
+    _banner(f"decode worst rel {worst:.3e}")
+    assert worst <= BAR
+
+
+def test_decode_empty_tail_is_shared_context_only():
+    L = lib()
+    s = configs.SHARED_KV.with_(name="dec_small", cfg_id=51, num_layers=2, tokens_per_frame=64, n_streams=3,
+                                tail_capacity=4)
+    sc = Scenario(s)
+    for f in range(3):
+        sc.push(f)
+    G, cap, D = s.n_streams, s.tail_capacity, s.head_dim
+    tk = torch.zeros((2, G, cap, 1, D), dtype=torch.int16, device="cuda")
+    tv = torch.zeros_like(tk)
+    lens = torch.zeros(G, dtype=torch.int32, device="cuda")
+    q = synth.decode_q(s, 3, 0)
+    a = L.decode_args(0, 2, s.n_q_heads, G, cap, s.scale, L.PA_F32, 2)
+    wsb = L.pattn_decode_workspace_bytes(sc.ring, a)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((2, G, s.n_q_heads, D), dtype=torch.float32, device="cuda")
+    L.pattn_decode(sc.ring, a, dev(q), tk, tv, lens, out, ws, wsb)
+    got = host(out).astype(np.float64)
+    for l in range(2):
+        ck, cv = sc.cached_context(l)
+        assert rel_err(got[l], full_attention(synth.widen(q[l]), ck, cv, s.scale)) <= BAR
+
+
+# ------------------------------------------------------------ denoise step ---
+
+class StackRig:
+    """The 18-layer stack on a ring: device weights, gammas, and oracle inputs."""
+
+    def __init__(self, s, frames):
+        L = lib()
+        self.s = s
+        self.sc = Scenario(s)
+        for f in range(frames):
+            self.sc.push(f)
+        self.wq = [synth.proj_weights(s, l) for l in range(s.num_layers)]
+        self.wqkv_d = dev(np.stack([w[0] for w in self.wq]))
+        self.wo_d = dev(np.stack([w[1] for w in self.wq]))
+        self.st = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, self.wqkv_d, self.wo_d, s.eps,
+                             s.scale, 0.1)
+        self.wsb = L.pa_denoise_step_workspace_bytes(self.sc.ring, self.st)
+        self.ws = torch.empty(self.wsb, dtype=torch.uint8, device="cuda")
+
+    def oracle_gammas(self, frame, k):
+        state = synth.robot_state(self.s, frame)
+        t = stack.timesteps(10)[k]
+        return [_oracle_gamma(self.s, l, t, state) for l in range(self.s.num_layers)]
+
+
+def test_denoise_step_matches_oracle_chain():
+    L = lib()
+    _banner("denoise step 18 layers")
+    rig = StackRig(S3, 3)
+    s = S3
+    gam = rig.oracle_gammas(2, 0)
+    gam32 = np.stack(gam).astype(np.float32)
+    x = synth.flow_x(s, 2)
+    x_d = dev(x)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.pa_denoise_step(rig.sc.ring, rig.st, x_d, dev(gam32), s.model_dim, flag, rig.ws, rig.wsb)
+    torch.cuda.synchronize()
+    caches = [rig.sc.cached_context(l) for l in range(s.num_layers)]
+    x1, trace = stack.denoise_step(synth.widen(x), [g.astype(np.float32).astype(np.float64) for g in gam], s.eps,
+                                   [synth.widen(w[0]) for w in rig.wq], [synth.widen(w[1]) for w in rig.wq],
+                                   [c[0] for c in caches], [c[1] for c in caches], s.scale, s.n_q_heads,
+                                   s.n_kv_heads, s.head_dim)
+    err = rel_err(synth.widen(host(x_d)), x1)
+    _banner(f"denoise step x rel {err:.3e}")
+    assert err <= BAR
+    assert int(host(flag)[0]) == 0
+
+
+def test_graph_replay_matches_eager():
+    """Capture ten steps in a graph. Between replays the program pushes a
+    frame eagerly and synchronises; every replay must equal an eager run of
+    the same ten steps on the same ring contents, bit for bit."""
+    L = lib()
+    s = S3.with_(name="graph", cfg_id=80, num_layers=4)
+    rig = StackRig(s, s.num_slots)
+    gam = torch.from_numpy(np.stack([np.stack(rig.oracle_gammas(0, k)) for k in range(10)], axis=1)
+                           .astype(np.float32)).cuda()              # [L][10][model]
+    x0 = dev(synth.flow_x(s, 0))
+    x = x0.clone()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def ten_steps():
+        for k in range(10):
+            L.pa_denoise_step(rig.sc.ring, rig.st, x, gam[:, k], 10 * s.model_dim, flag, rig.ws, rig.wsb)
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        ten_steps()
+    for rep in range(3):
+        rig.sc.push(s.num_slots + rep)          # eager work between replays
+        torch.cuda.synchronize()
+        x.copy_(x0)
+        ten_steps()
+        torch.cuda.synchronize()
+        eager = host(x).copy()
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(x), eager), f"replay {rep} differs from eager"
+    assert int(host(flag)[0]) == 0
+    del g
+
+
+@pytest.mark.timeout(900)
+def test_finite_over_10k_frames_18_layers():
+    """The 18-layer stack in bf16 over 10^4 streamed frames, each a fresh
+    x ~ N(0, I) flow initialisation, ten steps per frame (the stress of
+    Table 5 in the Reflex review): no NaN or Inf anywhere in the norm outputs
+    or the stream."""
+    L = lib()
+    s = S3
+    rig = StackRig(s, s.num_slots)
+    layers = list(range(s.num_layers))
+    mlp = _mlp_dev(s, layers)
+    ts = stack.timesteps(10)
+    gamma = torch.empty((s.num_layers, 10, s.model_dim), dtype=torch.float32, device="cuda")
+    gwsb = L.ada_gamma_workspace_bytes(mlp, 10)
+    gws = torch.empty(gwsb, dtype=torch.uint8, device="cuda")
+    x = torch.empty((s.n_dyn, s.model_dim), dtype=torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = [tuple(dev(a) for a in synth.frame_kv(s, 1000 + i)) for i in range(4)]
+    state = torch.empty(s.state_dim, dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for k in range(10):
+            L.pa_denoise_step(rig.sc.ring, rig.st, x, gamma[:, k], 10 * s.model_dim, flag, rig.ws, rig.wsb)
+    n_frames = 10_000
+    chunk = 500
+    maxabs = torch.zeros(1, dtype=torch.float32, device="cuda")
+    for c0 in range(0, n_frames, chunk):
+        xs = dev(synth.normal((chunk, s.n_dyn, s.model_dim), "bf16", s.cfg_id, synth.T_X, 7, c0))
+        sts = dev(synth.normal((chunk, s.state_dim), "bf16", s.cfg_id, synth.T_STATE, 7, c0))
+        for i in range(chunk):
+            kk, vv = pool[(c0 + i) % 4]
+            rig.sc.ring.push_frame(kk, vv)
+            state.copy_(sts[i])
+            L.ada_gamma(mlp, ts, state, gamma, gws, gwsb)
+            x.copy_(xs[i])
+            g.replay()
+        torch.cuda.synchronize()
+        xf = (x.to(torch.int32) << 16).view(torch.float32)
+        maxabs = torch.maximum(maxabs, xf.abs().max().reshape(1))
+        _banner(f"stress frames {c0 + chunk} flag={int(flag.item())} max|x|={float(maxabs.item()):.3f}")
+        assert int(flag.item()) == 0
+    assert bool(torch.isfinite(maxabs).all())
