@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of partitioned attention over a ring-buffer KV cache on one MI355X.
+
+Headline workload (``--workload long_history_18L``, the default): 18 layers,
+8 query heads sharing 1 KV head of width 256, bf16; a pinned prefix of 256
+tokens and a sliding window of 8 frames x 768 tokens in the ring; a 51-token
+dynamic suffix; 10 denoising steps per frame; a new frame pushed (and the
+oldest evicted) every 10 steps. One step = one partitioned-attention pass
+over all 18 layers (split-KV partials + log-sum-exp combine) with that
+step's suffix Q/K/V; the frame push is inside the timed loop, once per 10
+steps. Inputs are seeded synthetic tensors already resident in HBM.
+
+Reported beside it in the same JSON line: the whole denoising step of the
+Pi0.5-like 18-layer stack (AdaRMSNorm fused into the packed QKV projection,
+partitioned attention over a 48 + 2 x 768 token cache, out-projection with
+residual, Euler update; the gamma MLP batched once per frame), replayed as
+a captured graph, in microseconds per step.
+
+``roofline`` describes the split-KV partial kernel, timed live with HIP
+events recorded around it on the launch stream. ``cpu_baseline`` is the
+float64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "denoise steps/sec + HBM GB/s (% roofline), Pi0.5-like 18L partitioned attn"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_work(s, cached_tokens):
+    """Algorithmic bytes and flops of one partial-kernel launch over all layers.
+
+    Bytes: the cached K and V read once, plus Q and the suffix K/V (partials,
+    padding and the combine's output are not counted). Flops: QK^T and PV,
+    2 * M * T * D each, M = tokens x heads, T = cached + suffix keys.
+    """
+    L, D, hq, hkv, n = s.num_layers, s.head_dim, s.n_q_heads, s.n_kv_heads, s.n_dyn
+    kv_cached = 2 * L * cached_tokens * hkv * D * 2
+    q_bytes = L * n * hq * D * 2
+    dyn = 2 * L * n * hkv * D * 2
+    t = cached_tokens + n
+    flops = 2 * 2 * L * n * hq * t * D
+    return kv_cached + q_bytes + dyn, flops, kv_cached
+
+
+def bench_long_history(args, torch, L, configs, synth):
+    s = configs.LONG_18L
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
+    k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
+                              s.tokens_per_frame, L.PA_BF16), k_buf, v_buf)
+    pk, pv = synth.pin_kv(s)
+    ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
+    log("generating the frame pool and step inputs")
+    pool = [tuple(dev(a) for a in synth.frame_kv(s, f)) for f in range(4)]
+    steps_in = [tuple(dev(a) for a in synth.suffix_qkv(s, 0, k)) for k in range(s.steps_per_frame)]
+    for f in range(s.num_slots):
+        ring.push_frame(*pool[f % 4])
+    args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits)
+    wsb = L.pattn_workspace_bytes(ring, args_)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    frame = [s.num_slots]
+
+    def one_step(i, ev=None):
+        if i % s.steps_per_frame == 0:
+            ring.push_frame(*pool[frame[0] % 4])
+            frame[0] += 1
+        q, kd, vd = steps_in[i % s.steps_per_frame]
+        if ev is None:
+            L.pattn_step(ring, args_, q, kd, vd, out, ws, wsb, stream)
+        else:
+            L.pattn_step_timed(ring, args_, q, kd, vd, out, ws, wsb, stream, ev[0].cuda_event, ev[1].cuda_event)
+
+    for i in range(args.warmup):
+        one_step(i)
+    events = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)        # creates the events; the library re-records them
+        events.append((a, b))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in events]
+    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    cached = s.pin_tokens + s.num_slots * s.tokens_per_frame
+    algo_bytes, flops, kv_bytes = attention_work(s, cached)
+    res = {
+        "elapsed_s": elapsed,
+        "steps_per_s": args.steps / elapsed,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "partial_us": avg_kern_s * 1e6,
+        "partial_tflops": flops / avg_kern_s / 1e12,
+        "partial_gbs": algo_bytes / avg_kern_s / 1e9,
+        "kv_gbs_step": kv_bytes / (elapsed / args.steps) / 1e9,
+        "algo_bytes": algo_bytes,
+        "flops": flops,
+        "splits": args.splits,
+        "frames": frame[0],
+    }
+    ring.close()
+    return res
+
+
+def bench_stack(args, torch, L, configs, synth):
+    """Whole 18-layer denoising step of the Pi0.5-like stack, graph-replayed."""
+    s = configs.PI05_18L
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    import numpy as np
+    shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
+    k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
+                              s.tokens_per_frame, L.PA_BF16), k_buf, v_buf)
+    pk, pv = synth.pin_kv(s)
+    ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
+    pool = [tuple(dev(a) for a in synth.frame_kv(s, f)) for f in range(4)]
+    for f in range(s.num_slots):
+        ring.push_frame(*pool[f % 4])
+    log("generating 18 layers of projection and gamma-MLP weights")
+    pw = [synth.proj_weights(s, l) for l in range(s.num_layers)]
+    wqkv = dev(np.stack([w[0] for w in pw]))
+    wo = dev(np.stack([w[1] for w in pw]))
+    mw = [synth.mlp_weights(s, l) for l in range(s.num_layers)]
+    mlp = L.ada_mlp(*(dev(np.stack([w[i] for w in mw])) for i in range(4)), s.num_layers, s.cond_emb,
+                    s.state_dim, s.hidden_dim, s.model_dim)
+    st = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, wqkv, wo, s.eps, s.scale, 0.1)
+    wsb = L.pa_denoise_step_workspace_bytes(ring, st)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    gamma = torch.empty((s.num_layers, s.steps_per_frame, s.model_dim), dtype=torch.float32, device="cuda")
+    gwsb = L.ada_gamma_workspace_bytes(mlp, s.steps_per_frame)
+    gws = torch.empty(gwsb, dtype=torch.uint8, device="cuda")
+    ts = [1.0 - k / s.steps_per_frame for k in range(s.steps_per_frame)]
+    x = torch.empty((s.n_dyn, s.model_dim), dtype=torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n_frames = args.stack_frames
+    xs = dev(synth.normal((n_frames, s.n_dyn, s.model_dim), "bf16", s.cfg_id, synth.T_X, 11))
+    states = dev(synth.normal((n_frames, s.state_dim), "bf16", s.cfg_id, synth.T_STATE, 11))
+    state = torch.empty(s.state_dim, dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        for k in range(s.steps_per_frame):
+            L.pa_denoise_step(ring, st, x, gamma[:, k], s.steps_per_frame * s.model_dim, flag, ws, wsb)
+
+    def frame(i):
+        ring.push_frame(*pool[i % 4])
+        state.copy_(states[i % n_frames])
+        L.ada_gamma(mlp, ts, state, gamma, gws, gwsb)
+        x.copy_(xs[i % n_frames])
+        g.replay()
+
+    for i in range(2):
+        frame(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_frames):
+        frame(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    # the ten steps alone (graph replays back to back, no push / gamma)
+    t1 = time.perf_counter()
+    for i in range(n_frames):
+        g.replay()
+    torch.cuda.synchronize()
+    el_steps = time.perf_counter() - t1
+    ring.close()
+    return {
+        "workload": "pi05_like_18L_stack",
+        "us_per_step": el_steps / (n_frames * s.steps_per_frame) * 1e6,
+        "steps_per_s": n_frames * s.steps_per_frame / el_steps,
+        "frames_per_s_incl_push_gamma": n_frames / el,
+        "us_per_frame_incl_push_gamma": el / n_frames * 1e6,
+        "frames_timed": n_frames,
+        "nonfinite_flag": int(flag.item()),
+        "config": {"layers": 18, "model_dim": 1024, "q_heads": 8, "kv_heads": 1, "head_dim": 256,
+                   "pin_tokens": 48, "window": "2x768", "suffix": 51, "steps_per_frame": 10},
+    }
+
+
+def cpu_baseline(budget_s):
+    """Time the float64 CPU oracle on a bounded sample of the long-history step."""
+    import numpy as np
+    from oracle.attention import full_attention
+    from partitioned_kv_cache_amd import configs, synth
+    s = configs.LONG_18L
+    pk, pv = synth.pin_kv(s)
+    frames = [synth.frame_kv(s, f % 4) for f in range(s.num_slots)]
+    q, kd, vd = synth.suffix_qkv(s, 0, 0)
+    ctx = []
+    for l in range(s.num_layers):
+        ck = np.concatenate([synth.widen(pk[l])] + [synth.widen(f[0][l]) for f in frames] + [synth.widen(kd[l])])
+        cv = np.concatenate([synth.widen(pv[l])] + [synth.widen(f[1][l]) for f in frames] + [synth.widen(vd[l])])
+        ctx.append((synth.widen(q[l]), ck, cv))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    layers_done = 0
+    t0 = time.perf_counter()
+    while True:
+        for l in range(s.num_layers):
+            full_attention(ctx[l][0], ctx[l][1], ctx[l][2], s.scale)
+            layers_done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    steps = layers_done / s.num_layers
+    return {"value": steps / el, "unit": "denoise steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{layers_done} layer-attentions ({steps:.2f} 18-layer steps) of the long-history step, "
+                      f"float64 NumPy, {el:.1f} s; cpu: {_cpu_model()}"}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--splits", type=int, default=0, help="KV splits per layer (0 = library default)")
+    ap.add_argument("--stack-frames", type=int, default=50)
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is built for a "
+              "single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from partitioned_kv_cache_amd import _lib as L, configs, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    lh = bench_long_history(args, torch, L, configs, synth)
+    log(f"long history: {lh['steps_per_s']:.1f} steps/s, partial kernel {lh['partial_us']:.1f} us "
+        f"({lh['partial_tflops']:.0f} TFLOP/s, {lh['partial_gbs']:.0f} GB/s)")
+    stack = None
+    if not args.no_stack:
+        stack = bench_stack(args, torch, L, configs, synth)
+        log(f"pi05 18L stack: {stack['us_per_step']:.1f} us/step")
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(args.cpu_budget)
+        log(f"cpu oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
+    s = configs.LONG_18L
+    line = {
+        "metric": METRIC,
+        "value": lh["steps_per_s"],
+        "unit": "denoise steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": lh["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q, resident in HBM)",
+        "config": {"workload": "long_history_18L", "layers": s.num_layers, "q_heads": s.n_q_heads,
+                   "kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "pin_tokens": s.pin_tokens,
+                   "window": f"{s.num_slots}x{s.tokens_per_frame}", "suffix": s.n_dyn,
+                   "steps_per_frame": s.steps_per_frame, "kv_splits": lh["splits"] or "default"},
+        "frames_per_s": lh["steps_per_s"] / s.steps_per_frame,
+        "roofline": {"bound": "mfma", "achieved": round(lh["partial_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(lh["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "partial_mfma<256>", "kernel_us": round(lh["partial_us"], 3),
+                     "flops_per_launch": lh["flops"], "algo_bytes_per_launch": lh["algo_bytes"]},
+        "hbm": {"achieved": round(lh["partial_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(lh["partial_gbs"] / HBM_PEAK_GBS, 4),
+                "kv_stream_gbs_whole_step": round(lh["kv_gbs_step"], 1)},
+        "cpu_baseline": cpu,
+    }
+    if stack is not None:
+        line["pi05_18L_full_step"] = stack
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,6 +12,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# torch first: its HIP runtime is then the one this library binds to, so
+# torch's streams, events and allocations are valid handles here.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpattn.so")
 

@@ -21,13 +21,19 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace pa {
 
-constexpr int KT = 32;           // keys per MFMA tile
-constexpr int MFMA_WAVES = 4;    // waves per workgroup, 32 query rows each
+constexpr int KT = 32;           // key granularity of splits, keys per LDS tile
+constexpr int MFMA_WAVES = 8;    // waves per workgroup: two per SIMD, 32 query rows each
+constexpr int MFMA_OCC = 1;      // workgroups per CU
+constexpr int NBUF = 4;          // K/V tile buffers in the LDS ring: NBUF - 1 tiles in flight
+constexpr int N_XCD = 8;         // accelerator complex dies, one L2 each
 constexpr int ROWS_PER_WG = MFMA_WAVES * 32;
+constexpr float RESCALE_SLACK = 8.f;   // log2 units the running max may lag the true max
 constexpr int VALU_ROWS = 4;     // query rows per workgroup of the vector kernels
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -117,40 +123,167 @@ __global__ __launch_bounds__(256) void partial_valu(const T* q, long long q_laye
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA partial. Each wave owns 32 query rows; the workgroup stages one
-// tile of KT keys at a time in LDS (K row-major, V transposed) and every
-// wave computes
+// bf16 MFMA partial. Each wave owns 32 query rows; the workgroup streams the
+// split's keys through LDS in tiles of KT keys and every wave computes
 //     S^T (KT x 32)  = K_tile (KT x D) . Q^T (D x 32)        v_mfma_f32_32x32x16_bf16
 //     O^T (D x 32)  += V_tile^T (D x KT) . P^T (KT x 32)
 // In the transposed form each lane holds one query row's scores, so the
 // softmax statistics are per lane plus one swap with lane ^ 32, and P feeds
 // the second product straight from registers. The K rows fed to the first
-// product are permuted (bits 2 and 3 of the row index swapped) so that
-// after the product every lane holds 8 consecutive keys per 16-key step:
-// exactly the B-operand layout of the second product.
+// product are permuted (bits 2 and 3 of the row index swapped) so that after
+// it every lane holds 8 consecutive keys per 16-key step: exactly the
+// B-operand layout of the second product.
 //
 // MFMA 32x32x16 operand layout (64 lanes, l32 = lane % 32, hi = lane / 32):
 //   A[m][k]: lane holds m = l32, k = 8 hi .. 8 hi + 7
 //   B[k][n]: lane holds n = l32, k = 8 hi .. 8 hi + 7
 //   C[m][n]: lane holds n = l32, m = 8 (r / 4) + 4 hi + r % 4, r = 0 .. 15
 //
-// grid (splits, ceil(M / 128), Lb * Hkv), block 256.
+// Data movement (gfx950):
+// * tiles go global -> LDS by direct-to-LDS loads (global_load_lds, 16 bytes
+//   per lane, lane i landing at base + 16 i), double-buffered: the next
+//   tile's loads are in flight while the current tile is multiplied, and
+//   they cost no registers;
+// * K and V stay token-major, as the ring stores them. A tile is kept in
+//   "planes" of 32 dims: plane p holds dims [32p, 32p + 32) of all KT keys,
+//   64 bytes per key. In a K plane the four 16-byte chunks of key r are
+//   rotated by XOR with (r / 4) % 4, which makes the A-operand reads of 16
+//   different keys hit 16 different bank groups;
+// * V^T operands come from ds_read_b64_tr_b16. Within 16 lanes, lane i
+//   addresses 4 dims of one key (key R + i / 4, dims D0 + 4 (i % 4)); the
+//   transposed read hands lane l the 4 keys R .. R + 3 of dim D0 + l, i.e.
+//   the A operand of O^T = V^T P^T, straight from the token-major tile.
+// Waves whose 32 rows are all padding skip the arithmetic but still load.
+//
+// grid: 1-D, ceil(layers x KV heads x splits / 8) x 8 x row blocks workgroups of 256 threads.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
+// Per-wave arithmetic on one LDS tile of KTILE keys (NKB blocks of 32 keys)
+// for the wave's 32 query rows.
+template <int D, int KTILE>
+__device__ __forceinline__ void tile_math(const char* kb, const char* vb, int koff0, int koff1, int voff, int base,
+                                          int k_end, int hi, float scale_log2, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
+    constexpr int KD = D / 16, DB = D / 32, PLANE = KTILE * 64, NKB = KTILE / 32;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int c = 0; c < NKB; ++c) s[c] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+#pragma unroll
+        for (int c = 0; c < NKB; ++c) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(kb + (kk >> 1) * PLANE + c * 2048 + ((kk & 1) ? koff1 : koff0));
+            s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[c], 0, 0, 0);
+        }
+    }
+    // Row max on the raw scores (scale > 0 keeps the order); keys past the
+    // split's end exist only in its last tile and are masked there alone.
+    float rmax = -INFINITY;
+    if (base + KTILE <= k_end) {
+#pragma unroll
+        for (int c = 0; c < NKB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[c][r]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < NKB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = base + 32 * c + 16 * (r >> 3) + 8 * hi + (r & 7);
+                s[c][r] = key < k_end ? s[c][r] : -INFINITY;
+                rmax = fmaxf(rmax, s[c][r]);
+            }
+    }
+    float tmax = rmax * scale_log2;
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Lazy rescale: keep the reference max unless some row's max got more than
+    // RESCALE_SLACK above it. Exact (numerator and denominator share the
+    // reference); probabilities stay below 2^RESCALE_SLACK.
+    if (__any(tmax > m_run + RESCALE_SLACK)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+        m_run = m_new;
+    }
+    // p = 2^(scale log2e s - m): one FMA and the hardware exp2 (v_exp_f32);
+    // results below 2^-126 flush to zero, far below what a bf16 P can carry.
+    bf16x8 pf[NKB][2];
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NKB; ++c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[c][r], scale_log2, -m_run));
+            psum += p;
+            pf[c][r >> 3][r & 7] = (__bf16)p;
+        }
+    }
+    l_run += psum;
+#pragma unroll
+    for (int c = 0; c < NKB; ++c) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                const char* vp = vb + b * PLANE + c * 2048 + (16 * s2) * 64 + voff;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp));
+                const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 4 * 64));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c][s2], acc[b], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// One LDS tile buffer per (index, size): distinct objects, so the compiler
+// can prove that loads in flight into one buffer never alias reads of another.
+template <int I, int BYTES>
+__device__ __forceinline__ char* lds_buffer() {
+    __shared__ __attribute__((aligned(1024))) char b[BYTES];
+    return b;
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order), leaving the LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 template <int D>
-__global__ __launch_bounds__(MFMA_WAVES * 64, 2) void partial_mfma(const uint16_t* __restrict__ q, long long q_layer,
-                                                                   int hq, int group, int m_rows, KvSource src,
-                                                                   int chunk, float scale_log2, Partials part) {
-    constexpr int KD = D / 16;    // k-steps over the head dimension
-    constexpr int DB = D / 32;    // 32-wide blocks of the output
-    constexpr int KP = D + 8;     // K tile pitch (elements): 16-byte skew per row
-    constexpr int VP = KT + 8;    // V^T tile pitch
-    constexpr int CH = KT * D / 8;  // 16-byte chunks per tile
-    __shared__ __attribute__((aligned(16))) uint16_t ks[KT * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VP];
+__global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
+                                                                          long long q_layer, int hq, int group,
+                                                                          int m_rows, KvSource src, int chunk,
+                                                                          float scale_log2, Partials part, int parts,
+                                                                          int row_blocks) {
+    constexpr int KD = D / 16;               // k-steps over the head dimension
+    constexpr int DB = D / 32;               // 32-wide output blocks = planes
+    constexpr int PLANE = KT * 64;           // bytes per plane (KT keys x 32 dims x 2 B)
+    constexpr int TILE = DB * PLANE;         // bytes per K or V tile
+    constexpr int NBLK = TILE / 1024;        // 1 KB direct-to-LDS loads per tile and tensor
+    constexpr int DPW = (NBLK + MFMA_WAVES - 1) / MFMA_WAVES;   // loads per wave, per tile and tensor
+    static_assert(NBLK % 2 == 0 && (NBLK <= MFMA_WAVES || NBLK % MFMA_WAVES == 0), "tile / wave split");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int split = blockIdx.x, lg = blockIdx.z;
+    // XCD-aware placement. Workgroups go to the 8 XCDs round-robin by id, and
+    // each XCD has its own L2. All row blocks of one (layer, split) read the
+    // same keys, so they are given ids congruent mod 8: same XCD, same L2,
+    // dispatched back to back, and the split's K/V leaves HBM once.
+    const int xcd = blockIdx.x & (N_XCD - 1), slot = blockIdx.x / N_XCD;
+    const int unit = (slot / row_blocks) * N_XCD + xcd;       // (layer, split) index
+    if (unit >= parts * part.lg_count) return;                 // id padding, whole workgroup
+    const int split = unit % parts, lg = unit / parts, rblk = slot % row_blocks;
     const int lb = lg / src.hkv, g = lg % src.hkv;
-    const int row = blockIdx.y * ROWS_PER_WG + wave * 32 + l32;
+    const int row0 = rblk * ROWS_PER_WG + wave * 32;
+    const int row = row0 + l32;
+    const bool active = row0 < m_rows;       // wave-uniform
 
     bf16x8 qf[KD];
     if (row < m_rows) {
@@ -162,76 +295,85 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, 2) void partial_mfma(const uint16_
         for (int kk = 0; kk < KD; ++kk) qf[kk] = bf16x8{};
     }
 
+    const int k_begin = split * chunk, k_end = min(k_begin + chunk, src.total());
+
+    // Base pointers of this (layer, KV head), hoisted so that choosing between
+    // the ring and the suffix buffer is a register select, not a memory load.
+    const int stride = src.hkv * D;                     // elements per token
+    const uint16_t* rk = static_cast<const uint16_t*>(src.ring_k) + lb * src.ring_layer + g * D;
+    const uint16_t* rv = static_cast<const uint16_t*>(src.ring_v) + lb * src.ring_layer + g * D;
+    const uint16_t* dk = static_cast<const uint16_t*>(src.dyn_k) + lb * src.dyn_layer + g * D;
+    const uint16_t* dv = static_cast<const uint16_t*>(src.dyn_v) + lb * src.dyn_layer + g * D;
+    const int n_cached = src.pinned + src.n_slide, pinned = src.pinned, gap = src.pin_cap - src.pinned;
+
+    // Direct-to-LDS loads: one 1 KB load = 16 keys x 64 B of one plane, lane
+    // -> (key, 16-byte chunk). Wave w loads blocks w, w + 8, ... of a tile;
+    // block b is plane b / 2, keys 16 (b % 2) .. + 15. With 8 waves every
+    // block a wave loads has the same keys, so one address per tile serves.
+    const int dma_key = lane >> 2, dma_pos = lane & 3;
+    const int kq = wave & 1;
+    const int key_in_tile = kq * 16 + dma_key;
+    const int kchunk = (dma_pos ^ ((key_in_tile >> 2) & 3)) << 3;   // K plane rotation
+    auto issue_tile = [&](int t, char* kbuf, char* vbuf) {
+        if (DPW * MFMA_WAVES > NBLK && wave >= NBLK) return;         // fewer blocks than waves
+        const int j = min(k_begin + t * KT + key_in_tile, k_end - 1);  // ragged tail: a valid key, masked later
+        const bool dyn = j >= n_cached;
+        const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap);
+        const int off = tok * stride + (wave >> 1) * 32;
+        const uint16_t* kp = (dyn ? dk : rk) + off + kchunk;
+        const uint16_t* vp = (dyn ? dv : rv) + off + (dma_pos << 3);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) {
+            const int blk = __builtin_amdgcn_readfirstlane(wave + i * MFMA_WAVES);
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(kp + i * (MFMA_WAVES / 2) * 32),
+                                             (LDS_AS void*)(kbuf + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(vp + i * (MFMA_WAVES / 2) * 32),
+                                             (LDS_AS void*)(vbuf + blk * 1024), 16, 0, 0);
+        }
+    };
+
+    // per-lane LDS read offsets (key rows within a 32-key block)
+    const int prow = (l32 & ~0xC) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+    const int koff0 = prow * 64 + (((0 + hi) ^ ((prow >> 2) & 3)) << 4);
+    const int koff1 = prow * 64 + (((2 + hi) ^ ((prow >> 2) & 3)) << 4);
+    const int gi = lane >> 4, li = lane & 15;
+    const int voff = (8 * (gi >> 1) + (li >> 2)) * 64 + ((2 * (gi & 1) + ((li & 3) >> 1)) << 4) + ((li & 1) << 3);
+
     f32x16 acc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
-    const int k_begin = split * chunk, k_end = min(k_begin + chunk, src.total());
-    const int prow = (l32 & ~0xC) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
 
-    for (int base = k_begin; base < k_end; base += KT) {
-        for (int c = tid; c < CH; c += MFMA_WAVES * 64) {       // K: row-major
-            const int key = c / (D / 8), dc = c % (D / 8), j = base + key;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (j < k_end) {
-                bool dyn;
-                const long long off = src.offset(lb, g, j, dyn);
-                val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dyn ? src.dyn_k : src.ring_k) + off + dc * 8);
-            }
-            *reinterpret_cast<uint4*>(&ks[key * KP + dc * 8]) = val;
-        }
-        for (int c = tid; c < CH; c += MFMA_WAVES * 64) {       // V: transposed
-            const int key = c % KT, dc = c / KT, j = base + key;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (j < k_end) {
-                bool dyn;
-                const long long off = src.offset(lb, g, j, dyn);
-                val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dyn ? src.dyn_v : src.ring_v) + off + dc * 8);
-            }
-            const uint16_t* e = reinterpret_cast<const uint16_t*>(&val);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vt[(dc * 8 + i) * VP + key] = e[i];
-        }
+    const int n_tiles = (k_end - k_begin + KT - 1) / KT;
+    // Step through tile t held in ring buffer J: wait for its loads, meet at
+    // the barrier (which also frees buffer J - 1 for reuse), refill that
+    // buffer with tile t + NBUF - 1, multiply tile t.
+    auto step = [&](auto J_, int t) {
+        constexpr int J = decltype(J_)::value;
+        constexpr int JN = (J + NBUF - 1) % NBUF;
+        if (t >= n_tiles) return;
+        const int after = min(NBUF - 2, n_tiles - 1 - t);   // tiles issued after t
+        if (after >= 2)
+            wait_vmem<2 * 2 * DPW>();
+        else if (after == 1)
+            wait_vmem<2 * DPW>();
+        else
+            wait_vmem<0>();
         __syncthreads();
-
-        f32x16 s = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[prow * KP + 16 * kk + 8 * hi]);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = base + 16 * (r >> 3) + 8 * hi + (r & 7);
-            const float x = key < k_end ? s[r] * scale_log2 : -INFINITY;
-            s[r] = x;
-            tmax = fmaxf(tmax, x);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.f;
-        bf16x8 pf[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = exp2f(s[r] - m_new);
-            psum += p;
-            pf[r >> 3][r & 7] = (__bf16)p;
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) acc[b] *= alpha;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(32 * b + l32) * VP + 16 * s2 + 8 * hi]);
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], acc[b], 0, 0, 0);
-            }
-        }
-        __syncthreads();
+        if (t + NBUF - 1 < n_tiles) issue_tile(t + NBUF - 1, lds_buffer<JN, TILE>(), lds_buffer<NBUF + JN, TILE>());
+        if (active)
+            tile_math<D, KT>(lds_buffer<J, TILE>(), lds_buffer<NBUF + J, TILE>(), koff0, koff1, voff,
+                             k_begin + t * KT, k_end, hi, scale_log2, qf, acc, m_run, l_run);
+    };
+    static_assert(NBUF == 4, "the prologue and the unrolled loop below assume four buffers");
+    issue_tile(0, lds_buffer<0, TILE>(), lds_buffer<NBUF + 0, TILE>());
+    if (1 < n_tiles) issue_tile(1, lds_buffer<1, TILE>(), lds_buffer<NBUF + 1, TILE>());
+    if (2 < n_tiles) issue_tile(2, lds_buffer<2, TILE>(), lds_buffer<NBUF + 2, TILE>());
+    for (int t = 0; t < n_tiles; t += NBUF) {
+        step(std::integral_constant<int, 0>{}, t);
+        step(std::integral_constant<int, 1>{}, t + 1);
+        step(std::integral_constant<int, 2>{}, t + 2);
+        step(std::integral_constant<int, 3>{}, t + 3);
     }
 
     l_run += __shfl_xor(l_run, 32);
@@ -387,11 +529,11 @@ struct Plan {
 
 static int valu_row_blocks(int m) { return (m + VALU_ROWS - 1) / VALU_ROWS; }
 
-// Choose the split count: enough workgroups for two per CU on 256 CUs, but
-// no split shorter than 128 keys.
+// Choose the split count: as many workgroups as fit at once (one per CU on
+// 256 CUs) without a partial second wave, and no split shorter than 128 keys.
 static int default_splits(int lg_count, int row_blocks, int max_keys) {
     const int base = lg_count * row_blocks;
-    int s = (512 + base - 1) / base;
+    int s = 256 * MFMA_OCC / base;
     int by_len = max_keys / 128;
     if (by_len < 1) by_len = 1;
     if (s > by_len) s = by_len;
@@ -475,14 +617,19 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
     const float scale_log2 = scale * 1.4426950408889634f;
     const int d = r->cfg.head_dim;
     if (p.mfma) {
-        dim3 grid(p.parts, (p.m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG, p.lg_count);
+        const int row_blocks = (p.m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG;
+        const int units = p.parts * p.lg_count;
+        const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         if (d == 256)
-            partial_mfma<256><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, scale_log2, part);
+            partial_mfma<256><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk,
+                                                                   scale_log2, part, p.parts, row_blocks);
         else if (d == 128)
-            partial_mfma<128><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, scale_log2, part);
+            partial_mfma<128><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk,
+                                                                   scale_log2, part, p.parts, row_blocks);
         else
-            partial_mfma<64><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, scale_log2, part);
+            partial_mfma<64><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk,
+                                                                  scale_log2, part, p.parts, row_blocks);
     } else {
         dim3 grid(p.parts, valu_row_blocks(p.m_rows), p.lg_count);
         partial_valu<float><<<grid, 256, VALU_ROWS * d * sizeof(float), stream>>>(

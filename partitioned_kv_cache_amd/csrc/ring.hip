@@ -48,7 +48,8 @@ extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, r
     PA_CHECK_ARG(cfg->head_dim % 8 == 0 && cfg->head_dim <= 256, PA_ESHAPE,
                  "rb_create: head_dim %d must be a multiple of 8 and <= 256", cfg->head_dim);
     int64_t seq = (int64_t)cfg->pin_capacity + (int64_t)cfg->num_slots * cfg->tokens_per_frame;
-    PA_CHECK_ARG(seq < (1LL << 31), PA_ESHAPE, "rb_create: P + W*F too large");
+    PA_CHECK_ARG(seq * cfg->num_kv_heads * cfg->head_dim < (1LL << 31), PA_ESHAPE,
+                 "rb_create: (P + W*F) * Hkv * D must stay below 2^31 elements per layer");
     Ring* r = new (std::nothrow) Ring();
     PA_CHECK_ARG(r, PA_EINVAL, "rb_create: out of host memory");
     r->cfg = *cfg;
