@@ -236,6 +236,44 @@ def cpu_baseline(budget_s):
                       f"float64 NumPy, {el:.1f} s; cpu: {_cpu_model()}"}
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "partial_mfma_long_history_traffic.md")
+KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "partitioned_kv_cache_amd", "csrc",
+                             "attention.hip")
+
+
+def stored_traffic():
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings), or
+    None when the summary is missing or the kernel source changed since."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("source_sha256:", "traffic_bytes:")))
+    if fields.get("source_sha256", "").strip() != src:
+        return None
+    try:
+        return int(float(fields["traffic_bytes"].strip()))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mb):
+    """A plain device copy of known size, for scaling the traffic counters."""
+    n = mb * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -255,6 +293,8 @@ def main():
     ap.add_argument("--stack-frames", type=int, default=50)
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB MiB five times (traffic-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is built for a "
@@ -266,6 +306,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
     lh = bench_long_history(args, torch, L, configs, synth)
     log(f"long history: {lh['steps_per_s']:.1f} steps/s, partial kernel {lh['partial_us']:.1f} us "
         f"({lh['partial_tflops']:.0f} TFLOP/s, {lh['partial_gbs']:.0f} GB/s)")
@@ -298,7 +341,8 @@ def main():
         "frames_per_s": lh["steps_per_s"] / s.steps_per_frame,
         "roofline": {"bound": "mfma", "achieved": round(lh["partial_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(lh["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "partial_mfma<256>", "kernel_us": round(lh["partial_us"], 3),
+                     "traffic": stored_traffic(), "kernel": "partial_mfma<256>",
+                     "kernel_us": round(lh["partial_us"], 3),
                      "flops_per_launch": lh["flops"], "algo_bytes_per_launch": lh["algo_bytes"]},
         "hbm": {"achieved": round(lh["partial_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lh["partial_gbs"] / HBM_PEAK_GBS, 4),

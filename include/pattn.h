@@ -122,7 +122,7 @@ typedef struct {
     int32_t n_dyn;             /* N >= 1 dynamic-suffix tokens */
     float   scale;             /* the 1/sqrt(d) of Eq. 1, applied once */
     int32_t out_dtype;         /* PA_F32 or PA_BF16 */
-    int32_t num_splits;        /* KV splits per layer; 0 = library's choice */
+    int32_t num_splits;        /* KV splits per layer, 0..127; 0 = library's choice */
 } pattn_args;
 
 /* Workspace needed by pattn_step for these arguments (0 on invalid input). */
@@ -230,7 +230,11 @@ pa_status ada_rmsnorm(const void* x, int32_t rows, const ada_mlp* mlp, int32_t l
  * x bf16 [rows][model_dim]; w_qkv bf16 [(Hq + 2 Hkv) * D][model_dim]
  * (nn.Linear layout: q heads, then k heads, then v heads);
  * q bf16 [rows][Hq][D], k_dyn and v_dyn bf16 [rows][Hkv][D].
- * rows <= 64; model_dim a multiple of 256; D a multiple of 32. */
+ * rows <= 64; model_dim = 128 x {2, 4, 6, 8, 12, 16}; D a multiple of 32;
+ * x, gamma and w_qkv 16-byte aligned. The norm is fused into the projection
+ * (every workgroup forms its A operand from x on the fly), so the workspace
+ * size is 0 and `workspace` may be NULL. *nonfinite (nullable) gets bit 0 if a
+ * normalised element is NaN or Inf. */
 size_t ada_rmsnorm_qkv_workspace_bytes(int32_t rows, int32_t model_dim);
 pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const float* gamma,
                           float eps, const void* w_qkv, int32_t n_q_heads, int32_t n_kv_heads,
@@ -245,7 +249,8 @@ pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const 
  * and, when x is not NULL, the Euler update of the flow state
  *     x <- bf16(x - dt * h)                       (v = last layer's stream)
  * o bf16 [rows][in_dim]; w_o bf16 [model_dim][in_dim]; h, x bf16 [rows][model_dim].
- * rows <= 64; in_dim a multiple of 256; model_dim a multiple of 32.
+ * rows <= 64; in_dim = 128 x {2, 4, 6, 8, 12, 16}; model_dim a multiple of 32.
+ * *nonfinite (nullable) gets bit 0 if a new h or x element is NaN or Inf.
  * ====================================================================== */
 pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, int32_t in_dim,
                          int32_t model_dim, void* x, float dt, uint32_t* nonfinite, void* stream);
@@ -265,7 +270,7 @@ pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, 
 typedef struct {
     int32_t num_layers;
     int32_t rows;              /* N suffix tokens, <= 64 */
-    int32_t model_dim;         /* multiple of 256 */
+    int32_t model_dim;         /* 128 x {2, 4, 6, 8, 12, 16} */
     int32_t n_q_heads;
     const void* w_qkv;         /* bf16 [L][(Hq + 2 Hkv) * D][model_dim] */
     const void* w_o;           /* bf16 [L][model_dim][Hq * D] */

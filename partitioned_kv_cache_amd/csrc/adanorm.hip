@@ -161,12 +161,19 @@ __global__ __launch_bounds__(256) void rmsnorm_rows(const uint16_t* x, const flo
 
 // ------------------------------------------------- skinny GEMM, A W^T -------
 // C[m][n] = sum_k A[m][k] W[n][k] for m < rows <= 64, bf16 in, FP32 accumulate,
-// with W in nn.Linear layout [N][K]. A workgroup owns 32 output columns; its
-// four waves split K and reduce through LDS. Weight-streaming bound: every
-// W element is read once, by one lane.
+// W in nn.Linear layout [N][K]. Weight streaming: every W element is read
+// once, by one lane, and used by two MFMAs (row blocks 0-31 and 32-63).
+// A workgroup of 8 waves owns 32 output columns; wave w owns the k-range
+// [w K/8, (w+1) K/8) = KS k-steps of 16, issues all of its weight loads at
+// once (so the whole weight matrix is in flight across the GPU), and the
+// eight partial sums meet in LDS.
 //   A operand (32 rows x 16 k): lane row l32, k 8hi..8hi+7 -> 16 B of A's row
 //   B operand (16 k x 32 cols): lane col l32, k 8hi..8hi+7 -> 16 B of W's row
+// With NORM the A operand is AdaRMSNorm's output formed on the fly,
+// bf16(x[m][k] * rsqrt(mean_k x[m]^2 + eps) * gamma[k]), the mean of
+// squares taken in FP32 by the workgroup before the products.
 enum GemmMode { GEMM_QKV = 0, GEMM_OPROJ = 1 };
+constexpr int GEMM_WAVES = 8;
 
 struct GemmOut {
     // GEMM_QKV: columns [0, nq) -> q, [nq, nq+nk) -> k, [nq+nk, nq+2nk) -> v
@@ -176,27 +183,99 @@ struct GemmOut {
     uint32_t* nonfinite;
 };
 
-template <int MODE>
-__global__ __launch_bounds__(256) void gemm_awt(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w, int rows,
-                                                int K, int N, GemmOut out) {
-    __shared__ float red[4][2][16][64];
+template <int MODE, int KS, bool NORM>
+__global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t* __restrict__ a,
+                                                                 const float* __restrict__ gamma, float eps,
+                                                                 const uint16_t* __restrict__ w, int rows, int N,
+                                                                 GemmOut out) {
+    constexpr int K = GEMM_WAVES * KS * 16;
+    __shared__ float red[GEMM_WAVES][2][16][64];
+    __shared__ float rinv_s[64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int n0 = blockIdx.x * 32;
-    const int kw = K / 4, k0 = wave * kw;
-    const bool two = rows > 32;
-    f32x16 c0 = f32x16{}, c1 = f32x16{};
-    const uint16_t* wp = w + (long long)(n0 + l32) * K + 8 * hi;
-    const uint16_t* ap0 = a + (long long)l32 * K + 8 * hi;
-    const uint16_t* ap1 = a + (long long)(32 + l32) * K + 8 * hi;
+    const int k0 = wave * KS * 16 + 8 * hi;
+
+    bf16x8 wf[KS];
+    const uint16_t* wp = w + (long long)(n0 + l32) * K + k0;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) wf[i] = *reinterpret_cast<const bf16x8*>(wp + 16 * i);
+
     const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
-    for (int k = k0; k < k0 + kw; k += 16) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(wp + k);
-        const bf16x8 x0 = r0 ? *reinterpret_cast<const bf16x8*>(ap0 + k) : bf16x8{};
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, b, c0, 0, 0, 0);
-        if (two) {
-            const bf16x8 x1 = r1 ? *reinterpret_cast<const bf16x8*>(ap1 + k) : bf16x8{};
-            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, b, c1, 0, 0, 0);
+    bf16x8 a0[KS], a1[KS];
+    if (!NORM) {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(a + (long long)l32 * K + k0 + 16 * i) : bf16x8{};
+            a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
         }
+    } else {
+        // mean of squares per row, FP32: wave w takes rows w, w + 8, ...; all
+        // of a wave's loads are issued before any is used
+        constexpr int RPW = 64 / GEMM_WAVES;        // rows per wave
+        constexpr int LPR = (K + 511) / 512;        // 16-byte loads per lane and row
+        uint4 raw[RPW][LPR];
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int r = wave + rr * GEMM_WAVES;
+#pragma unroll
+            for (int c = 0; c < LPR; ++c)
+                raw[rr][c] = (r < rows && c * 512 + lane * 8 < K)
+                                 ? *reinterpret_cast<const uint4*>(a + (long long)r * K + c * 512 + lane * 8)
+                                 : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < LPR; ++c) {
+                const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][c]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float v = bf2f(e[u]);
+                    ss += v * v;
+                }
+            }
+            ss = wsum(ss);
+            const int r = wave + rr * GEMM_WAVES;
+            if (lane == 0 && r < rows) rinv_s[r] = 1.f / sqrtf(ss / (float)K + eps);
+        }
+        __syncthreads();
+        const float ri0 = r0 ? rinv_s[l32] : 0.f, ri1 = r1 ? rinv_s[32 + l32] : 0.f;
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            const int k = k0 + 16 * i;
+            const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
+            const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
+            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+            if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)l32 * K + k);
+            if (r1) x1 = *reinterpret_cast<const uint4*>(a + (long long)(32 + l32) * K + k);
+            const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
+            const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a0[i][u] = (__bf16)(bf2f(e0[u]) * ri0 * gg[u]);
+                a1[i][u] = (__bf16)(bf2f(e1[u]) * ri1 * gg[u]);
+            }
+        }
+        // every workgroup forms the same normalised rows; the first reports
+        // a non-finite element (padding rows are zeros)
+        if (blockIdx.x == 0 && out.nonfinite) {
+            bool bad = false;
+#pragma unroll
+            for (int i = 0; i < KS; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) bad |= !finite_f((float)a0[i][u]) || !finite_f((float)a1[i][u]);
+            if (__any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
+        }
+    }
+
+    f32x16 c0 = f32x16{}, c1 = f32x16{};
+    const bool two = rows > 32;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wf[i], c0, 0, 0, 0);
+        if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wf[i], c1, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -204,39 +283,60 @@ __global__ __launch_bounds__(256) void gemm_awt(const uint16_t* __restrict__ a, 
         red[wave][1][r][lane] = c1[r];
     }
     __syncthreads();
-    // wave w finishes registers r = 4w .. 4w+3 of both row blocks
+    // wave w finishes 4 of the 32 (block, register) pairs
     bool bad = false;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int u = 0; u < 4; ++u) {
+        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
+        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int n = n0 + l32;
+        if (m >= rows) continue;
+        float v = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = wave * 4 + rr;
-            const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const int n = n0 + l32;
-            if (m >= rows || n >= N) continue;
-            const float v = red[0][blk][r][lane] + red[1][blk][r][lane] + red[2][blk][r][lane] + red[3][blk][r][lane];
-            if (MODE == GEMM_QKV) {
-                if (n < out.nq)
-                    out.q[(long long)m * out.nq + n] = f2bf(v);
-                else if (n < out.nq + out.nk)
-                    out.k[(long long)m * out.nk + (n - out.nq)] = f2bf(v);
-                else
-                    out.v[(long long)m * out.nk + (n - out.nq - out.nk)] = f2bf(v);
-            } else {
-                uint16_t* hp = out.h + (long long)m * N + n;
-                const float hn = bf2f(f2bf(bf2f(*hp) + v));
-                *hp = f2bf(hn);
-                bad |= !finite_f(hn);
-                if (out.x) {
-                    uint16_t* xp = out.x + (long long)m * N + n;
-                    const float xn = bf2f(*xp) - out.dt * hn;
-                    bad |= !finite_f(xn);
-                    *xp = f2bf(xn);
-                }
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        if (MODE == GEMM_QKV) {
+            if (n < out.nq)
+                out.q[(long long)m * out.nq + n] = f2bf(v);
+            else if (n < out.nq + out.nk)
+                out.k[(long long)m * out.nk + (n - out.nq)] = f2bf(v);
+            else
+                out.v[(long long)m * out.nk + (n - out.nq - out.nk)] = f2bf(v);
+        } else {
+            uint16_t* hp = out.h + (long long)m * N + n;
+            const float hn = bf2f(f2bf(bf2f(*hp) + v));
+            *hp = f2bf(hn);
+            bad |= !finite_f(hn);
+            if (out.x) {
+                uint16_t* xp = out.x + (long long)m * N + n;
+                const float xn = bf2f(*xp) - out.dt * hn;
+                bad |= !finite_f(xn);
+                *xp = f2bf(xn);
             }
         }
     }
     if (MODE == GEMM_OPROJ && out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
+}
+
+// K = 128 * KS; the k-step counts the library is built for.
+static bool gemm_k_supported(int K) {
+    if (K % 128) return false;
+    const int ks = K / 128;
+    return ks == 2 || ks == 4 || ks == 6 || ks == 8 || ks == 12 || ks == 16;
+}
+
+template <int MODE, bool NORM>
+static hipError_t launch_gemm(const uint16_t* a, const float* gamma, float eps, const uint16_t* w, int rows, int K,
+                              int N, const GemmOut& o, hipStream_t s) {
+    const dim3 grid(N / 32), block(GEMM_WAVES * 64);
+    switch (K / 128) {
+        case 2: gemm_skinny<MODE, 2, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
+        case 4: gemm_skinny<MODE, 4, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
+        case 6: gemm_skinny<MODE, 6, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
+        case 8: gemm_skinny<MODE, 8, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
+        case 12: gemm_skinny<MODE, 12, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
+        default: gemm_skinny<MODE, 16, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
+    }
+    return hipGetLastError();
 }
 
 static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -334,36 +434,38 @@ extern "C" pa_status ada_rmsnorm(const void* x, int32_t rows, const ada_mlp* m, 
 }
 
 extern "C" size_t ada_rmsnorm_qkv_workspace_bytes(int32_t rows, int32_t model_dim) {
-    if (rows < 1 || model_dim < 1) return 0;
-    return align_up((size_t)rows * model_dim * sizeof(uint16_t), 256);
+    (void)rows;
+    (void)model_dim;
+    return 0;   // the norm is fused into the projection; kept for ABI stability
 }
 
 extern "C" pa_status ada_rmsnorm_qkv(const void* x, int32_t rows, int32_t model_dim, const float* gamma, float eps,
                                      const void* w_qkv, int32_t hq, int32_t hkv, int32_t d, void* q, void* k_dyn,
                                      void* v_dyn, uint32_t* nonfinite, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
-    PA_CHECK_ARG(x && gamma && w_qkv && q && k_dyn && v_dyn && ws, PA_EINVAL, "ada_rmsnorm_qkv: null argument");
-    PA_CHECK_ARG(al16(x) && al16(w_qkv) && al16(ws), PA_EINVAL, "ada_rmsnorm_qkv: x, w_qkv, workspace must be 16-byte aligned");
+    (void)ws;
+    (void)ws_bytes;
+    PA_CHECK_ARG(x && gamma && w_qkv && q && k_dyn && v_dyn, PA_EINVAL, "ada_rmsnorm_qkv: null argument");
+    PA_CHECK_ARG(al16(x) && al16(w_qkv) && al16(gamma), PA_EINVAL,
+                 "ada_rmsnorm_qkv: x, gamma and w_qkv must be 16-byte aligned");
     PA_CHECK_ARG(rows >= 1 && rows <= 64, PA_ESHAPE, "ada_rmsnorm_qkv: rows %d not in [1, 64]", rows);
-    PA_CHECK_ARG(model_dim >= 64 && model_dim % 64 == 0, PA_ESHAPE, "ada_rmsnorm_qkv: model_dim must be a multiple of 64");
+    PA_CHECK_ARG(gemm_k_supported(model_dim), PA_ESHAPE,
+                 "ada_rmsnorm_qkv: model_dim %d must be 128 x {2, 4, 6, 8, 12, 16}", model_dim);
     PA_CHECK_ARG(hq >= 1 && hkv >= 1 && hq % hkv == 0 && d >= 32 && d % 32 == 0, PA_ESHAPE,
                  "ada_rmsnorm_qkv: need Hq a multiple of Hkv and D a multiple of 32");
     PA_CHECK_ARG(eps >= 0.f, PA_EINVAL, "ada_rmsnorm_qkv: eps must be >= 0");
-    PA_CHECK_ARG(ws_bytes >= ada_rmsnorm_qkv_workspace_bytes(rows, model_dim), PA_ERANGE,
-                 "ada_rmsnorm_qkv: workspace too small");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    uint16_t* y = static_cast<uint16_t*>(ws);
-    rmsnorm_rows<uint16_t><<<rows, 256, 0, s>>>(static_cast<const uint16_t*>(x), gamma, model_dim, eps, y, nonfinite);
-    PA_LAUNCHED();
     GemmOut o{};
+    o.nonfinite = nonfinite;
     o.q = static_cast<uint16_t*>(q);
     o.k = static_cast<uint16_t*>(k_dyn);
     o.v = static_cast<uint16_t*>(v_dyn);
     o.nq = hq * d;
     o.nk = hkv * d;
     const int n = (hq + 2 * hkv) * d;
-    gemm_awt<GEMM_QKV><<<n / 32, 256, 0, s>>>(y, static_cast<const uint16_t*>(w_qkv), rows, model_dim, n, o);
-    PA_LAUNCHED();
+    const hipError_t e = launch_gemm<GEMM_QKV, true>(static_cast<const uint16_t*>(x), gamma, eps,
+                                                     static_cast<const uint16_t*>(w_qkv), rows, model_dim, n, o,
+                                                     static_cast<hipStream_t>(stream));
+    PA_CHECK_ARG(e == hipSuccess, PA_EDEVICE, "ada_rmsnorm_qkv: launch failed: %s", hipGetErrorString(e));
     return PA_OK;
 }
 
@@ -373,7 +475,8 @@ extern "C" pa_status oproj_residual(const void* o, const void* w_o, void* h, int
     PA_CHECK_ARG(o && w_o && h, PA_EINVAL, "oproj_residual: null argument");
     PA_CHECK_ARG(al16(o) && al16(w_o), PA_EINVAL, "oproj_residual: o and w_o must be 16-byte aligned");
     PA_CHECK_ARG(rows >= 1 && rows <= 64, PA_ESHAPE, "oproj_residual: rows %d not in [1, 64]", rows);
-    PA_CHECK_ARG(in_dim >= 64 && in_dim % 64 == 0, PA_ESHAPE, "oproj_residual: in_dim must be a multiple of 64");
+    PA_CHECK_ARG(gemm_k_supported(in_dim), PA_ESHAPE, "oproj_residual: in_dim %d must be 128 x {2, 4, 6, 8, 12, 16}",
+                 in_dim);
     PA_CHECK_ARG(model_dim >= 32 && model_dim % 32 == 0, PA_ESHAPE, "oproj_residual: model_dim must be a multiple of 32");
     PA_CHECK_ARG(isfinite(dt), PA_EINVAL, "oproj_residual: dt must be finite");
     GemmOut g{};
@@ -381,8 +484,9 @@ extern "C" pa_status oproj_residual(const void* o, const void* w_o, void* h, int
     g.x = static_cast<uint16_t*>(x);
     g.dt = dt;
     g.nonfinite = nonfinite;
-    gemm_awt<GEMM_OPROJ><<<model_dim / 32, 256, 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(w_o), rows, in_dim, model_dim, g);
-    PA_LAUNCHED();
+    const hipError_t e = launch_gemm<GEMM_OPROJ, false>(static_cast<const uint16_t*>(o), nullptr, 0.f,
+                                                        static_cast<const uint16_t*>(w_o), rows, in_dim, model_dim, g,
+                                                        static_cast<hipStream_t>(stream));
+    PA_CHECK_ARG(e == hipSuccess, PA_EDEVICE, "oproj_residual: launch failed: %s", hipGetErrorString(e));
     return PA_OK;
 }

@@ -464,23 +464,34 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m
     const int row = blockIdx.x * VALU_ROWS + wave, lg = blockIdx.y;
     if (row >= m_rows) return;
     const int lb = lg / hkv, g = lg % hkv;
-    float mx = -INFINITY;
-    for (int s = 0; s < n_parts; ++s) mx = fmaxf(mx, part.ml[part.idx(s, lg, row)].x);
-    float lsum = 0.f;
-    for (int s = 0; s < n_parts; ++s) {
-        const float2 ml = part.ml[part.idx(s, lg, row)];
-        if (ml.x != -INFINITY) lsum += ml.y * exp2f(ml.x - mx);
-    }
+    // lane s (and s + 64) holds partial s's statistics
+    float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = make_float2(-INFINITY, 0.f);
+    if (lane < n_parts) ml0 = part.ml[part.idx(lane, lg, row)];
+    if (lane + 64 < n_parts) ml1 = part.ml[part.idx(lane + 64, lg, row)];
+    const float mx = wave_max(fmaxf(ml0.x, ml1.x));
+    // weights 2^(m_s - m*); an empty partial (m = -inf, l = 0) weighs 0
+    const float w0 = ml0.x == -INFINITY ? 0.f : exp2f(ml0.x - mx);
+    const float w1 = ml1.x == -INFINITY ? 0.f : exp2f(ml1.x - mx);
+    const float lsum = wave_sum(w0 * ml0.y + w1 * ml1.y);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     TO* op = out + lb * out_layer + ((long long)(row / group) * hq + g * group + row % group) * D;
     for (int d = lane * 4; d < D; d += 256) {
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < n_parts; ++s) {
-            const float ms = part.ml[part.idx(s, lg, row)].x;
-            if (ms == -INFINITY) continue;
-            const float w = exp2f(ms - mx);
-            const float4 v = *reinterpret_cast<const float4*>(part.o + part.idx(s, lg, row) * D + d);
-            a.x += w * v.x; a.y += w * v.y; a.z += w * v.z; a.w += w * v.w;
+        for (int s0 = 0; s0 < n_parts; s0 += 4) {     // four independent loads in flight
+            float4 v[4];
+            float w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sp = s0 + i;
+                const bool ok = sp < n_parts;
+                w[i] = ok ? __shfl(sp < 64 ? w0 : w1, sp & 63) : 0.f;
+                v[i] = ok ? *reinterpret_cast<const float4*>(part.o + part.idx(sp, lg, row) * D + d)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a.x += w[i] * v[i].x; a.y += w[i] * v[i].y; a.z += w[i] * v[i].z; a.w += w[i] * v[i].w;
+            }
         }
         st(op + d + 0, a.x * inv);
         st(op + d + 1, a.y * inv);
@@ -566,7 +577,7 @@ static pa_status plan_for(const Ring* r, int layer_begin, int num_layers, int hq
     PA_CHECK_ARG(hq >= 1 && hq % c.num_kv_heads == 0, PA_ESHAPE, "n_q_heads %d is not a multiple of num_kv_heads %d",
                  hq, c.num_kv_heads);
     PA_CHECK_ARG(n_rows_tokens >= 1, PA_ESHAPE, "need at least one query token");
-    PA_CHECK_ARG(req_splits >= 0 && req_splits <= 256, PA_EINVAL, "num_splits %d not in [0, 256]", req_splits);
+    PA_CHECK_ARG(req_splits >= 0 && req_splits <= 127, PA_EINVAL, "num_splits %d not in [0, 127]", req_splits);
     p->mfma = c.dtype == PA_BF16;
     if (p->mfma)
         PA_CHECK_ARG(c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256, PA_ESHAPE,

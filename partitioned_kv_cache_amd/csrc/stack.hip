@@ -19,7 +19,7 @@
 namespace pa {
 
 struct StackWs {
-    size_t h, y, q, k, v, o, attn, total;
+    size_t h, q, k, v, o, attn, total;
 };
 
 static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes) {
@@ -32,7 +32,6 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
         return at;
     };
     w.h = take(n * m * 2);
-    w.y = take(n * m * 2);
     w.q = take(n * st->n_q_heads * d * 2);
     w.k = take(n * hkv * d * 2);
     w.v = take(n * hkv * d * 2);
@@ -48,8 +47,8 @@ static pa_status check_stack(const Ring* r, const pa_stack* st) {
     PA_CHECK_ARG(st->num_layers >= 1 && st->num_layers <= r->cfg.num_layers, PA_ESHAPE,
                  "pa_denoise_step: %d layers but the ring has %d", st->num_layers, r->cfg.num_layers);
     PA_CHECK_ARG(st->rows >= 1 && st->rows <= 64, PA_ESHAPE, "pa_denoise_step: rows %d not in [1, 64]", st->rows);
-    PA_CHECK_ARG(st->model_dim >= 256 && st->model_dim % 256 == 0, PA_ESHAPE,
-                 "pa_denoise_step: model_dim must be a multiple of 256");
+    PA_CHECK_ARG(st->model_dim % 128 == 0 && st->model_dim >= 256 && st->model_dim <= 2048, PA_ESHAPE,
+                 "pa_denoise_step: model_dim must be a multiple of 128 in [256, 2048]");
     PA_CHECK_ARG(st->n_q_heads >= 1 && st->n_q_heads % r->cfg.num_kv_heads == 0, PA_ESHAPE,
                  "pa_denoise_step: n_q_heads must be a multiple of num_kv_heads");
     PA_CHECK_ARG((st->n_q_heads * r->cfg.head_dim) % 256 == 0, PA_ESHAPE,
@@ -106,12 +105,11 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
     const int in_dim = st->n_q_heads * d;
     const size_t wqkv_layer = (size_t)(st->n_q_heads + 2 * hkv) * d * st->model_dim;
     const size_t wo_layer = (size_t)st->model_dim * in_dim;
-    const size_t y_bytes = align_up((size_t)st->rows * st->model_dim * 2, 256);
     for (int l = 0; l < st->num_layers; ++l) {
         const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
         const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
         s = ada_rmsnorm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq, st->n_q_heads,
-                            hkv, d, q, k, v, nonfinite, base + w.y, y_bytes, stream);
+                            hkv, d, q, k, v, nonfinite, nullptr, 0, stream);
         if (s != PA_OK) return s;
         const pattn_args a = attn_args(st, l);
         s = pattn_step(ring, &a, q, k, v, o, aws, attn, stream);
