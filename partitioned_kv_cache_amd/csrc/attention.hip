@@ -49,13 +49,29 @@ template <typename T> __device__ __forceinline__ float ldf(const T* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
 
+// Split partials in the workspace. (m, l) per row; the unnormalised
+// accumulator O in MFMA-fragment order, so that a wave's accumulator tile is
+// stored and reloaded with fully contiguous 1 KB accesses:
+//   O[part][lg][row / 32][d / 32][j][lane][e],  lane = row % 32 + 32 hi,
+//   (d % 32) = 8 j + 4 hi + e   (j < 4, hi < 2, e < 4)
+// which is the C/D register layout of v_mfma_f32_32x32x16 for O^T.
 struct Partials {
-    float* o;        // [parts][lg][mpad][D]
+    float* o;
     float2* ml;      // [parts][lg][mpad]   (m, l)
-    int mpad;
+    int mpad;        // rows padded to a multiple of 32
     int lg_count;    // call-layers x KV heads
+    int d;           // head dim
     __device__ __forceinline__ long long idx(int part, int lg, int row) const {
         return ((long long)part * lg_count + lg) * mpad + row;
+    }
+    // first float of the 32-row block holding `row`
+    __device__ __forceinline__ long long oblock(int part, int lg, int row) const {
+        return (((long long)part * lg_count + lg) * mpad + (row & ~31)) * d;
+    }
+    // float offset of element (row, dim) within that block
+    __device__ __forceinline__ int oelem(int row, int dim) const {
+        const int dd = dim & 31;
+        return (((dim >> 5) * 4 + (dd >> 3)) * 64 + (row & 31) + 32 * ((dd >> 2) & 1)) * 4 + (dd & 3);
     }
 };
 
@@ -112,11 +128,11 @@ __global__ __launch_bounds__(256) void partial_valu(const T* q, long long q_laye
         m = mn;
     }
     if (row_ok) {
-        float* op = part.o + part.idx(split, lg, row) * D;
+        float* op = part.o + part.oblock(split, lg, row);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d = lane + 64 * c;
-            if (d < D) op[d] = o[c];
+            if (d < D) op[part.oelem(row, d)] = o[c];
         }
         if (lane == 0) part.ml[part.idx(split, lg, row)] = make_float2(m, l);
     }
@@ -161,42 +177,43 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
 
-// Per-wave arithmetic on one LDS tile of KTILE keys (NKB blocks of 32 keys)
-// for the wave's 32 query rows.
-template <int D, int KTILE>
-__device__ __forceinline__ void tile_math(const char* kb, const char* vb, int koff0, int koff1, int voff, int base,
-                                          int k_end, int hi, float scale_log2, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
-    constexpr int KD = D / 16, DB = D / 32, PLANE = KTILE * 64, NKB = KTILE / 32;
-    f32x16 s[NKB];
-#pragma unroll
-    for (int c = 0; c < NKB; ++c) s[c] = f32x16{};
+// Per-wave arithmetic on one LDS tile of KT = 32 keys for the wave's 32
+// query rows:
+//   qk_scores:    S^T = K_tile . Q^T       (16 MFMAs, K from LDS)
+//   softmax_tile: online softmax of S -> P (VALU)
+//   pv_tile:      O^T += V^T P^T           (16 MFMAs, V from LDS)
+template <int D>
+__device__ __forceinline__ f32x16 qk_scores(const char* kb, int koff0, int koff1, const bf16x8 (&qf)[D / 16]) {
+    constexpr int KD = D / 16, PLANE = KT * 64;
+    f32x16 s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
-#pragma unroll
-        for (int c = 0; c < NKB; ++c) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(kb + (kk >> 1) * PLANE + c * 2048 + ((kk & 1) ? koff1 : koff0));
-            s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[c], 0, 0, 0);
-        }
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (kk >> 1) * PLANE + ((kk & 1) ? koff1 : koff0));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
     }
+    return s;
+}
+
+// Online softmax of one tile's scores: updates the running (m, l), rescales
+// O when the reference max moves, and returns P in bf16 in the B-operand
+// layout of the PV product.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int hi, float scale_log2,
+                                             f32x16 (&acc)[D / 32], float& m_run, float& l_run, bf16x8 (&pf)[2]) {
+    constexpr int DB = D / 32;
     // Row max on the raw scores (scale > 0 keeps the order); keys past the
     // split's end exist only in its last tile and are masked there alone.
     float rmax = -INFINITY;
-    if (base + KTILE <= k_end) {
+    if (base + KT <= k_end) {
 #pragma unroll
-        for (int c = 0; c < NKB; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[c][r]);
+        for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
     } else {
 #pragma unroll
-        for (int c = 0; c < NKB; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = base + 32 * c + 16 * (r >> 3) + 8 * hi + (r & 7);
-                s[c][r] = key < k_end ? s[c][r] : -INFINITY;
-                rmax = fmaxf(rmax, s[c][r]);
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int key = base + 16 * (r >> 3) + 8 * hi + (r & 7);
+            s[r] = key < k_end ? s[r] : -INFINITY;
+            rmax = fmaxf(rmax, s[r]);
+        }
     }
     float tmax = rmax * scale_log2;
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -213,30 +230,30 @@ __device__ __forceinline__ void tile_math(const char* kb, const char* vb, int ko
     }
     // p = 2^(scale log2e s - m): one FMA and the hardware exp2 (v_exp_f32);
     // results below 2^-126 flush to zero, far below what a bf16 P can carry.
-    bf16x8 pf[NKB][2];
     float psum = 0.f;
 #pragma unroll
-    for (int c = 0; c < NKB; ++c) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[c][r], scale_log2, -m_run));
-            psum += p;
-            pf[c][r >> 3][r & 7] = (__bf16)p;
-        }
+    for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
+        psum += p;
+        pf[r >> 3][r & 7] = (__bf16)p;
     }
     l_run += psum;
+}
+
+// O^T += V^T P^T for one tile (16 MFMAs; V^T straight from the token-major
+// tile by transposed LDS reads).
+template <int D>
+__device__ __forceinline__ void pv_tile(const char* vb, int voff, const bf16x8 (&pf)[2], f32x16 (&acc)[D / 32]) {
+    constexpr int DB = D / 32, PLANE = KT * 64;
 #pragma unroll
-    for (int c = 0; c < NKB; ++c) {
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const char* vp = vb + b * PLANE + c * 2048 + (16 * s2) * 64 + voff;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp));
-                const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 4 * 64));
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c][s2], acc[b], 0, 0, 0);
-            }
+        for (int b = 0; b < DB; ++b) {
+            const char* vp = vb + b * PLANE + (16 * s2) * 64 + voff;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp));
+            const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 4 * 64));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], acc[b], 0, 0, 0);
         }
     }
 }
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     const int n_tiles = (k_end - k_begin + KT - 1) / KT;
     // Step through tile t held in ring buffer J: wait for its loads, meet at
     // the barrier (which also frees buffer J - 1 for reuse), refill that
-    // buffer with tile t + NBUF - 1, multiply tile t.
+    // buffer with tile t + NBUF - 1, then S = K Q^T, softmax, O += V P.
     auto step = [&](auto J_, int t) {
         constexpr int J = decltype(J_)::value;
         constexpr int JN = (J + NBUF - 1) % NBUF;
@@ -361,9 +378,12 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
             wait_vmem<0>();
         __syncthreads();
         if (t + NBUF - 1 < n_tiles) issue_tile(t + NBUF - 1, lds_buffer<JN, TILE>(), lds_buffer<NBUF + JN, TILE>());
-        if (active)
-            tile_math<D, KT>(lds_buffer<J, TILE>(), lds_buffer<NBUF + J, TILE>(), koff0, koff1, voff,
-                             k_begin + t * KT, k_end, hi, scale_log2, qf, acc, m_run, l_run);
+        if (active) {
+            bf16x8 pf[2];
+            const f32x16 sc = qk_scores<D>(lds_buffer<J, TILE>(), koff0, koff1, qf);
+            softmax_tile<D>(sc, k_begin + t * KT, k_end, hi, scale_log2, acc, m_run, l_run, pf);
+            pv_tile<D>(lds_buffer<NBUF + J, TILE>(), voff, pf, acc);
+        }
     };
     static_assert(NBUF == 4, "the prologue and the unrolled loop below assume four buffers");
     issue_tile(0, lds_buffer<0, TILE>(), lds_buffer<NBUF + 0, TILE>());
@@ -377,15 +397,15 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     }
 
     l_run += __shfl_xor(l_run, 32);
-    if (row < m_rows) {
-        float* op = part.o + part.idx(split, lg, row) * D;
+    if (active) {       // whole 32-row block, fragment order: each store is 1 KB contiguous
+        float* op = part.o + part.oblock(split, lg, row0) + lane * 4;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<float4*>(op + 32 * b + 8 * j + 4 * hi) =
+                *reinterpret_cast<float4*>(op + (b * 4 + j) * 256) =
                     make_float4(acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]);
-        if (hi == 0) part.ml[part.idx(split, lg, row)] = make_float2(m_run, l_run);
+        if (hi == 0 && row < m_rows) part.ml[part.idx(split, lg, row)] = make_float2(m_run, l_run);
     }
 }
 
@@ -439,11 +459,11 @@ __global__ __launch_bounds__(256) void partial_tail(const T* q, long long q_laye
         m = mn;
     }
     if (row_ok) {
-        float* op = part.o + part.idx(slot, lg, row) * D;
+        float* op = part.o + part.oblock(slot, lg, row);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d = lane + 64 * c;
-            if (d < D) op[d] = o[c];
+            if (d < D) op[part.oelem(row, d)] = o[c];
         }
         if (lane == 0) part.ml[part.idx(slot, lg, row)] = make_float2(m, l);
     }
@@ -457,46 +477,44 @@ template <typename TO> __device__ __forceinline__ void st(TO* p, float v);
 template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
 
-template <typename TO>
+template <typename TO, int D>
 __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m_rows, int group, int hq, int hkv,
-                                               int D, long long out_layer, TO* out) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = blockIdx.x * VALU_ROWS + wave, lg = blockIdx.y;
-    if (row >= m_rows) return;
+                                               long long out_layer, TO* out) {
+    constexpr int DB = D / 32;
+    // one wave per (32-row block, 32-dim block): 1 KB contiguous per split
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int unit = blockIdx.x * 4 + wave, lg = blockIdx.y;
+    const int row0 = (unit / DB) * 32, b = unit % DB;
+    if (row0 >= m_rows) return;
+    const int row = row0 + l32;
+    const bool ok = row < m_rows;
     const int lb = lg / hkv, g = lg % hkv;
-    // lane s (and s + 64) holds partial s's statistics
-    float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = make_float2(-INFINITY, 0.f);
-    if (lane < n_parts) ml0 = part.ml[part.idx(lane, lg, row)];
-    if (lane + 64 < n_parts) ml1 = part.ml[part.idx(lane + 64, lg, row)];
-    const float mx = wave_max(fmaxf(ml0.x, ml1.x));
-    // weights 2^(m_s - m*); an empty partial (m = -inf, l = 0) weighs 0
-    const float w0 = ml0.x == -INFINITY ? 0.f : exp2f(ml0.x - mx);
-    const float w1 = ml1.x == -INFINITY ? 0.f : exp2f(ml1.x - mx);
-    const float lsum = wave_sum(w0 * ml0.y + w1 * ml1.y);
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    TO* op = out + lb * out_layer + ((long long)(row / group) * hq + g * group + row % group) * D;
-    for (int d = lane * 4; d < D; d += 256) {
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s0 = 0; s0 < n_parts; s0 += 4) {     // four independent loads in flight
-            float4 v[4];
-            float w[4];
+    float mx = -INFINITY;
+    for (int s = 0; s < n_parts; ++s) mx = fmaxf(mx, ok ? part.ml[part.idx(s, lg, row)].x : -INFINITY);
+    float4 acc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sp = s0 + i;
-                const bool ok = sp < n_parts;
-                w[i] = ok ? __shfl(sp < 64 ? w0 : w1, sp & 63) : 0.f;
-                v[i] = ok ? *reinterpret_cast<const float4*>(part.o + part.idx(sp, lg, row) * D + d)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+    for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
+    for (int s = 0; s < n_parts; ++s) {
+        const float2 ml = ok ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
+        const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx);   // an empty partial weighs 0
+        lsum += w * ml.y;
+        const float* op = part.o + part.oblock(s, lg, row0) + (b * 4) * 256 + lane * 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a.x += w[i] * v[i].x; a.y += w[i] * v[i].y; a.z += w[i] * v[i].z; a.w += w[i] * v[i].w;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(op + j * 256);
+            acc[j].x += w * v.x; acc[j].y += w * v.y; acc[j].z += w * v.z; acc[j].w += w * v.w;
         }
-        st(op + d + 0, a.x * inv);
-        st(op + d + 1, a.y * inv);
-        st(op + d + 2, a.z * inv);
-        st(op + d + 3, a.w * inv);
+    }
+    if (!ok) return;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    TO* orow = out + lb * out_layer + ((long long)(row / group) * hq + g * group + row % group) * D + 32 * b + 4 * hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        st(orow + 8 * j + 0, acc[j].x * inv);
+        st(orow + 8 * j + 1, acc[j].y * inv);
+        st(orow + 8 * j + 2, acc[j].z * inv);
+        st(orow + 8 * j + 3, acc[j].w * inv);
     }
 }
 
@@ -565,6 +583,7 @@ static Partials partials_in(void* ws, const Plan& p, int d) {
                                         align_up((size_t)p.max_parts * p.lg_count * p.mpad * d * sizeof(float), 256));
     part.mpad = p.mpad;
     part.lg_count = p.lg_count;
+    part.d = d;
     return part;
 }
 
@@ -652,14 +671,26 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
 
 static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int hq, long long out_layer, void* out,
                                 int out_dtype, const Partials& part, hipStream_t stream) {
-    dim3 grid(valu_row_blocks(p.m_rows), p.lg_count);
     const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
-    if (out_dtype == PA_F32)
-        combine<float><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv, d, out_layer,
-                                                 static_cast<float*>(out));
-    else
-        combine<uint16_t><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv, d, out_layer,
-                                                    static_cast<uint16_t*>(out));
+    const int units = (p.m_rows + 31) / 32 * (d / 32);          // (32-row, 32-dim) blocks, one wave each
+    const dim3 grid((units + 3) / 4, p.lg_count);
+#define PA_COMBINE(TO, DD)                                                                                  \
+    combine<TO, DD><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv, out_layer,        \
+                                              static_cast<TO*>(out))
+    if (out_dtype == PA_F32) {
+        if (d == 256) PA_COMBINE(float, 256);
+        else if (d == 128) PA_COMBINE(float, 128);
+        else if (d == 64) PA_COMBINE(float, 64);
+        else if (d == 32) PA_COMBINE(float, 32);
+        else return fail(PA_ESHAPE, "combine: head_dim %d must be 32, 64, 128 or 256", d);
+    } else {
+        if (d == 256) PA_COMBINE(uint16_t, 256);
+        else if (d == 128) PA_COMBINE(uint16_t, 128);
+        else if (d == 64) PA_COMBINE(uint16_t, 64);
+        else if (d == 32) PA_COMBINE(uint16_t, 32);
+        else return fail(PA_ESHAPE, "combine: head_dim %d must be 32, 64, 128 or 256", d);
+    }
+#undef PA_COMBINE
     PA_LAUNCHED();
     return PA_OK;
 }

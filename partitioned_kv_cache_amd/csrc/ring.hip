@@ -45,8 +45,8 @@ extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, r
     PA_CHECK_ARG(cfg->num_layers > 0 && cfg->num_kv_heads > 0 && cfg->head_dim > 0 && cfg->num_slots > 0 &&
                      cfg->tokens_per_frame > 0 && cfg->pin_capacity >= 0,
                  PA_ESHAPE, "rb_create: sizes must be positive (pin capacity >= 0)");
-    PA_CHECK_ARG(cfg->head_dim % 8 == 0 && cfg->head_dim <= 256, PA_ESHAPE,
-                 "rb_create: head_dim %d must be a multiple of 8 and <= 256", cfg->head_dim);
+    PA_CHECK_ARG(cfg->head_dim == 32 || cfg->head_dim == 64 || cfg->head_dim == 128 || cfg->head_dim == 256,
+                 PA_ESHAPE, "rb_create: head_dim %d must be 32, 64, 128 or 256", cfg->head_dim);
     int64_t seq = (int64_t)cfg->pin_capacity + (int64_t)cfg->num_slots * cfg->tokens_per_frame;
     PA_CHECK_ARG(seq * cfg->num_kv_heads * cfg->head_dim < (1LL << 31), PA_ESHAPE,
                  "rb_create: (P + W*F) * Hkv * D must stay below 2^31 elements per layer");
