@@ -14,7 +14,9 @@ Reported beside it in the same JSON line: the whole denoising step of the
 Pi0.5-like 18-layer stack (AdaRMSNorm fused into the packed QKV projection,
 partitioned attention over a 48 + 2 x 768 token cache, out-projection with
 residual, Euler update; the gamma MLP batched once per frame), replayed as
-a captured graph, in microseconds per step.
+a captured graph, in microseconds per step; and the shared-KV multi-reader
+frame (the action suffix plus 16 decode streams with private tails over the
+long-history cache), in frames/s and decode tokens/s.
 
 ``roofline`` describes the split-KV partial kernel, timed live with HIP
 events recorded around it on the launch stream. ``cpu_baseline`` is the
@@ -200,6 +202,69 @@ def bench_stack(args, torch, L, configs, synth):
     }
 
 
+def bench_shared_kv(args, torch, L, configs, synth):
+    """Shared-KV multi-reader frame: the long-history cache read by the action
+    suffix (10 denoising steps, 18 layers) and by 16 decode streams (one query
+    token each, one decode step per frame) with private tails of up to 30
+    appended tokens."""
+    import numpy as np
+    s = configs.SHARED_KV
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
+    k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
+                              s.tokens_per_frame, L.PA_BF16), k_buf, v_buf)
+    pk, pv = synth.pin_kv(s)
+    ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
+    pool = [tuple(dev(a) for a in synth.frame_kv(s, f)) for f in range(4)]
+    for f in range(s.num_slots):
+        ring.push_frame(*pool[f % 4])
+    steps_in = [tuple(dev(a) for a in synth.suffix_qkv(s, 0, k)) for k in range(s.steps_per_frame)]
+    a_args = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16)
+    a_wsb = L.pattn_workspace_bytes(ring, a_args)
+    a_ws = torch.empty(a_wsb, dtype=torch.uint8, device="cuda")
+    a_out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+    G, cap = s.n_streams, s.tail_capacity
+    d_args = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_BF16)
+    d_wsb = L.pattn_decode_workspace_bytes(ring, d_args)
+    d_ws = torch.empty(d_wsb, dtype=torch.uint8, device="cuda")
+    tail_k = torch.zeros((s.num_layers, G, cap, s.n_kv_heads, s.head_dim), dtype=torch.int16, device="cuda")
+    tail_v = torch.zeros_like(tail_k)
+    tail_len = dev(np.array([(2 * j) % (cap - 10) for j in range(G)], dtype=np.int32))
+    dq = dev(synth.decode_q(s, 0, 0))
+    dk, dv = (dev(a) for a in synth.decode_kv(s, 0, 0))
+    d_out = torch.empty((s.num_layers, G, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+    n_frames = 10           # tails stay below capacity: lengths start at most cap - 11
+
+    def frame(i, ev=None):
+        ring.push_frame(*pool[i % 4])
+        for k in range(s.steps_per_frame):
+            L.pattn_step(ring, a_args, *steps_in[k], a_out, a_ws, a_wsb)
+        if ev is not None:
+            ev[0].record()
+        L.pattn_append_private(ring, d_args, tail_k, tail_v, tail_len, dk, dv)
+        L.pattn_decode(ring, d_args, dq, tail_k, tail_v, tail_len, d_out, d_ws, d_wsb)
+        if ev is not None:
+            ev[1].record()
+
+    frame(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_frames)]
+    t0 = time.perf_counter()
+    for i in range(n_frames):
+        frame(1 + i, evs[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    dec_us = sum(a.elapsed_time(b) for a, b in evs) / n_frames * 1e3
+    ring.close()
+    return {"workload": "shared_kv_multitask", "frames_per_s": n_frames / el,
+            "decode_tokens_per_s": G * n_frames / el, "decode_step_us": dec_us,
+            "frames_timed": n_frames,
+            "config": {"layers": 18, "cache": "256 + 8x768", "action_suffix": 51, "steps_per_frame": 10,
+                       "decode_streams": G, "tail_capacity": cap, "decode_steps_per_frame": 1}}
+
+
 def cpu_baseline(budget_s):
     """Time the float64 CPU oracle on a bounded sample of the long-history step."""
     import numpy as np
@@ -292,6 +357,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="KV splits per layer (0 = library default)")
     ap.add_argument("--stack-frames", type=int, default=50)
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-KV multi-reader frame")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB five times (traffic-counter calibration)")
@@ -316,6 +382,10 @@ def main():
     if not args.no_stack:
         stack = bench_stack(args, torch, L, configs, synth)
         log(f"pi05 18L stack: {stack['us_per_step']:.1f} us/step")
+    shared = None
+    if not args.no_shared:
+        shared = bench_shared_kv(args, torch, L, configs, synth)
+        log(f"shared KV: {shared['frames_per_s']:.1f} frames/s, decode step {shared['decode_step_us']:.1f} us")
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(args.cpu_budget)
@@ -351,6 +421,8 @@ def main():
     }
     if stack is not None:
         line["pi05_18L_full_step"] = stack
+    if shared is not None:
+        line["shared_kv_multitask"] = shared
     print(json.dumps(line), flush=True)
 
 

@@ -65,7 +65,7 @@ const char* pa_last_error(void);
 typedef struct {
     int32_t num_layers;        /* L  > 0 */
     int32_t num_kv_heads;      /* Hkv > 0 */
-    int32_t head_dim;          /* D: 32 or 64 (f32 rings), 64, 128 or 256 (bf16 rings) */
+    int32_t head_dim;          /* D: 32, 64, 128 or 256 (f32 rings); 64, 128 or 256 (bf16 rings) */
     int32_t pin_capacity;      /* P >= 0 */
     int32_t num_slots;         /* W > 0: frames in the sliding window */
     int32_t tokens_per_frame;  /* F > 0 */
