@@ -48,15 +48,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <typename T> __device__ __forceinline__ float ldf(const T* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+__device__ __forceinline__ void stp(float* p, float v) { *p = v; }
+__device__ __forceinline__ void stp(uint16_t* p, float v) { *p = f2bf(v); }
+// two floats -> two bf16 (round to nearest even), first in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
 
-// Split partials in the workspace. (m, l) per row; the unnormalised
+// Split partials in the workspace. (m, l) per row in FP32; the unnormalised
 // accumulator O in MFMA-fragment order, so that a wave's accumulator tile is
-// stored and reloaded with fully contiguous 1 KB accesses:
+// stored and reloaded with fully contiguous accesses. O is FP32 for f32 rings
+// and bf16 for bf16 rings (whose products already round P to bf16; the extra
+// rounding of O is of the same relative size, 2^-9):
 //   O[part][lg][row / 32][d / 32][j][lane][e],  lane = row % 32 + 32 hi,
 //   (d % 32) = 8 j + 4 hi + e   (j < 4, hi < 2, e < 4)
 // which is the C/D register layout of v_mfma_f32_32x32x16 for O^T.
 struct Partials {
-    float* o;
+    void* o;         // float (f32 rings) or bf16 bits (bf16 rings)
     float2* ml;      // [parts][lg][mpad]   (m, l)
     int mpad;        // rows padded to a multiple of 32
     int lg_count;    // call-layers x KV heads
@@ -64,11 +72,12 @@ struct Partials {
     __device__ __forceinline__ long long idx(int part, int lg, int row) const {
         return ((long long)part * lg_count + lg) * mpad + row;
     }
-    // first float of the 32-row block holding `row`
+    template <typename PO> __device__ __forceinline__ PO* optr() const { return static_cast<PO*>(o); }
+    // first element of the 32-row block holding `row`
     __device__ __forceinline__ long long oblock(int part, int lg, int row) const {
         return (((long long)part * lg_count + lg) * mpad + (row & ~31)) * d;
     }
-    // float offset of element (row, dim) within that block
+    // element offset of (row, dim) within that block
     __device__ __forceinline__ int oelem(int row, int dim) const {
         const int dd = dim & 31;
         return (((dim >> 5) * 4 + (dd >> 3)) * 64 + (row & 31) + 32 * ((dd >> 2) & 1)) * 4 + (dd & 3);
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(256) void partial_valu(const T* q, long long q_laye
         m = mn;
     }
     if (row_ok) {
-        float* op = part.o + part.oblock(split, lg, row);
+        float* op = part.optr<float>() + part.oblock(split, lg, row);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d = lane + 64 * c;
@@ -216,7 +225,10 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int 
         }
     }
     float tmax = rmax * scale_log2;
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    {   // the other half of the row's keys sits in lane ^ 32: swap the wave's halves
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     // Lazy rescale: keep the reference max unless some row's max got more than
     // RESCALE_SLACK above it. Exact (numerator and denominator share the
     // reference); probabilities stay below 2^RESCALE_SLACK.
@@ -397,14 +409,14 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     }
 
     l_run += __shfl_xor(l_run, 32);
-    if (active) {       // whole 32-row block, fragment order: each store is 1 KB contiguous
-        float* op = part.o + part.oblock(split, lg, row0) + lane * 4;
+    if (active) {       // whole 32-row block, fragment order: each store is 512 B contiguous
+        uint16_t* op = part.optr<uint16_t>() + part.oblock(split, lg, row0) + lane * 4;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<float4*>(op + (b * 4 + j) * 256) =
-                    make_float4(acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]);
+                *reinterpret_cast<uint2*>(op + (b * 4 + j) * 256) =
+                    make_uint2(pack_bf16(acc[b][4 * j], acc[b][4 * j + 1]), pack_bf16(acc[b][4 * j + 2], acc[b][4 * j + 3]));
         if (hi == 0 && row < m_rows) part.ml[part.idx(split, lg, row)] = make_float2(m_run, l_run);
     }
 }
@@ -459,11 +471,11 @@ __global__ __launch_bounds__(256) void partial_tail(const T* q, long long q_laye
         m = mn;
     }
     if (row_ok) {
-        float* op = part.o + part.oblock(slot, lg, row);
+        T* op = part.optr<T>() + part.oblock(slot, lg, row);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d = lane + 64 * c;
-            if (d < D) op[part.oelem(row, d)] = o[c];
+            if (d < D) stp(op + part.oelem(row, d), o[c]);
         }
         if (lane == 0) part.ml[part.idx(slot, lg, row)] = make_float2(m, l);
     }
@@ -473,11 +485,25 @@ __global__ __launch_bounds__(256) void partial_tail(const T* q, long long q_laye
 // Log-sum-exp combine of `n_parts` partials per row (Prop. A.1), FP32.
 // One wave per query row; writes out[lb][token][head][d] in the output dtype.
 // grid (ceil(M / 4), Lb * Hkv), block 256.
-template <typename TO> __device__ __forceinline__ void st(TO* p, float v);
-template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
-template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
+// Four consecutive outputs of one row: one 8-byte (bf16) or 16-byte (f32) store.
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void st4(uint16_t* p, float4 v) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+}
 
-template <typename TO, int D>
+// Splits merged per batch: every load of a batch is issued before the first
+// one is used, so a batch costs one memory round trip.
+constexpr int COMBINE_BATCH = 8;
+
+// Four consecutive partial-O elements as floats.
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <typename TO, int D, typename PO>
 __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m_rows, int group, int hq, int hkv,
                                                long long out_layer, TO* out) {
     constexpr int DB = D / 32;
@@ -489,33 +515,49 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m
     const int row = row0 + l32;
     const bool ok = row < m_rows;
     const int lb = lg / hkv, g = lg % hkv;
-    float mx = -INFINITY;
-    for (int s = 0; s < n_parts; ++s) mx = fmaxf(mx, ok ? part.ml[part.idx(s, lg, row)].x : -INFINITY);
+    // Online merge over batches of splits: (mx, lsum, acc) is the merge of
+    // the splits seen so far, referenced to mx.
+    float mx = -INFINITY, lsum = 0.f;
     float4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lsum = 0.f;
-    for (int s = 0; s < n_parts; ++s) {
-        const float2 ml = ok ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
-        const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx);   // an empty partial weighs 0
-        lsum += w * ml.y;
-        const float* op = part.o + part.oblock(s, lg, row0) + (b * 4) * 256 + lane * 4;
+    for (int s0 = 0; s0 < n_parts; s0 += COMBINE_BATCH) {
+        float2 ml[COMBINE_BATCH];
+        float4 v[COMBINE_BATCH][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 v = *reinterpret_cast<const float4*>(op + j * 256);
-            acc[j].x += w * v.x; acc[j].y += w * v.y; acc[j].z += w * v.z; acc[j].w += w * v.w;
+        for (int i = 0; i < COMBINE_BATCH; ++i) {
+            const int s = min(s0 + i, n_parts - 1);     // past the end: a valid split, weighed 0 below
+            ml[i] = ok && s0 + i < n_parts ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
+            const PO* op = part.optr<PO>() + part.oblock(s, lg, row0) + (b * 4) * 256 + lane * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[i][j] = ld4(op + j * 256);
         }
+        float bm = mx;
+#pragma unroll
+        for (int i = 0; i < COMBINE_BATCH; ++i) bm = fmaxf(bm, ml[i].x);
+        if (bm == -INFINITY) continue;                  // nothing non-empty yet
+        const float sc = exp2f(mx - bm);                // 0 while mx is -inf
+        lsum *= sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { acc[j].x *= sc; acc[j].y *= sc; acc[j].z *= sc; acc[j].w *= sc; }
+#pragma unroll
+        for (int i = 0; i < COMBINE_BATCH; ++i) {
+            const float w = ml[i].x == -INFINITY ? 0.f : exp2f(ml[i].x - bm);   // an empty partial weighs 0
+            lsum += w * ml[i].y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[j].x += w * v[i][j].x; acc[j].y += w * v[i][j].y;
+                acc[j].z += w * v[i][j].z; acc[j].w += w * v[i][j].w;
+            }
+        }
+        mx = bm;
     }
     if (!ok) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     TO* orow = out + lb * out_layer + ((long long)(row / group) * hq + g * group + row % group) * D + 32 * b + 4 * hi;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        st(orow + 8 * j + 0, acc[j].x * inv);
-        st(orow + 8 * j + 1, acc[j].y * inv);
-        st(orow + 8 * j + 2, acc[j].z * inv);
-        st(orow + 8 * j + 3, acc[j].w * inv);
-    }
+    for (int j = 0; j < 4; ++j)
+        st4(orow + 8 * j, make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv));
 }
 
 // ---------------------------------------------------------------------------
@@ -554,6 +596,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 struct Plan {
     int group, m_rows, mpad, lg_count, total, chunk, parts, max_parts;
     bool mfma;
+    int o_bytes;     // bytes per partial-O element: 2 (bf16 rings) or 4 (f32 rings)
 };
 
 static int valu_row_blocks(int m) { return (m + VALU_ROWS - 1) / VALU_ROWS; }
@@ -571,16 +614,16 @@ static int default_splits(int lg_count, int row_blocks, int max_keys) {
 }
 
 static size_t partial_bytes(const Plan& p, int d) {
-    const size_t o = align_up((size_t)p.max_parts * p.lg_count * p.mpad * d * sizeof(float), 256);
+    const size_t o = align_up((size_t)p.max_parts * p.lg_count * p.mpad * d * p.o_bytes, 256);
     const size_t ml = align_up((size_t)p.max_parts * p.lg_count * p.mpad * sizeof(float2), 256);
     return o + ml;
 }
 
 static Partials partials_in(void* ws, const Plan& p, int d) {
     Partials part;
-    part.o = static_cast<float*>(ws);
+    part.o = ws;
     part.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                        align_up((size_t)p.max_parts * p.lg_count * p.mpad * d * sizeof(float), 256));
+                                        align_up((size_t)p.max_parts * p.lg_count * p.mpad * d * p.o_bytes, 256));
     part.mpad = p.mpad;
     part.lg_count = p.lg_count;
     part.d = d;
@@ -598,6 +641,7 @@ static pa_status plan_for(const Ring* r, int layer_begin, int num_layers, int hq
     PA_CHECK_ARG(n_rows_tokens >= 1, PA_ESHAPE, "need at least one query token");
     PA_CHECK_ARG(req_splits >= 0 && req_splits <= 127, PA_EINVAL, "num_splits %d not in [0, 127]", req_splits);
     p->mfma = c.dtype == PA_BF16;
+    p->o_bytes = p->mfma ? 2 : 4;
     if (p->mfma)
         PA_CHECK_ARG(c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256, PA_ESHAPE,
                      "bf16 attention supports head_dim 64, 128 or 256 (got %d)", c.head_dim);
@@ -675,8 +719,14 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
     const int units = (p.m_rows + 31) / 32 * (d / 32);          // (32-row, 32-dim) blocks, one wave each
     const dim3 grid((units + 3) / 4, p.lg_count);
 #define PA_COMBINE(TO, DD)                                                                                  \
-    combine<TO, DD><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv, out_layer,        \
-                                              static_cast<TO*>(out))
+    do {                                                                                                    \
+        if (p.o_bytes == 2)                                                                                 \
+            combine<TO, DD, uint16_t><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv,  \
+                                                                out_layer, static_cast<TO*>(out));          \
+        else                                                                                                \
+            combine<TO, DD, float><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv,     \
+                                                             out_layer, static_cast<TO*>(out));             \
+    } while (0)
     if (out_dtype == PA_F32) {
         if (d == 256) PA_COMBINE(float, 256);
         else if (d == 128) PA_COMBINE(float, 128);

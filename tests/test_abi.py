@@ -105,8 +105,14 @@ def test_workspace_grows_with_splits():
     w4 = L.pattn_workspace_bytes(r, L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_F32, 4))
     w8 = L.pattn_workspace_bytes(r, L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_F32, 8))
     assert w8 > w4 > 0
-    # 408 rows pad to 416; 8 splits x 18 layers x 416 rows x 256 dims x 4 bytes, plus (m, l)
-    assert w8 == 8 * 18 * 416 * 256 * 4 + ((8 * 18 * 416 * 8 + 255) // 256) * 256
+    # 408 rows pad to 416; 8 splits x 18 layers x 416 rows x 256 dims of bf16 partial O
+    # (a bf16 ring), plus FP32 (m, l)
+    ml = ((8 * 18 * 416 * 8 + 255) // 256) * 256
+    assert w8 == 8 * 18 * 416 * 256 * 2 + ml
+    r.close()
+    # an f32 ring keeps FP32 partial O
+    r = L.Ring(L.rb_config(18, 1, 256, 256, 8, 768, L.PA_F32), _fake(1), _fake(2))
+    assert L.pattn_workspace_bytes(r, L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_F32, 8)) == 8 * 18 * 416 * 256 * 4 + ml
     r.close()
 
 
