@@ -8,7 +8,11 @@ dynamic suffix; 10 denoising steps per frame; a new frame pushed (and the
 oldest evicted) every 10 steps. One step = one partitioned-attention pass
 over all 18 layers (split-KV partials + log-sum-exp combine) with that
 step's suffix Q/K/V; the frame push is inside the timed loop, once per 10
-steps. Inputs are seeded synthetic tensors already resident in HBM.
+steps. Inputs are seeded synthetic tensors already resident in HBM. The
+headline is the cold case: three independent rings (sessions) are served
+round-robin, so each step's 118 MB of K/V comes from HBM rather than the
+256 MB last-level cache; the single-ring (warm) figure is reported beside it,
+as are microseconds per call on the two small configurations.
 
 Reported beside it in the same JSON line: the whole denoising step of the
 Pi0.5-like 18-layer stack (AdaRMSNorm fused into the packed QKV projection,
@@ -58,44 +62,55 @@ def attention_work(s, cached_tokens):
     return kv_cached + q_bytes + dyn, flops, kv_cached
 
 
-def bench_long_history(args, torch, L, configs, synth):
+def bench_long_history(args, torch, L, configs, synth, n_rings=1):
+    """The headline step. With n_rings > 1, that many independent rings (one
+    per session) are served round-robin, one step each in turn; three rings
+    hold 354 MB of K/V, more than the 256 MB last-level cache (MALL), so
+    every step streams its ring's K/V from HBM (the cold case). One ring of
+    118 MB stays resident in the MALL between steps (the warm case)."""
     s = configs.LONG_18L
     dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
     shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
-    k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
-    v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
-    ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
-                              s.tokens_per_frame, L.PA_BF16), k_buf, v_buf)
     pk, pv = synth.pin_kv(s)
-    ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
     log("generating the frame pool and step inputs")
     pool = [tuple(dev(a) for a in synth.frame_kv(s, f)) for f in range(4)]
     steps_in = [tuple(dev(a) for a in synth.suffix_qkv(s, 0, k)) for k in range(s.steps_per_frame)]
-    for f in range(s.num_slots):
-        ring.push_frame(*pool[f % 4])
+    rings, bufs = [], []
+    for r in range(n_rings):
+        k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+        v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+        ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
+                                  s.tokens_per_frame, L.PA_BF16), k_buf, v_buf)
+        ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
+        for f in range(s.num_slots):
+            ring.push_frame(*pool[(f + r) % 4])
+        rings.append(ring)
+        bufs.append((k_buf, v_buf))
     args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits)
-    wsb = L.pattn_workspace_bytes(ring, args_)
+    wsb = L.pattn_workspace_bytes(rings[0], args_)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
-    frame = [s.num_slots]
+    frame = [s.num_slots] * n_rings
 
     def one_step(i, ev=None):
-        if i % s.steps_per_frame == 0:
-            ring.push_frame(*pool[frame[0] % 4])
-            frame[0] += 1
-        q, kd, vd = steps_in[i % s.steps_per_frame]
+        r, j = i % n_rings, i // n_rings         # ring, and that ring's own step count
+        if j % s.steps_per_frame == 0:
+            rings[r].push_frame(*pool[frame[r] % 4])
+            frame[r] += 1
+        q, kd, vd = steps_in[j % s.steps_per_frame]
         if ev is None:
-            L.pattn_step(ring, args_, q, kd, vd, out, ws, wsb, stream)
+            L.pattn_step(rings[r], args_, q, kd, vd, out, ws, wsb, stream)
         else:
-            L.pattn_step_timed(ring, args_, q, kd, vd, out, ws, wsb, stream, ev[0].cuda_event, ev[1].cuda_event)
+            L.pattn_step_timed(rings[r], args_, q, kd, vd, out, ws, wsb, stream, ev[0].cuda_event, ev[1].cuda_event)
 
     for i in range(args.warmup):
         one_step(i)
     # The partial kernel is timed on one step of every frame (the middle
     # one): an event pair on every launch would add several microseconds of
     # dispatch latency to every step of the timed loop.
-    sampled = [i for i in range(args.steps) if (args.warmup + i) % s.steps_per_frame == s.steps_per_frame // 2]
+    half = s.steps_per_frame // 2
+    sampled = [i for i in range(args.steps) if ((args.warmup + i) // n_rings) % s.steps_per_frame == half]
     events = {}
     for i in sampled:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -124,10 +139,63 @@ def bench_long_history(args, torch, L, configs, synth):
         "algo_bytes": algo_bytes,
         "flops": flops,
         "splits": args.splits,
-        "frames": frame[0],
+        "rings": n_rings,
     }
-    ring.close()
+    for ring in rings:
+        ring.close()
     return res
+
+
+def bench_small(args, torch, L, cfg, n_calls=2000):
+    """Microseconds per pattn_step call on a small, launch-latency-bound
+    configuration (whole window full)."""
+    dt = torch.float32 if cfg.dtype == "f32" else torch.int16
+    pdt = L.PA_F32 if cfg.dtype == "f32" else L.PA_BF16
+    from partitioned_kv_cache_amd import synth
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    shp = (cfg.num_layers, cfg.max_seq_len, cfg.n_kv_heads, cfg.head_dim)
+    k_buf, v_buf = torch.zeros(shp, dtype=dt, device="cuda"), torch.zeros(shp, dtype=dt, device="cuda")
+    ring = L.Ring(L.rb_config(cfg.num_layers, cfg.n_kv_heads, cfg.head_dim, cfg.pin_tokens, cfg.num_slots,
+                              cfg.tokens_per_frame, pdt), k_buf, v_buf)
+    pk, pv = synth.pin_kv(cfg)
+    ring.pin_prefix(dev(pk), dev(pv), cfg.pin_tokens)
+    for f in range(cfg.num_slots):
+        ring.push_frame(*(dev(a) for a in synth.frame_kv(cfg, f)))
+    q, kd, vd = (dev(a) for a in synth.suffix_qkv(cfg, 0, 0))
+    a = L.pattn_args(0, cfg.num_layers, cfg.n_q_heads, cfg.n_dyn, cfg.scale, pdt, 0)
+    wsb = L.pattn_workspace_bytes(ring, a)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.num_layers, cfg.n_dyn, cfg.n_q_heads, cfg.head_dim), dtype=dt, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(50):
+        L.pattn_step(ring, a, q, kd, vd, out, ws, wsb, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        L.pattn_step(ring, a, q, kd, vd, out, ws, wsb, stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    # the same calls captured in a graph (no host launch cost), timed with events
+    per_graph = 20
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        cs = torch.cuda.current_stream()
+        for _ in range(per_graph):
+            L.pattn_step(ring, a, q, kd, vd, out, ws, wsb, cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, n_calls // per_graph)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    g_us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+    ring.close()
+    return {"workload": cfg.name, "us_per_call": el / n_calls * 1e6, "us_per_call_graph": g_us, "calls": n_calls,
+            "cached_tokens": cfg.max_seq_len, "suffix": cfg.n_dyn, "layers": cfg.num_layers}
 
 
 def bench_stack(args, torch, L, configs, synth):
@@ -289,21 +357,30 @@ def cpu_baseline(budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    layers_done = 0
-    t0 = time.perf_counter()
-    while True:
-        for l in range(s.num_layers):
+
+    def timed(budget):
+        layers_done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 <= budget:
+            l = layers_done % s.num_layers
             full_attention(ctx[l][0], ctx[l][1], ctx[l][2], s.scale)
             layers_done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
+        return layers_done, time.perf_counter() - t0
+
+    layers_done, el = timed(budget_s)
     steps = layers_done / s.num_layers
-    return {"value": steps / el, "unit": "denoise steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{layers_done} layer-attentions ({steps:.2f} 18-layer steps) of the long-history step, "
-                      f"float64 NumPy, {el:.1f} s; cpu: {_cpu_model()}"}
+    res = {"value": steps / el, "unit": "denoise steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"{layers_done} layer-attentions ({steps:.2f} 18-layer steps) of the long-history step, "
+                     f"float64 NumPy, {el:.1f} s; cpu: {_cpu_model()}"}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            n1, el1 = timed(budget_s / 2)
+        res["value_1_thread"] = n1 / s.num_layers / el1
+        res["sample_1_thread"] = f"{n1} layer-attentions, one BLAS thread, {el1:.1f} s"
+    except ImportError:
+        pass
+    return res
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -364,6 +441,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-KV multi-reader frame")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--cold-rings", type=int, default=3,
+                    help="independent rings served round-robin for the cold-MALL headline (3 x 118 MB > 256 MB)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB five times (traffic-counter calibration)")
     args = ap.parse_args()
@@ -380,9 +459,14 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
         return
-    lh = bench_long_history(args, torch, L, configs, synth)
-    log(f"long history: {lh['steps_per_s']:.1f} steps/s, partial kernel {lh['partial_us']:.1f} us "
-        f"({lh['partial_tflops']:.0f} TFLOP/s, {lh['partial_gbs']:.0f} GB/s)")
+    warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
+    log(f"long history, warm MALL: {warm['steps_per_s']:.1f} steps/s, partial kernel {warm['partial_us']:.1f} us")
+    lh = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings)
+    log(f"long history, cold MALL ({args.cold_rings} rings): {lh['steps_per_s']:.1f} steps/s, partial kernel "
+        f"{lh['partial_us']:.1f} us ({lh['partial_tflops']:.0f} TFLOP/s, {lh['partial_gbs']:.0f} GB/s)")
+    small = [bench_small(args, torch, L, c) for c in (configs.TINY, configs.PI05_1L)]
+    for sm in small:
+        log(f"{sm['workload']}: {sm['us_per_call']:.1f} us per call eager, {sm['us_per_call_graph']:.1f} in a graph")
     stack = None
     if not args.no_stack:
         stack = bench_stack(args, torch, L, configs, synth)
@@ -408,11 +492,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) K/V/Q, resident in HBM)",
+        "data": f"synthetic (seeded N(0,1) K/V/Q, resident in HBM; {lh['rings']} rings served round-robin, "
+                "so K/V streams from HBM, not the MALL)",
         "config": {"workload": "long_history_18L", "layers": s.num_layers, "q_heads": s.n_q_heads,
                    "kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "pin_tokens": s.pin_tokens,
                    "window": f"{s.num_slots}x{s.tokens_per_frame}", "suffix": s.n_dyn,
-                   "steps_per_frame": s.steps_per_frame, "kv_splits": lh["splits"] or "default"},
+                   "steps_per_frame": s.steps_per_frame, "kv_splits": lh["splits"] or "default",
+                   "rings": lh["rings"], "mall": "cold"},
         "frames_per_s": lh["steps_per_s"] / s.steps_per_frame,
         "roofline": {"bound": "mfma", "achieved": round(lh["partial_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(lh["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -423,6 +509,14 @@ def main():
                 "frac": round(lh["partial_gbs"] / HBM_PEAK_GBS, 4),
                 "kv_stream_gbs_whole_step": round(lh["kv_gbs_step"], 1)},
         "cpu_baseline": cpu,
+        "warm_mall": {"rings": 1, "steps_per_s": warm["steps_per_s"], "ms_per_step": warm["ms_per_step"],
+                      "partial_us": round(warm["partial_us"], 3),
+                      "partial_tflops": round(warm["partial_tflops"], 2),
+                      "kv_stream_gbs_whole_step": round(warm["kv_gbs_step"], 1)},
+        "small_configs": {sm["workload"]: {"us_per_call": round(sm["us_per_call"], 2),
+                                           "us_per_call_graph": round(sm["us_per_call_graph"], 2), "calls": sm["calls"],
+                                           "layers": sm["layers"], "cached_tokens": sm["cached_tokens"],
+                                           "suffix": sm["suffix"]} for sm in small},
     }
     if stack is not None:
         line["pi05_18L_full_step"] = stack

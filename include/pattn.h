@@ -172,7 +172,8 @@ typedef struct {
  * tail_len[g] of every layer, then tail_len[g] += 1 (on the device).
  * A stream whose tail is full is left unchanged and its bit is set in
  * *overflow_mask (device uint32, nullable; bit g%32). Retire a stream by
- * setting its tail_len to 0. */
+ * setting its tail_len to 0. tail_k, tail_v ([Lb][G][cap][Hkv][D]), k_new and
+ * v_new must be 16-byte aligned (PA_EINVAL otherwise). */
 pa_status pattn_append_private(const rb_ring* ring, const pattn_decode_args* args,
                                void* tail_k, void* tail_v, int32_t* tail_len,
                                const void* k_new, const void* v_new,
@@ -181,7 +182,8 @@ pa_status pattn_append_private(const rb_ring* ring, const pattn_decode_args* arg
 size_t pattn_decode_workspace_bytes(const rb_ring* ring, const pattn_decode_args* args);
 
 /* q [Lb][G][Hq][D]; out [Lb][G][Hq][D]. Each stream attends over
- * [pin; window; its own tail[0, tail_len[g])]. */
+ * [pin; window; its own tail[0, tail_len[g])]. q, out, the tails and the
+ * workspace must be 16-byte aligned (PA_EINVAL otherwise). */
 pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* args, const void* q,
                        const void* tail_k, const void* tail_v, const int32_t* tail_len,
                        void* out, void* workspace, size_t ws_bytes, void* stream);

@@ -85,66 +85,116 @@ struct Partials {
 };
 
 // ---------------------------------------------------------------------------
-// Vector (VALU) partial: one wave per query row, FP32 arithmetic. Used for
-// f32 rings, where parity is held to 1e-5 absolute.
-// grid (splits, ceil(M / 4), Lb * Hkv), block 256, dynamic LDS 4 * D floats.
-template <typename T>
-__global__ __launch_bounds__(256) void partial_valu(const T* q, long long q_layer, int hq, int group, int m_rows,
-                                                    KvSource src, int chunk, float scale_log2, Partials part) {
-    extern __shared__ float qs[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int split = blockIdx.x, lg = blockIdx.z;
-    const int lb = lg / src.hkv, g = lg % src.hkv;
-    const int row = blockIdx.y * VALU_ROWS + wave;
-    const int D = src.d;
-    const bool row_ok = row < m_rows;
-    const int tok = row / group, head = g * group + row % group;
-    for (int d = lane; d < D; d += 64)
-        qs[wave * D + d] = row_ok ? ldf(q + lb * q_layer + ((long long)tok * hq + head) * D + d) : 0.f;
-    __syncthreads();
+// Vector (VALU) attention of one query row per wave over keys [k_begin,
+// k_end), FP32 arithmetic. Keys go 64 at a time, lane j scoring key j:
+// its K row is read with 16-byte loads, all of a group in flight at once.
+// For O += P V, lane i owns dims 4i .. 4i + 3, and the rows of eight keys are
+// loaded before any is used. `row_of(j, v)` gives key j's K (v = false) or V
+// (v = true) row. Updates the running (m, l, O) in base-2 units.
+template <typename T> __device__ __forceinline__ float4 ld4f(const T* p);
+template <> __device__ __forceinline__ float4 ld4f<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> __device__ __forceinline__ float4 ld4f<uint16_t>(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+}
 
-    const int k_begin = split * chunk, k_end = min(k_begin + chunk, src.total());
-    float m = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+template <typename T, int D, typename RowOf>
+__device__ __forceinline__ void valu_row(const float* qrow, int k_begin, int k_end, float scale_log2, RowOf row_of,
+                                         float& m, float& l, float4& o) {
+    constexpr int EG = D < 64 ? D : 64;           // K elements per group of loads in flight
+    const int lane = threadIdx.x & 63;
     for (int base = k_begin; base < k_end; base += 64) {
         const int j = base + lane;
-        float s = -INFINITY;
-        if (j < k_end) {
-            bool dyn;
-            const long long off = src.offset(lb, g, j, dyn);
-            const T* kp = static_cast<const T*>(dyn ? src.dyn_k : src.ring_k) + off;
-            float z = 0.f;
-            for (int d = 0; d < D; ++d) z += qs[wave * D + d] * ldf(kp + d);
-            s = z * scale_log2;
+        const bool jv = j < k_end;
+        const T* kp = row_of(jv ? j : k_end - 1, false);
+        float z = 0.f;
+#pragma unroll 1
+        for (int g0 = 0; g0 < D; g0 += EG) {
+            float4 kv[EG / 4];
+#pragma unroll
+            for (int i = 0; i < EG / 4; ++i) kv[i] = ld4f<T>(kp + g0 + 4 * i);
+#pragma unroll
+            for (int i = 0; i < EG / 4; ++i) {
+                const float4 qq = *reinterpret_cast<const float4*>(qrow + g0 + 4 * i);
+                z = fmaf(qq.x, kv[i].x, z);
+                z = fmaf(qq.y, kv[i].y, z);
+                z = fmaf(qq.z, kv[i].z, z);
+                z = fmaf(qq.w, kv[i].w, z);
+            }
         }
-        const float mn = fmaxf(m, wave_max(s));      // finite: base < k_end
+        const float sc = jv ? z * scale_log2 : -INFINITY;
+        const float mn = fmaxf(m, wave_max(sc));      // finite: base < k_end
         const float alpha = exp2f(m - mn);
-        const float p = j < k_end ? exp2f(s - mn) : 0.f;
+        const float p = jv ? exp2f(sc - mn) : 0.f;
         l = l * alpha + wave_sum(p);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] *= alpha;
+        o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
         const int nvalid = min(64, k_end - base);
-        for (int jj = 0; jj < nvalid; ++jj) {
-            const float pj = __shfl(p, jj);
-            bool dyn;
-            const long long off = src.offset(lb, g, base + jj, dyn);
-            const T* vp = static_cast<const T*>(dyn ? src.dyn_v : src.ring_v) + off;
+        for (int j0 = 0; j0 < nvalid; j0 += 8) {
+            float4 v[8];
+            float pj[8];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int d = lane + 64 * c;
-                if (d < D) o[c] += pj * ldf(vp + d);
+            for (int u = 0; u < 8; ++u) {
+                const int jj = j0 + u;                      // < 64; p is 0 past nvalid
+                pj[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), jj));
+                const T* vp = row_of(base + min(jj, nvalid - 1), true);
+                v[u] = 4 * lane < D ? ld4f<T>(vp + 4 * lane) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                o.x = fmaf(pj[u], v[u].x, o.x); o.y = fmaf(pj[u], v[u].y, o.y);
+                o.z = fmaf(pj[u], v[u].z, o.z); o.w = fmaf(pj[u], v[u].w, o.w);
             }
         }
         m = mn;
     }
-    if (row_ok) {
-        float* op = part.optr<float>() + part.oblock(split, lg, row);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int d = lane + 64 * c;
-            if (d < D) op[part.oelem(row, d)] = o[c];
-        }
-        if (lane == 0) part.ml[part.idx(split, lg, row)] = make_float2(m, l);
+}
+
+// Store one row's partial: O (lane i: dims 4i .. 4i + 3) and (m, l).
+template <typename PO>
+__device__ __forceinline__ void store_row_partial(const Partials& part, int slot, int lg, int row, int D, float m,
+                                                  float l, float4 o) {
+    const int lane = threadIdx.x & 63;
+    PO* op = part.optr<PO>() + part.oblock(slot, lg, row);
+    if (4 * lane < D) {
+        const int d = 4 * lane;
+        stp(op + part.oelem(row, d), o.x);
+        stp(op + part.oelem(row, d + 1), o.y);
+        stp(op + part.oelem(row, d + 2), o.z);
+        stp(op + part.oelem(row, d + 3), o.w);
     }
+    if (lane == 0) part.ml[part.idx(slot, lg, row)] = make_float2(m, l);
+}
+
+// Vector partial for f32 rings (parity held to 1e-5 absolute): one wave per
+// query row of one split.
+// grid (splits, ceil(M / 4), Lb * Hkv), block 256.
+template <int D>
+__global__ __launch_bounds__(256) void partial_valu(const float* q, long long q_layer, int hq, int group, int m_rows,
+                                                    KvSource src, int chunk, float scale_log2, Partials part) {
+    __shared__ __attribute__((aligned(16))) float qs[VALU_ROWS][D];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int split = blockIdx.x, lg = blockIdx.z;
+    const int lb = lg / src.hkv, g = lg % src.hkv;
+    const int row = blockIdx.y * VALU_ROWS + wave;
+    const bool row_ok = row < m_rows;
+    const int tok = row / group, head = g * group + row % group;
+    for (int d = lane; d < D; d += 64) qs[wave][d] = row_ok ? q[lb * q_layer + ((long long)tok * hq + head) * D + d] : 0.f;
+    __syncthreads();
+    const int k_begin = split * chunk, k_end = min(k_begin + chunk, src.total());
+    const float* rk = static_cast<const float*>(src.ring_k);
+    const float* rv = static_cast<const float*>(src.ring_v);
+    const float* dk = static_cast<const float*>(src.dyn_k);
+    const float* dv = static_cast<const float*>(src.dyn_v);
+    auto row_of = [&](int j, bool v) -> const float* {
+        bool dyn;
+        const long long off = src.offset(lb, g, j, dyn);
+        return (dyn ? (v ? dv : dk) : (v ? rv : rk)) + off;
+    };
+    float m = -INFINITY, l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    valu_row<float, D>(qs[wave], k_begin, k_end, scale_log2, row_of, m, l, o);
+    if (row_ok) store_row_partial<float>(part, split, lg, row, D, m, l, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,67 +474,31 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
 // ---------------------------------------------------------------------------
 // Private-tail partial of the decode readers: one wave per (stream, head)
 // row over that stream's own appended tokens. Writes partial slot `slot`.
-// grid (ceil(M / 4), Lb * Hkv), block 256, dynamic LDS 4 * D floats.
-template <typename T>
+// grid (ceil(M / 4), Lb * Hkv), block 256.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void partial_tail(const T* q, long long q_layer, int hq, int group, int m_rows,
                                                     const T* tail_k, const T* tail_v, const int32_t* tail_len,
-                                                    int n_streams, int cap, int hkv, int D, float scale_log2,
-                                                    int slot, Partials part) {
-    extern __shared__ float qs[];
+                                                    int n_streams, int cap, int hkv, float scale_log2, int slot,
+                                                    Partials part) {
+    __shared__ __attribute__((aligned(16))) float qs[VALU_ROWS][D];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lg = blockIdx.y, lb = lg / hkv, g = lg % hkv;
     const int row = blockIdx.x * VALU_ROWS + wave;
     const bool row_ok = row < m_rows;
     const int strm = row_ok ? row / group : 0, head = g * group + row % group;
     for (int d = lane; d < D; d += 64)
-        qs[wave * D + d] = row_ok ? ldf(q + lb * q_layer + ((long long)strm * hq + head) * D + d) : 0.f;
+        qs[wave][d] = row_ok ? ldf(q + lb * q_layer + ((long long)strm * hq + head) * D + d) : 0.f;
     __syncthreads();
     int n = row_ok ? tail_len[strm] : 0;
     n = n < 0 ? 0 : (n > cap ? cap : n);
     const long long tok_base = ((long long)lb * n_streams + strm) * cap;
-    float m = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int base = 0; base < n; base += 64) {
-        const int j = base + lane;
-        float s = -INFINITY;
-        if (j < n) {
-            const T* kp = tail_k + ((tok_base + j) * hkv + g) * D;
-            float z = 0.f;
-            for (int d = 0; d < D; ++d) z += qs[wave * D + d] * ldf(kp + d);
-            s = z * scale_log2;
-        }
-        const float mn = fmaxf(m, wave_max(s));
-        const float alpha = exp2f(m - mn);
-        const float p = j < n ? exp2f(s - mn) : 0.f;
-        l = l * alpha + wave_sum(p);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] *= alpha;
-        const int nvalid = min(64, n - base);
-        for (int jj = 0; jj < nvalid; ++jj) {
-            const float pj = __shfl(p, jj);
-            const T* vp = tail_v + ((tok_base + base + jj) * hkv + g) * D;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int d = lane + 64 * c;
-                if (d < D) o[c] += pj * ldf(vp + d);
-            }
-        }
-        m = mn;
-    }
-    if (row_ok) {
-        T* op = part.optr<T>() + part.oblock(slot, lg, row);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int d = lane + 64 * c;
-            if (d < D) stp(op + part.oelem(row, d), o[c]);
-        }
-        if (lane == 0) part.ml[part.idx(slot, lg, row)] = make_float2(m, l);
-    }
+    auto row_of = [&](int j, bool v) -> const T* { return (v ? tail_v : tail_k) + ((tok_base + j) * hkv + g) * D; };
+    float m = -INFINITY, l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    valu_row<T, D>(qs[wave], 0, n, scale_log2, row_of, m, l, o);
+    if (row_ok) store_row_partial<T>(part, slot, lg, row, D, m, l, o);
 }
 
-// ---------------------------------------------------------------------------
-// Log-sum-exp combine of `n_parts` partials per row (Prop. A.1), FP32.
-// One wave per query row; writes out[lb][token][head][d] in the output dtype.
-// grid (ceil(M / 4), Lb * Hkv), block 256.
 // Four consecutive outputs of one row: one 8-byte (bf16) or 16-byte (f32) store.
 __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 __device__ __forceinline__ void st4(uint16_t* p, float4 v) {
@@ -562,21 +576,39 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m
 
 // ---------------------------------------------------------------------------
 // Append one token per decode stream to its private tail, in every layer.
+// 16-byte chunks; each thread copies up to APPEND_BATCH chunks (of any
+// layers) with every load issued before the first store.
 // grid (G), block 256.
-template <typename T>
-__global__ __launch_bounds__(256) void append_tail(T* tail_k, T* tail_v, int32_t* tail_len, const T* k_new,
-                                                   const T* v_new, int n_layers, int n_streams, int cap,
-                                                   int tok_elems, uint32_t* overflow) {
+constexpr int APPEND_BATCH = 8;
+
+__global__ __launch_bounds__(256) void append_tail(uint4* __restrict__ tail_k, uint4* __restrict__ tail_v,
+                                                   int32_t* tail_len, const uint4* __restrict__ k_new,
+                                                   const uint4* __restrict__ v_new, int n_layers, int n_streams,
+                                                   int cap, int tok_chunks, uint32_t* overflow) {
     const int strm = blockIdx.x;
     const int n = tail_len[strm];
     const bool ok = n >= 0 && n < cap;
     if (ok) {
-        for (int lb = 0; lb < n_layers; ++lb) {
-            const long long src = ((long long)lb * n_streams + strm) * tok_elems;
-            const long long dst = (((long long)lb * n_streams + strm) * cap + n) * tok_elems;
-            for (int e = threadIdx.x; e < tok_elems; e += blockDim.x) {
-                tail_k[dst + e] = k_new[src + e];
-                tail_v[dst + e] = v_new[src + e];
+        const int total = n_layers * tok_chunks;       // (layer, chunk) items of this stream
+        for (int i0 = threadIdx.x; i0 < total; i0 += 256 * APPEND_BATCH) {
+            uint4 kk[APPEND_BATCH], vv[APPEND_BATCH];
+#pragma unroll
+            for (int u = 0; u < APPEND_BATCH; ++u) {
+                const int it = min(i0 + 256 * u, total - 1);
+                const int lb = it / tok_chunks, c = it % tok_chunks;
+                const long long src = ((long long)lb * n_streams + strm) * tok_chunks + c;
+                kk[u] = k_new[src];
+                vv[u] = v_new[src];
+            }
+#pragma unroll
+            for (int u = 0; u < APPEND_BATCH; ++u) {
+                const int it = i0 + 256 * u;
+                if (it < total) {
+                    const int lb = it / tok_chunks, c = it % tok_chunks;
+                    const long long dst = (((long long)lb * n_streams + strm) * cap + n) * tok_chunks + c;
+                    tail_k[dst] = kk[u];
+                    tail_v[dst] = vv[u];
+                }
             }
         }
     }
@@ -706,8 +738,14 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
                                                                   scale_log2, part, p.parts, row_blocks);
     } else {
         dim3 grid(p.parts, valu_row_blocks(p.m_rows), p.lg_count);
-        partial_valu<float><<<grid, 256, VALU_ROWS * d * sizeof(float), stream>>>(
-            static_cast<const float*>(q), q_layer, hq, p.group, p.m_rows, src, p.chunk, scale_log2, part);
+        const float* qf = static_cast<const float*>(q);
+#define PA_VALU(DD) partial_valu<DD><<<grid, 256, 0, stream>>>(qf, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
+                                                                scale_log2, part)
+        if (d == 256) PA_VALU(256);
+        else if (d == 128) PA_VALU(128);
+        else if (d == 64) PA_VALU(64);
+        else PA_VALU(32);
+#undef PA_VALU
     }
     PA_LAUNCHED();
     return PA_OK;
@@ -819,16 +857,14 @@ extern "C" pa_status pattn_append_private(const rb_ring* ring, const pattn_decod
     pa_status st = check_decode(r, a);
     if (st != PA_OK) return st;
     PA_CHECK_ARG(tail_k && tail_v && tail_len && k_new && v_new, PA_EINVAL, "pattn_append_private: null argument");
+    PA_CHECK_ARG(aligned16(tail_k) && aligned16(tail_v) && aligned16(k_new) && aligned16(v_new), PA_EINVAL,
+                 "pattn_append_private: buffers must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int tok = r->cfg.num_kv_heads * r->cfg.head_dim;
-    if (r->cfg.dtype == PA_F32)
-        append_tail<float><<<a->n_streams, 256, 0, s>>>(static_cast<float*>(tail_k), static_cast<float*>(tail_v), tail_len,
-                                                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
-                                                        a->num_layers, a->n_streams, a->tail_capacity, tok, overflow);
-    else
-        append_tail<uint16_t><<<a->n_streams, 256, 0, s>>>(
-            static_cast<uint16_t*>(tail_k), static_cast<uint16_t*>(tail_v), tail_len, static_cast<const uint16_t*>(k_new),
-            static_cast<const uint16_t*>(v_new), a->num_layers, a->n_streams, a->tail_capacity, tok, overflow);
+    // a token of one layer is Hkv * D elements: a whole number of 16-byte chunks (D >= 32)
+    const int tok_chunks = (int)((size_t)r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes() / 16);
+    append_tail<<<a->n_streams, 256, 0, s>>>(static_cast<uint4*>(tail_k), static_cast<uint4*>(tail_v), tail_len,
+                                             static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                                             a->num_layers, a->n_streams, a->tail_capacity, tok_chunks, overflow);
     PA_LAUNCHED();
     return PA_OK;
 }
@@ -849,7 +885,8 @@ extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* 
     pa_status st = check_decode(r, a);
     if (st != PA_OK) return st;
     PA_CHECK_ARG(q && tail_k && tail_v && tail_len && out && ws, PA_EINVAL, "pattn_decode: null argument");
-    PA_CHECK_ARG(aligned16(q) && aligned16(out) && aligned16(ws) && aligned16(r->k) && aligned16(r->v), PA_EINVAL,
+    PA_CHECK_ARG(aligned16(q) && aligned16(out) && aligned16(ws) && aligned16(r->k) && aligned16(r->v) &&
+                     aligned16(tail_k) && aligned16(tail_v), PA_EINVAL,
                  "pattn_decode: buffers must be 16-byte aligned");
     Plan p;
     st = plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_streams, 0, a->num_splits, 1, &p);
@@ -866,15 +903,21 @@ extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* 
     if (st != PA_OK) return st;
     const float scale_log2 = a->scale * 1.4426950408889634f;
     dim3 grid(valu_row_blocks(p.m_rows), p.lg_count);
-    if (r->cfg.dtype == PA_F32)
-        partial_tail<float><<<grid, 256, VALU_ROWS * d * sizeof(float), s>>>(
-            static_cast<const float*>(q), q_layer, a->n_q_heads, p.group, p.m_rows, static_cast<const float*>(tail_k),
-            static_cast<const float*>(tail_v), tail_len, a->n_streams, a->tail_capacity, hkv, d, scale_log2, p.parts, part);
-    else
-        partial_tail<uint16_t><<<grid, 256, VALU_ROWS * d * sizeof(float), s>>>(
-            static_cast<const uint16_t*>(q), q_layer, a->n_q_heads, p.group, p.m_rows,
-            static_cast<const uint16_t*>(tail_k), static_cast<const uint16_t*>(tail_v), tail_len, a->n_streams,
-            a->tail_capacity, hkv, d, scale_log2, p.parts, part);
+#define PA_TAIL(T, DD)                                                                                          \
+    partial_tail<T, DD><<<grid, 256, 0, s>>>(static_cast<const T*>(q), q_layer, a->n_q_heads, p.group, p.m_rows, \
+                                             static_cast<const T*>(tail_k), static_cast<const T*>(tail_v), tail_len, \
+                                             a->n_streams, a->tail_capacity, hkv, scale_log2, p.parts, part)
+    if (r->cfg.dtype == PA_F32) {
+        if (d == 256) PA_TAIL(float, 256);
+        else if (d == 128) PA_TAIL(float, 128);
+        else if (d == 64) PA_TAIL(float, 64);
+        else PA_TAIL(float, 32);
+    } else {
+        if (d == 256) PA_TAIL(uint16_t, 256);
+        else if (d == 128) PA_TAIL(uint16_t, 128);
+        else PA_TAIL(uint16_t, 64);
+    }
+#undef PA_TAIL
     PA_LAUNCHED();
     return launch_combine(r, p, p.parts + 1, a->n_q_heads, q_layer, out, a->out_dtype, part, s);
 }
