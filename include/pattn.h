@@ -102,6 +102,35 @@ pa_status rb_push_frame(rb_ring* ring, const void* k, const void* v, void* strea
 
 pa_status rb_get_state(const rb_ring* ring, rb_state* out);
 
+/* ------------------------------------------------------------------------
+ * Capsules (FlashRT article, PaperDaily, "FlashRT开源：27倍加速…": the
+ * section on what a capsule is, and Fig. 2, the snapshot / restore / fork /
+ * rollback verbs as operations on a set of static device buffers). The
+ * ring's live state at a frame boundary is its valid K/V region plus the
+ * metadata in rb_state. A capsule holds that region compactly: K then V,
+ * each [L][pinned + count*F][Hkv][D] (per layer the pinned tokens, then the
+ * first `count` slots). It may live in device memory or in host memory
+ * (pinned host memory keeps the copies asynchronous).
+ *   fork     = restore one capsule into several rings of the same config;
+ *   rollback = restore an earlier capsule of the same ring.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of a capsule of the ring's current state (0 for a null ring). */
+size_t rb_capsule_bytes(const rb_ring* ring);
+
+/* Copy the valid region into `capsule` (stream-ordered) and return the
+ * metadata in *state. PA_ERANGE: capsule_bytes < rb_capsule_bytes(). */
+pa_status rb_snapshot(const rb_ring* ring, void* capsule, size_t capsule_bytes, rb_state* state,
+                      void* stream);
+
+/* Copy a capsule back into the ring's buffers (stream-ordered) and adopt
+ * *state. Tokens outside the restored valid region keep whatever they held;
+ * no call reads them. The ring must have the capsule's config.
+ * PA_EINVAL: a state no ring of this config reaches (pinned > P, or head /
+ * count not consistent with frames_pushed); PA_ERANGE: capsule too small. */
+pa_status rb_restore(rb_ring* ring, const void* capsule, size_t capsule_bytes, const rb_state* state,
+                     void* stream);
+
 /* ========================================================================
  * Partitioned attention (Reflex review §3 Eq. 1; Prop. A.1):
  *     out = softmax(scale * Q [K_pin; K_slide; K_dyn]^T) [V_pin; V_slide; V_dyn]

@@ -13,11 +13,22 @@ review:
   ``ptr = 0``; ``add_new_prefix`` adds the new observation and reports the
   eviction; ``evict_source_prefix`` removes the oldest frame from all layers.
 
+Capsules follow the FlashRT article (PaperDaily, "FlashRT开源：27倍加速…"),
+the section on what a capsule is and Fig. 2: the live state at a commit
+boundary is a fixed set of buffers plus metadata; snapshot freezes it,
+restore copies it back and rebinds the metadata, fork restores one capsule
+into several sessions, rollback restores an earlier one. For the ring the
+live state is the valid region (pinned tokens and the first ``count`` slots
+of every layer) and (head, count, pinned, frames_pushed).
+
 Readings taken:
 * the pin occupies tokens [0, P) of the same buffer, so max_seq_len = P + W*F;
 * ``ptr`` is a slot index that advances by one per frame, modulo W;
 * a push overwrites slot ``head`` in every layer (that overwrite *is* the
-  eviction of the frame pushed W frames earlier) and nothing else moves.
+  eviction of the frame pushed W frames earlier) and nothing else moves;
+* a capsule stores the valid region compactly, K then V, each
+  ``[L][pinned + count*F][Hkv][D]``; a restore writes it back in place and
+  leaves every other token as it was (no call reads those).
 
 The model stores raw words (``uint16`` for bf16 bits, ``uint32`` for fp32
 bits) so that device buffers can be compared with ``array_equal``.
@@ -84,3 +95,28 @@ class RingModel:
     def state(self) -> dict:
         return {"head": self.head, "count": self.count, "pinned": self.pinned,
                 "frames_pushed": self.frames_pushed}
+
+    # -- capsules: snapshot / restore (fork and rollback are restores) --------
+    def valid_tokens(self) -> list[int]:
+        """Token indices of the valid region of a layer, in capsule order."""
+        return list(range(self.pinned)) + list(range(self.P, self.P + self.count * self.F))
+
+    def capsule(self) -> dict:
+        """The valid region, compact, plus the metadata."""
+        idx = self.valid_tokens()
+        return {"k": self.k[:, idx].copy(), "v": self.v[:, idx].copy(), "state": self.state()}
+
+    def restore(self, cap: dict) -> None:
+        st = cap["state"]
+        fp, count, head, pinned = st["frames_pushed"], st["count"], st["head"], st["pinned"]
+        if not (0 <= pinned <= self.P and fp >= 0 and count == min(fp, self.W) and head == fp % self.W):
+            raise ValueError(f"state {st} is not reachable by this ring")
+        self.pinned, self.count, self.head, self.frames_pushed = pinned, count, head, fp
+        idx = self.valid_tokens()
+        self.k[:, idx] = cap["k"]
+        self.v[:, idx] = cap["v"]
+        # slot s holds the latest frame f < frames_pushed with f = s (mod W)
+        self.slot_frame = [-1] * self.W
+        for f in range(max(0, fp - self.W), fp):
+            self.slot_frame[f % self.W] = f
+

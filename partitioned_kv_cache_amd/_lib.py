@@ -35,7 +35,7 @@ EXPORTS = (
     "pattn_workspace_bytes", "pattn_step", "pattn_append_private", "pattn_decode_workspace_bytes",
     "pattn_decode", "ada_gamma_workspace_bytes", "ada_gamma", "ada_rmsnorm_workspace_bytes", "ada_rmsnorm",
     "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
-    "pa_denoise_step_workspace_bytes", "pa_denoise_step",
+    "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
 )
 
 
@@ -95,6 +95,9 @@ _sig("rb_destroy", _i32, _vp)
 _sig("rb_pin_prefix", _i32, _vp, _vp, _vp, _i32, _vp)
 _sig("rb_push_frame", _i32, _vp, _vp, _vp, _vp, C.POINTER(C.c_int64))
 _sig("rb_get_state", _i32, _vp, C.POINTER(RbState))
+_sig("rb_capsule_bytes", _sz, _vp)
+_sig("rb_snapshot", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
+_sig("rb_restore", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
 _sig("pattn_workspace_bytes", _sz, _vp, C.POINTER(PattnArgs))
 _sig("pattn_step", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp)
 _sig("pattn_step_timed", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp)
@@ -168,6 +171,21 @@ class Ring:
         s = RbState()
         _check(_lib.rb_get_state(self.handle, C.byref(s)), "rb_get_state")
         return {"head": s.head, "count": s.count, "pinned": s.pinned, "frames_pushed": s.frames_pushed}
+
+    # capsules: the valid K/V region plus the metadata (rb_snapshot / rb_restore)
+    def capsule_bytes(self) -> int:
+        return _lib.rb_capsule_bytes(self.handle)
+
+    def snapshot(self, capsule, capsule_bytes: int | None = None, stream=None) -> dict:
+        s = RbState()
+        nb = capsule.numel() * capsule.element_size() if capsule_bytes is None else capsule_bytes
+        _check(_lib.rb_snapshot(self.handle, ptr(capsule), nb, C.byref(s), _stream(stream)), "rb_snapshot")
+        return {"head": s.head, "count": s.count, "pinned": s.pinned, "frames_pushed": s.frames_pushed}
+
+    def restore(self, capsule, state: dict, capsule_bytes: int | None = None, stream=None):
+        s = RbState(state["head"], state["count"], state["pinned"], 0, state["frames_pushed"])
+        nb = capsule.numel() * capsule.element_size() if capsule_bytes is None else capsule_bytes
+        _check(_lib.rb_restore(self.handle, ptr(capsule), nb, C.byref(s), _stream(stream)), "rb_restore")
 
 
 def rb_config(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype) -> RbConfig:

@@ -120,3 +120,90 @@ extern "C" pa_status rb_get_state(const rb_ring* ring, rb_state* out) {
     out->frames_pushed = r->frames_pushed;
     return PA_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Capsules: FlashRT article (PaperDaily, "FlashRT开源：27倍加速…"), the
+// section on what a capsule is and Fig. 2 (snapshot, restore, fork and
+// rollback as operations on a set of static buffers). For this ring the live
+// state at a frame boundary is the valid K/V region plus (head, count,
+// pinned, frames_pushed). A capsule stores that region compactly, K then V,
+// each [L][pinned + count * F][Hkv][D]: the pinned tokens of a layer, then
+// its first count slots (the slots a ring fills before it wraps, or all of
+// them once full).
+
+static int64_t capsule_tokens(const Ring* r) { return (int64_t)r->pinned + (int64_t)r->count * r->cfg.tokens_per_frame; }
+
+static size_t capsule_bytes_of(const Ring* r, int64_t ctok) {
+    return (size_t)(2 * r->cfg.num_layers * ctok * r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes());
+}
+
+// Copy the valid region between the ring (layer pitch P + W*F tokens) and a
+// capsule (layer pitch ctok tokens), one 2-D copy per region and tensor.
+static pa_status capsule_copy(Ring* r, char* cap, int32_t pinned, int64_t count, bool to_capsule, hipStream_t s) {
+    const int64_t tok = (int64_t)r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes();
+    const int64_t ctok = pinned + count * r->cfg.tokens_per_frame;
+    const size_t rpitch = (size_t)(r->seq_len() * tok), cpitch = (size_t)(ctok * tok);
+    const size_t layers = (size_t)r->cfg.num_layers;
+    for (int t = 0; t < 2; ++t) {
+        char* ring = static_cast<char*>(t == 0 ? r->k : r->v);
+        char* c = cap + (size_t)t * layers * cpitch;
+        struct { int64_t ring_tok, cap_tok, n; } reg[2] = {
+            {0, 0, pinned}, {r->cfg.pin_capacity, pinned, count * r->cfg.tokens_per_frame}};
+        for (const auto& g : reg) {
+            if (g.n == 0) continue;
+            char* rp = ring + g.ring_tok * tok;
+            char* cp = c + g.cap_tok * tok;
+            const size_t w = (size_t)(g.n * tok);
+            if (to_capsule)
+                PA_HIP(hipMemcpy2DAsync(cp, cpitch, rp, rpitch, w, layers, hipMemcpyDefault, s));
+            else
+                PA_HIP(hipMemcpy2DAsync(rp, rpitch, cp, cpitch, w, layers, hipMemcpyDefault, s));
+        }
+    }
+    return PA_OK;
+}
+
+extern "C" size_t rb_capsule_bytes(const rb_ring* ring) {
+    pa::clear_error();
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    return r ? capsule_bytes_of(r, capsule_tokens(r)) : 0;
+}
+
+extern "C" pa_status rb_snapshot(const rb_ring* ring, void* capsule, size_t capsule_bytes, rb_state* state,
+                                 void* stream) {
+    pa::clear_error();
+    Ring* r = const_cast<Ring*>(reinterpret_cast<const Ring*>(ring));
+    PA_CHECK_ARG(r && state, PA_EINVAL, "rb_snapshot: null argument");
+    const size_t need = capsule_bytes_of(r, capsule_tokens(r));
+    PA_CHECK_ARG(capsule || need == 0, PA_EINVAL, "rb_snapshot: null capsule");
+    PA_CHECK_ARG(capsule_bytes >= need, PA_ERANGE, "rb_snapshot: capsule %zu bytes < %zu needed", capsule_bytes, need);
+    pa_status st = capsule_copy(r, static_cast<char*>(capsule), r->pinned, r->count, true, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+    return rb_get_state(ring, state);
+}
+
+extern "C" pa_status rb_restore(rb_ring* ring, const void* capsule, size_t capsule_bytes, const rb_state* state,
+                                void* stream) {
+    pa::clear_error();
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    PA_CHECK_ARG(r && state, PA_EINVAL, "rb_restore: null argument");
+    const int W = r->cfg.num_slots;
+    const int64_t fp = state->frames_pushed;
+    PA_CHECK_ARG(state->pinned >= 0 && state->pinned <= r->cfg.pin_capacity, PA_EINVAL,
+                 "rb_restore: pinned %d not in [0, %d]", state->pinned, r->cfg.pin_capacity);
+    PA_CHECK_ARG(fp >= 0 && state->count == (fp < W ? fp : W) && state->head == (int32_t)(fp % W), PA_EINVAL,
+                 "rb_restore: state (head %d, count %d, frames_pushed %lld) is not one a ring of %d slots reaches",
+                 state->head, state->count, (long long)fp, W);
+    const size_t need = capsule_bytes_of(r, state->pinned + (int64_t)state->count * r->cfg.tokens_per_frame);
+    PA_CHECK_ARG(capsule || need == 0, PA_EINVAL, "rb_restore: null capsule");
+    PA_CHECK_ARG(capsule_bytes >= need, PA_ERANGE, "rb_restore: capsule %zu bytes < %zu needed", capsule_bytes, need);
+    pa_status st = capsule_copy(r, const_cast<char*>(static_cast<const char*>(capsule)), state->pinned, state->count,
+                                false, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+    r->head = state->head;
+    r->count = state->count;
+    r->pinned = state->pinned;
+    r->frames_pushed = fp;
+    return PA_OK;
+}
+

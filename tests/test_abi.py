@@ -26,7 +26,7 @@ def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("rb_create", "rb_pin_prefix", "rb_push_frame", "rb_get_state", "pattn_step", "ada_rmsnorm",
               "ada_gamma", "ada_rmsnorm_qkv", "pattn_decode", "pattn_append_private", "oproj_residual",
-              "pa_last_error"):
+              "pa_last_error", "rb_capsule_bytes", "rb_snapshot", "rb_restore"):
         assert n in names
 
 
@@ -131,3 +131,29 @@ def test_ada_validation_without_device():
     with pytest.raises(L.PattnError) as e:
         L.oproj_residual(_fake(1), _fake(2), _fake(3), 51, 2000, 1024, stream=0)
     assert e.value.status == L.PA_ESHAPE
+
+
+def test_capsule_validation_without_device():
+    """Sizes and state checks of rb_snapshot / rb_restore run on the host before any copy."""
+    from partitioned_kv_cache_amd import _lib as L
+    r = L.Ring(L.rb_config(2, 1, 64, 16, 4, 16, L.PA_F32), _fake(1), _fake(2))
+    assert r.capsule_bytes() == 0                     # nothing pinned or pushed: an empty capsule
+    st = r.snapshot(None, capsule_bytes=0, stream=0)
+    assert st == {"head": 0, "count": 0, "pinned": 0, "frames_pushed": 0}
+    r.restore(None, st, capsule_bytes=0, stream=0)
+    # a full 4-slot window with 16 pinned tokens: 2 x 2 layers x (16 + 4 x 16) tokens x 64 x 4 bytes
+    full = {"head": 1, "count": 4, "pinned": 16, "frames_pushed": 9}
+    need = 2 * 2 * (16 + 4 * 16) * 64 * 4
+    with pytest.raises(L.PattnError) as e:
+        r.restore(_fake(3), full, capsule_bytes=need - 1, stream=0)
+    assert e.value.status == L.PA_ERANGE
+    for bad in ({"head": 2, "count": 4, "pinned": 16, "frames_pushed": 9},      # head != 9 mod 4
+                {"head": 1, "count": 3, "pinned": 16, "frames_pushed": 9},      # count != min(9, 4)
+                {"head": 0, "count": 0, "pinned": 17, "frames_pushed": 0},      # pinned > P
+                {"head": 0, "count": 0, "pinned": 0, "frames_pushed": -1}):
+        with pytest.raises(L.PattnError) as e:
+            r.restore(_fake(3), bad, capsule_bytes=need, stream=0)
+        assert e.value.status == L.PA_EINVAL
+    assert r.state() == {"head": 0, "count": 0, "pinned": 0, "frames_pushed": 0}   # rejected restores change nothing
+    r.close()
+

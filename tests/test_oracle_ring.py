@@ -64,3 +64,82 @@ def test_layout_matches_the_pages_buffer():
     ring = RingModel(18, 1, 256, 48, 2, 768)
     assert ring.k.shape == (18, 48 + 2 * 768, 1, 256) and ring.k.dtype == np.uint16
     assert not ring.k.any() and not ring.v.any()
+
+
+# ---------------------------------------------------------------- capsules ----
+# FlashRT article (PaperDaily), the section on what a capsule is and Fig. 2:
+# a restore must give back exactly the state frozen at the snapshot. The
+# expected state is rebuilt independently, by replaying the same pushes into
+# a fresh ring, never by the capsule code itself.
+
+def _replay(L, H, D, P, W, F, pin_n, n_frames):
+    r = RingModel(L, H, D, P, W, F)
+    if pin_n:
+        r.pin(np.full((L, pin_n, H, D), 60001, np.uint16), np.full((L, pin_n, H, D), 60002, np.uint16))
+    for f in range(n_frames):
+        r.push(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1))
+    return r
+
+
+def _context(r):
+    """Chronological [pin; window] K and V of every layer, read through the slot map."""
+    ks = [r.k[:, :r.pinned]] + [r.k[:, r.P + (g % r.W) * r.F:r.P + (g % r.W + 1) * r.F] for g in r.window_frames()]
+    vs = [r.v[:, :r.pinned]] + [r.v[:, r.P + (g % r.W) * r.F:r.P + (g % r.W + 1) * r.F] for g in r.window_frames()]
+    return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+
+
+@pytest.mark.parametrize("L,P,pin_n,W,F,t,more", [(2, 8, 8, 4, 3, 2, 7), (1, 5, 3, 3, 2, 5, 4), (3, 0, 0, 2, 4, 0, 3),
+                                                   (3, 6, 6, 4, 2, 9, 1)])
+def test_capsule_round_trip_equals_replay(L, P, pin_n, W, F, t, more):
+    H, D = 1, 2
+    live = _replay(L, H, D, P, W, F, pin_n, t)
+    cap = live.capsule()
+    # the compact layout: per layer the pinned tokens, then slots 0 .. count-1
+    ntok = pin_n + min(t, W) * F
+    assert cap["k"].shape == cap["v"].shape == (L, ntok, H, D)
+    assert np.all(cap["k"][:, :pin_n] == 60001) and np.all(cap["v"][:, :pin_n] == 60002)
+    for slot in range(min(t, W)):
+        f = max(g for g in range(t) if g % W == slot)          # the newest frame written to that slot
+        seg = slice(pin_n + slot * F, pin_n + (slot + 1) * F)
+        assert np.array_equal(cap["k"][:, seg], _frame(L, F, H, D, f, 0))
+        assert np.array_equal(cap["v"][:, seg], _frame(L, F, H, D, f, 1))
+    for f in range(t, t + more):                              # move on, wrapping the window
+        live.push(_frame(L, F, H, D, f + 100, 0), _frame(L, F, H, D, f + 100, 1))
+    live.restore(cap)                                          # rollback
+    ref = _replay(L, H, D, P, W, F, pin_n, t)
+    assert live.state() == ref.state() and live.window_frames() == ref.window_frames()
+    for a, b in zip(_context(live), _context(ref)):
+        assert np.array_equal(a, b)
+    # the restored ring keeps evolving like the original: same eviction ids, same bytes
+    for f in range(t, t + W + 1):
+        assert live.push(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1)) == \
+            ref.push(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1))
+        for a, b in zip(_context(live), _context(ref)):
+            assert np.array_equal(a, b)
+
+
+def test_fork_gives_independent_sessions():
+    L, H, D, P, W, F = 2, 1, 2, 4, 3, 2
+    src = _replay(L, H, D, P, W, F, 4, 5)
+    cap = src.capsule()
+    a, b = RingModel(L, H, D, P, W, F), RingModel(L, H, D, P, W, F)
+    a.restore(cap)
+    b.restore(cap)
+    for x in (a, b):
+        assert x.state() == src.state()
+        for u, w in zip(_context(x), _context(src)):
+            assert np.array_equal(u, w)
+    a.push(_frame(L, F, H, D, 900, 0), _frame(L, F, H, D, 900, 1))
+    b.push(_frame(L, F, H, D, 901, 0), _frame(L, F, H, D, 901, 1))
+    assert not np.array_equal(_context(a)[0], _context(b)[0])        # diverged
+    assert np.array_equal(_context(src)[0], _context(_replay(L, H, D, P, W, F, 4, 5))[0])   # source untouched
+
+
+def test_restore_rejects_unreachable_states():
+    r = RingModel(1, 1, 2, 4, 3, 2)
+    cap = r.capsule()
+    for bad in ({"head": 1, "count": 0, "pinned": 0, "frames_pushed": 0},
+                {"head": 0, "count": 3, "pinned": 0, "frames_pushed": 2},
+                {"head": 0, "count": 0, "pinned": 5, "frames_pushed": 0}):
+        with pytest.raises(ValueError):
+            r.restore({"k": cap["k"], "v": cap["v"], "state": bad})
