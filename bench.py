@@ -146,6 +146,66 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1):
     return res
 
 
+def bench_async_push(args, torch, L, configs, synth, n_frames=40):
+    """Frames/s of the long-history workload on a ring with a spare slot:
+    pushes on the denoising stream (synchronous) against frames staged on a
+    producer stream while the previous frame's ten steps run (overlapped)."""
+    s = configs.LONG_18L
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    seq = s.pin_tokens + (s.num_slots + 1) * s.tokens_per_frame
+    shp = (s.num_layers, seq, s.n_kv_heads, s.head_dim)
+    k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
+                              s.tokens_per_frame, L.PA_BF16, 1), k_buf, v_buf)
+    pk, pv = synth.pin_kv(s)
+    ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
+    pool = [tuple(dev(a) for a in synth.frame_kv(s, f)) for f in range(4)]
+    steps_in = [tuple(dev(a) for a in synth.suffix_qkv(s, 0, k)) for k in range(s.steps_per_frame)]
+    for f in range(s.num_slots + 1):
+        ring.push_frame(*pool[f % 4])
+    args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits)
+    wsb = L.pattn_workspace_bytes(ring, args_)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+    consumer, producer = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def steps():
+        for k in range(s.steps_per_frame):
+            q, kd, vd = steps_in[k]
+            L.pattn_step(ring, args_, q, kd, vd, out, ws, wsb, consumer)
+
+    def run_sync(n):
+        for f in range(n):
+            ring.push_frame(*pool[f % 4], consumer)
+            steps()
+
+    def run_async(n):
+        for f in range(n):
+            ring.commit_frame(consumer)               # frame f joins the window
+            ring.stage_frame(*pool[(f + 1) % 4], producer)   # frame f+1 fills the spare meanwhile
+            steps()
+
+    res = {}
+    for name, fn in (("sync", run_sync), ("async", None)):
+        if name == "async":
+            ring.stage_frame(*pool[0], producer)
+            fn = run_async
+        fn(3)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn(n_frames)
+        torch.cuda.synchronize()
+        res[name] = n_frames / (time.perf_counter() - t0)
+    ring.commit_frame(consumer)
+    torch.cuda.synchronize()
+    ring.close()
+    return {"workload": "long_history_18L, window of 8 frames plus one spare slot",
+            "frames_per_s_sync_push": res["sync"], "frames_per_s_overlapped_push": res["async"],
+            "us_per_frame_sync": 1e6 / res["sync"], "us_per_frame_overlapped": 1e6 / res["async"],
+            "frames_timed": n_frames}
+
+
 def bench_small(args, torch, L, cfg, n_calls=2000):
     """Microseconds per pattn_step call on a small, launch-latency-bound
     configuration (whole window full)."""
@@ -471,6 +531,9 @@ def main():
     if not args.no_stack:
         stack = bench_stack(args, torch, L, configs, synth)
         log(f"pi05 18L stack: {stack['us_per_step']:.1f} us/step")
+    async_push = bench_async_push(args, torch, L, configs, synth)
+    log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
+        f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
     shared = None
     if not args.no_shared:
         shared = bench_shared_kv(args, torch, L, configs, synth)
@@ -518,6 +581,7 @@ def main():
                                            "layers": sm["layers"], "cached_tokens": sm["cached_tokens"],
                                            "suffix": sm["suffix"]} for sm in small},
     }
+    line["async_push"] = async_push
     if stack is not None:
         line["pi05_18L_full_step"] = stack
     if shared is not None:

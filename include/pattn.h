@@ -56,11 +56,19 @@ const char* pa_last_error(void);
 /* ========================================================================
  * Ring buffer (Reflex review §3 ring-buffer diagram and component table,
  * §5 ring-buffer initialisation): two zero-initialised static buffers
- *     K, V : [num_layers][P + W*F][num_kv_heads][head_dim]
- * Tokens [0, P) hold the pinned prefix; slot s (0 <= s < W) holds tokens
- * [P + s*F, P + (s+1)*F). Frame f is written to slot f mod W, so a push
- * overwrites the frame pushed W frames earlier: that overwrite is the
- * eviction. The library never reallocates or moves the buffers.
+ *     K, V : [num_layers][P + S*F][num_kv_heads][head_dim],  S = W + spare_slots
+ * Tokens [0, P) hold the pinned prefix; slot s (0 <= s < S) holds tokens
+ * [P + s*F, P + (s+1)*F). Frame f is written to slot f mod S and the window
+ * is the newest W frames. With S = W a push overwrites the frame pushed W
+ * frames earlier: that overwrite is the eviction. The library never
+ * reallocates or moves the buffers.
+ *
+ * A spare slot (spare_slots = 1) lets a producer fill the next frame while
+ * steps on another stream still read the window (Reflex review, system
+ * architecture, Figure 3: a vision thread pushes into the shared cache while
+ * the policy thread denoises from it): the spare slot is never part of the
+ * window, rb_stage_frame fills it, rb_commit_frame makes it the newest
+ * window slot and frees the oldest, which becomes the next spare.
  * ====================================================================== */
 typedef struct {
     int32_t num_layers;        /* L  > 0 */
@@ -70,11 +78,12 @@ typedef struct {
     int32_t num_slots;         /* W > 0: frames in the sliding window */
     int32_t tokens_per_frame;  /* F > 0 */
     int32_t dtype;             /* pa_dtype of the K/V words */
+    int32_t spare_slots;       /* 0, or 1 for asynchronous pushes (rb_stage_frame / rb_commit_frame) */
 } rb_config;
 
 typedef struct {
-    int32_t head;              /* slot the next push writes */
-    int32_t count;             /* valid slots, min(frames_pushed, W) */
+    int32_t head;              /* slot the next push writes: frames_pushed mod S */
+    int32_t count;             /* frames in the window, min(frames_pushed, W) */
     int32_t pinned;            /* pinned prefix tokens (0 until rb_pin_prefix) */
     int32_t reserved;
     int64_t frames_pushed;
@@ -94,11 +103,25 @@ pa_status rb_destroy(rb_ring* ring);
 pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, int32_t n_tokens, void* stream);
 
 /* Enqueue one frame, K/V [L][F][Hkv][D]: one strided device copy into slot
- * `head` of every layer, then head = (head+1) mod W and count = min(count+1, W)
- * on the host. O(1) in the window length; no allocation.
- * *evicted_frame (nullable) receives the id of the frame overwritten, or -1. */
+ * `head` of every layer, then head = (head+1) mod S and count = min(count+1, W)
+ * on the host. O(1) in the window length; no allocation. The copy is ordered
+ * after earlier work on `stream` only.
+ * *evicted_frame (nullable) receives the id of the frame that left the
+ * window, or -1. PA_ESTATE: a staged frame is pending. */
 pa_status rb_push_frame(rb_ring* ring, const void* k, const void* v, void* stream,
                         int64_t* evicted_frame);
+
+/* Asynchronous push, step 1 (rings with a spare slot): copy the frame into
+ * the spare slot on the producer's `stream`, after every step enqueued before
+ * the last commit (they may still read the slot); the window is unchanged.
+ * PA_ESTATE: no spare slot, or a staged frame is already pending. */
+pa_status rb_stage_frame(rb_ring* ring, const void* k, const void* v, void* stream);
+
+/* Asynchronous push, step 2: work enqueued on the consumer's `stream` after
+ * this call waits for the staging copy and sees the new window (the staged
+ * frame newest, the oldest frame evicted). Host metadata only besides the
+ * two stream-ordered event operations. PA_ESTATE: nothing staged. */
+pa_status rb_commit_frame(rb_ring* ring, void* stream, int64_t* evicted_frame);
 
 pa_status rb_get_state(const rb_ring* ring, rb_state* out);
 

@@ -28,7 +28,14 @@ Readings taken:
   eviction of the frame pushed W frames earlier) and nothing else moves;
 * a capsule stores the valid region compactly, K then V, each
   ``[L][pinned + count*F][Hkv][D]``; a restore writes it back in place and
-  leaves every other token as it was (no call reads those).
+  leaves every other token as it was (no call reads those);
+* asynchronous pushes (Reflex review, system architecture, Figure 3: the
+  vision thread pushes into the shared cache while the policy thread
+  denoises) need a slot no running step reads: with ``spare_slots = 1`` the
+  ring has S = W + 1 physical slots, frame f goes to slot f mod S, and the
+  window (the newest W frames) never includes slot ``head``, which a
+  staged frame fills before its commit. A frame "evicted" is the one that
+  leaves the window.
 
 The model stores raw words (``uint16`` for bf16 bits, ``uint32`` for fp32
 bits) so that device buffers can be compared with ``array_equal``.
@@ -43,12 +50,17 @@ class RingModel:
     """Expected contents and metadata of the ring after each call."""
 
     def __init__(self, num_layers, num_kv_heads, head_dim, pin_capacity, num_slots,
-                 tokens_per_frame, word_dtype=np.uint16):
+                 tokens_per_frame, word_dtype=np.uint16, spare_slots=0):
         if min(num_layers, num_kv_heads, head_dim, num_slots, tokens_per_frame) <= 0 or pin_capacity < 0:
             raise ValueError("ring dimensions must be positive (pin capacity >= 0)")
+        if spare_slots not in (0, 1):
+            raise ValueError("spare_slots must be 0 or 1")
         self.L, self.Hkv, self.D = num_layers, num_kv_heads, head_dim
         self.P, self.W, self.F = pin_capacity, num_slots, tokens_per_frame
-        self.max_seq_len = self.P + self.W * self.F
+        self.spare = spare_slots
+        self.S = self.W + spare_slots          # physical slots
+        self.staged = False
+        self.max_seq_len = self.P + self.S * self.F
         shape = (self.L, self.max_seq_len, self.Hkv, self.D)
         self.k = np.zeros(shape, dtype=word_dtype)   # zeroed at creation (§5 code)
         self.v = np.zeros(shape, dtype=word_dtype)
@@ -56,7 +68,7 @@ class RingModel:
         self.count = 0         # valid slots, saturates at W
         self.pinned = 0        # pinned prefix tokens
         self.frames_pushed = 0
-        self.slot_frame = [-1] * self.W   # which frame id sits in each slot
+        self.slot_frame = [-1] * self.S   # which frame id sits in each slot
 
     # -- the pinned prefix: written once, at t = 0 ---------------------------
     def pin(self, k_words: np.ndarray, v_words: np.ndarray) -> None:
@@ -72,15 +84,30 @@ class RingModel:
 
     # -- one frame: enqueue newest, evict oldest ------------------------------
     def push(self, k_words: np.ndarray, v_words: np.ndarray) -> int:
-        """Overwrite slot ``head``; return the evicted frame id or -1."""
-        slot = self.head
-        lo = self.P + slot * self.F
+        """Overwrite slot ``head``; return the id of the frame that left the window, or -1."""
+        if self.staged:
+            raise RuntimeError("a staged frame is pending")
+        self.stage(k_words, v_words)
+        return self.commit()
+
+    def stage(self, k_words: np.ndarray, v_words: np.ndarray) -> None:
+        """Write the next frame into slot ``head`` without changing the window."""
+        if self.staged:
+            raise RuntimeError("a staged frame is pending")
+        lo = self.P + self.head * self.F
         self.k[:, lo:lo + self.F] = k_words
         self.v[:, lo:lo + self.F] = v_words
-        evicted = self.slot_frame[slot]
-        self.slot_frame[slot] = self.frames_pushed
+        self.staged = True
+
+    def commit(self) -> int:
+        """The staged frame becomes the newest of the window; return the frame that left it, or -1."""
+        if not self.staged:
+            raise RuntimeError("nothing staged")
+        self.staged = False
+        evicted = self.frames_pushed - self.W if self.frames_pushed >= self.W else -1
+        self.slot_frame[self.head] = self.frames_pushed
         self.frames_pushed += 1
-        self.head = (self.head + 1) % self.W
+        self.head = self.frames_pushed % self.S
         self.count = min(self.count + 1, self.W)
         return evicted
 
@@ -90,7 +117,7 @@ class RingModel:
         return [f for f in range(max(0, self.frames_pushed - self.W), self.frames_pushed)]
 
     def slot_of(self, frame_id: int) -> int:
-        return frame_id % self.W
+        return frame_id % self.S
 
     def state(self) -> dict:
         return {"head": self.head, "count": self.count, "pinned": self.pinned,
@@ -98,8 +125,10 @@ class RingModel:
 
     # -- capsules: snapshot / restore (fork and rollback are restores) --------
     def valid_tokens(self) -> list[int]:
-        """Token indices of the valid region of a layer, in capsule order."""
-        return list(range(self.pinned)) + list(range(self.P, self.P + self.count * self.F))
+        """Token indices of the valid region of a layer, in capsule order: the
+        pinned tokens, then the window's slots in physical order."""
+        slots = sorted(self.slot_of(f) for f in self.window_frames())
+        return list(range(self.pinned)) + [self.P + s * self.F + t for s in slots for t in range(self.F)]
 
     def capsule(self) -> dict:
         """The valid region, compact, plus the metadata."""
@@ -109,14 +138,16 @@ class RingModel:
     def restore(self, cap: dict) -> None:
         st = cap["state"]
         fp, count, head, pinned = st["frames_pushed"], st["count"], st["head"], st["pinned"]
-        if not (0 <= pinned <= self.P and fp >= 0 and count == min(fp, self.W) and head == fp % self.W):
+        if self.staged:
+            raise RuntimeError("a staged frame is pending")
+        if not (0 <= pinned <= self.P and fp >= 0 and count == min(fp, self.W) and head == fp % self.S):
             raise ValueError(f"state {st} is not reachable by this ring")
         self.pinned, self.count, self.head, self.frames_pushed = pinned, count, head, fp
         idx = self.valid_tokens()
         self.k[:, idx] = cap["k"]
         self.v[:, idx] = cap["v"]
-        # slot s holds the latest frame f < frames_pushed with f = s (mod W)
-        self.slot_frame = [-1] * self.W
-        for f in range(max(0, fp - self.W), fp):
-            self.slot_frame[f % self.W] = f
+        # slot s holds the latest frame f < frames_pushed with f = s (mod S)
+        self.slot_frame = [-1] * self.S
+        for f in range(max(0, fp - self.S), fp):
+            self.slot_frame[f % self.S] = f
 

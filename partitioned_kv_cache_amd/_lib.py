@@ -36,6 +36,7 @@ EXPORTS = (
     "pattn_decode", "ada_gamma_workspace_bytes", "ada_gamma", "ada_rmsnorm_workspace_bytes", "ada_rmsnorm",
     "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
     "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
+    "rb_stage_frame", "rb_commit_frame",
 )
 
 
@@ -49,7 +50,7 @@ class PattnError(RuntimeError):
 class RbConfig(C.Structure):
     _fields_ = [("num_layers", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("pin_capacity", C.c_int32), ("num_slots", C.c_int32), ("tokens_per_frame", C.c_int32),
-                ("dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("spare_slots", C.c_int32)]
 
 
 class RbState(C.Structure):
@@ -95,6 +96,8 @@ _sig("rb_destroy", _i32, _vp)
 _sig("rb_pin_prefix", _i32, _vp, _vp, _vp, _i32, _vp)
 _sig("rb_push_frame", _i32, _vp, _vp, _vp, _vp, C.POINTER(C.c_int64))
 _sig("rb_get_state", _i32, _vp, C.POINTER(RbState))
+_sig("rb_stage_frame", _i32, _vp, _vp, _vp, _vp)
+_sig("rb_commit_frame", _i32, _vp, _vp, C.POINTER(C.c_int64))
 _sig("rb_capsule_bytes", _sz, _vp)
 _sig("rb_snapshot", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
 _sig("rb_restore", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
@@ -167,6 +170,16 @@ class Ring:
         _check(_lib.rb_push_frame(self.handle, ptr(k), ptr(v), _stream(stream), C.byref(ev)), "rb_push_frame")
         return ev.value
 
+    def stage_frame(self, k, v, stream=None):
+        """Copy the next frame into the spare slot on the producer's stream (rb_stage_frame)."""
+        _check(_lib.rb_stage_frame(self.handle, ptr(k), ptr(v), _stream(stream)), "rb_stage_frame")
+
+    def commit_frame(self, stream=None) -> int:
+        """Make the staged frame the newest of the window for work enqueued on `stream` (rb_commit_frame)."""
+        ev = C.c_int64(0)
+        _check(_lib.rb_commit_frame(self.handle, _stream(stream), C.byref(ev)), "rb_commit_frame")
+        return ev.value
+
     def state(self) -> dict:
         s = RbState()
         _check(_lib.rb_get_state(self.handle, C.byref(s)), "rb_get_state")
@@ -188,8 +201,9 @@ class Ring:
         _check(_lib.rb_restore(self.handle, ptr(capsule), nb, C.byref(s), _stream(stream)), "rb_restore")
 
 
-def rb_config(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype) -> RbConfig:
-    return RbConfig(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype)
+def rb_config(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype,
+              spare_slots=0) -> RbConfig:
+    return RbConfig(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, tokens_per_frame, dtype, spare_slots)
 
 
 # ------------------------------------------------------------ attention ------

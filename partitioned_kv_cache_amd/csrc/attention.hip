@@ -384,6 +384,7 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     const uint16_t* dk = static_cast<const uint16_t*>(src.dyn_k) + lb * src.dyn_layer + g * D;
     const uint16_t* dv = static_cast<const uint16_t*>(src.dyn_v) + lb * src.dyn_layer + g * D;
     const int n_cached = src.pinned + src.n_slide, pinned = src.pinned, gap = src.pin_cap - src.pinned;
+    const int skip_at = pinned + src.skip_at, skip_len = src.skip_len;   // in context-key units
 
     // Direct-to-LDS loads: one 1 KB load = 16 keys x 64 B of one plane, lane
     // -> (key, 16-byte chunk). Wave w loads blocks w, w + 8, ... of a tile;
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
         if (DPW * MFMA_WAVES > NBLK && wave >= NBLK) return;         // fewer blocks than waves
         const int j = min(k_begin + t * KT + key_in_tile, k_end - 1);  // ragged tail: a valid key, masked later
         const bool dyn = j >= n_cached;
-        const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap);
+        const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap + (j >= skip_at ? skip_len : 0));
         const int off = tok * stride + (wave >> 1) * 32;
         const uint16_t* kp = (dyn ? dk : rk) + off + kchunk;
         const uint16_t* vp = (dyn ? dv : rv) + off + (dma_pos << 3);
@@ -711,6 +712,8 @@ static KvSource source_for(const Ring* r, int layer_begin, const void* k_dyn, co
     s.pinned = r->pinned;
     s.pin_cap = r->cfg.pin_capacity;
     s.n_slide = r->count * r->cfg.tokens_per_frame;
+    s.skip_at = r->skip_at();
+    s.skip_len = r->cfg.spare_slots ? r->cfg.tokens_per_frame : 0;
     s.n_dyn = n_dyn;
     s.hkv = r->cfg.num_kv_heads;
     s.d = r->cfg.head_dim;

@@ -41,16 +41,27 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ------------------------------------------------------------- ring handle --
 struct Ring {
     rb_config cfg;
-    void* k;              // device [L][P + W*F][Hkv][D]
+    void* k;              // device [L][P + S*F][Hkv][D], S = W + spare_slots physical slots
     void* v;
-    int32_t head = 0;
-    int32_t count = 0;
+    int32_t head = 0;     // physical slot the next frame goes to: frames_pushed mod S
+    int32_t count = 0;    // frames in the window, min(frames_pushed, W)
     int32_t pinned = 0;
     int64_t frames_pushed = 0;
+    // asynchronous pushes (spare_slots = 1): a frame staged into slot `head`
+    // by one stream and committed on another, fenced by two events
+    bool staged = false;
+    bool free_recorded = false;
+    hipEvent_t ev_staged = nullptr;   // the staging copy is done
+    hipEvent_t ev_free = nullptr;     // every step that could read the freed slot is done
     int64_t elem_bytes() const { return cfg.dtype == PA_F32 ? 4 : 2; }
-    int64_t seq_len() const { return (int64_t)cfg.pin_capacity + (int64_t)cfg.num_slots * cfg.tokens_per_frame; }
+    int32_t phys_slots() const { return cfg.num_slots + cfg.spare_slots; }
+    int64_t seq_len() const { return (int64_t)cfg.pin_capacity + (int64_t)phys_slots() * cfg.tokens_per_frame; }
     int64_t layer_elems() const { return seq_len() * cfg.num_kv_heads * cfg.head_dim; }
     int32_t cached_tokens() const { return pinned + count * cfg.tokens_per_frame; }
+    // The window's slots in physical order skip slot `head` (the spare, which
+    // may be being written); with no spare the window is slots [0, count).
+    // Window token u (of count * F) lives at slide token u + (u >= skip_at ? F : 0).
+    int32_t skip_at() const { return cfg.spare_slots ? head * cfg.tokens_per_frame : count * cfg.tokens_per_frame; }
 };
 
 // ------------------------------------------------------------ device types --
@@ -71,10 +82,12 @@ __device__ __forceinline__ bool finite_f(float x) { return (__float_as_uint(x) &
 // Where the keys of one (layer, kv-head) live. Logical key j of the context
 // [pin | window | dyn] maps to
 //   j <  pinned                     ring token j
-//   j <  pinned + n_slide           ring token P + (j - pinned)   (physical slot order)
+//   j <  pinned + n_slide           ring token P + u (+ F if u >= skip_at), u = j - pinned
 //   otherwise                       dyn token j - pinned - n_slide
-// n_slide = count * F: the valid slots are always the leading `count` slots,
-// because slot f mod W is written by frame f and slots fill from 0.
+// n_slide = count * F. Frame f sits in slot f mod S and slots fill from 0,
+// so the window is the leading `count` slots, except that a ring with a
+// spare slot (S = W + 1) leaves out slot `head`, the one a push may be
+// filling (physical slot order; softmax does not depend on key order).
 struct KvSource {
     const void* ring_k;        // element 0 of layer `layer_begin`
     const void* ring_v;
@@ -83,6 +96,7 @@ struct KvSource {
     const void* dyn_v;
     long long dyn_layer;       // elements per dyn layer (N * Hkv * D)
     int pinned, pin_cap, n_slide, n_dyn;
+    int skip_at, skip_len;     // window token u >= skip_at sits skip_len tokens further on
     int hkv, d;
 
     __device__ __forceinline__ int total() const { return pinned + n_slide + n_dyn; }
@@ -90,7 +104,8 @@ struct KvSource {
     // element offset of (call-layer lb, kv head g, logical key j) and which buffer
     __device__ __forceinline__ long long offset(int lb, int g, int j, bool& is_dyn) const {
         if (j < pinned + n_slide) {
-            int tok = j < pinned ? j : pin_cap + (j - pinned);
+            const int u = j - pinned;
+            int tok = j < pinned ? j : pin_cap + u + (u >= skip_at ? skip_len : 0);
             is_dyn = false;
             return (long long)lb * ring_layer + ((long long)tok * hkv + g) * d;
         }

@@ -47,7 +47,9 @@ extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, r
                  PA_ESHAPE, "rb_create: sizes must be positive (pin capacity >= 0)");
     PA_CHECK_ARG(cfg->head_dim == 32 || cfg->head_dim == 64 || cfg->head_dim == 128 || cfg->head_dim == 256,
                  PA_ESHAPE, "rb_create: head_dim %d must be 32, 64, 128 or 256", cfg->head_dim);
-    int64_t seq = (int64_t)cfg->pin_capacity + (int64_t)cfg->num_slots * cfg->tokens_per_frame;
+    PA_CHECK_ARG(cfg->spare_slots == 0 || cfg->spare_slots == 1, PA_EINVAL, "rb_create: spare_slots %d must be 0 or 1",
+                 cfg->spare_slots);
+    int64_t seq = (int64_t)cfg->pin_capacity + (int64_t)(cfg->num_slots + cfg->spare_slots) * cfg->tokens_per_frame;
     PA_CHECK_ARG(seq * cfg->num_kv_heads * cfg->head_dim < (1LL << 31), PA_ESHAPE,
                  "rb_create: (P + W*F) * Hkv * D must stay below 2^31 elements per layer");
     Ring* r = new (std::nothrow) Ring();
@@ -61,7 +63,12 @@ extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, r
 
 extern "C" pa_status rb_destroy(rb_ring* ring) {
     pa::clear_error();
-    delete reinterpret_cast<Ring*>(ring);
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    if (r) {
+        if (r->ev_staged) (void)hipEventDestroy(r->ev_staged);
+        if (r->ev_free) (void)hipEventDestroy(r->ev_free);
+    }
+    delete r;
     return PA_OK;
 }
 
@@ -91,20 +98,68 @@ extern "C" pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, 
     return PA_OK;
 }
 
+// Copy a frame into slot `head` of every layer.
+static pa_status write_head_slot(Ring* r, const void* k, const void* v, hipStream_t s) {
+    const int64_t tok0 = (int64_t)r->cfg.pin_capacity + (int64_t)r->head * r->cfg.tokens_per_frame;
+    pa_status st = copy_tokens(r, r->k, k, tok0, r->cfg.tokens_per_frame, s);
+    if (st != PA_OK) return st;
+    return copy_tokens(r, r->v, v, tok0, r->cfg.tokens_per_frame, s);
+}
+
+// The frame in slot `head` joins the window; the oldest leaves it.
+static int64_t advance(Ring* r) {
+    const int W = r->cfg.num_slots;
+    const int64_t ev = r->frames_pushed >= W ? r->frames_pushed - W : -1;
+    r->frames_pushed += 1;
+    r->head = (int32_t)(r->frames_pushed % r->phys_slots());
+    r->count = r->count < W ? r->count + 1 : W;
+    return ev;
+}
+
 extern "C" pa_status rb_push_frame(rb_ring* ring, const void* k, const void* v, void* stream, int64_t* evicted) {
     pa::clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_push_frame: null argument");
+    PA_CHECK_ARG(!r->staged, PA_ESTATE, "rb_push_frame: a staged frame is pending; commit it first");
+    pa_status st = write_head_slot(r, k, v, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+    const int64_t ev = advance(r);
+    if (evicted) *evicted = ev;
+    return PA_OK;
+}
+
+extern "C" pa_status rb_stage_frame(rb_ring* ring, const void* k, const void* v, void* stream) {
+    pa::clear_error();
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_stage_frame: null argument");
+    PA_CHECK_ARG(r->cfg.spare_slots == 1, PA_ESTATE, "rb_stage_frame: the ring has no spare slot");
+    PA_CHECK_ARG(!r->staged, PA_ESTATE, "rb_stage_frame: a staged frame is already pending");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t tok0 = (int64_t)r->cfg.pin_capacity + (int64_t)r->head * r->cfg.tokens_per_frame;
-    pa_status st = copy_tokens(r, r->k, k, tok0, r->cfg.tokens_per_frame, s);
+    if (!r->ev_staged) {
+        PA_HIP(hipEventCreateWithFlags(&r->ev_staged, hipEventDisableTiming));
+        PA_HIP(hipEventCreateWithFlags(&r->ev_free, hipEventDisableTiming));
+    }
+    if (r->free_recorded) PA_HIP(hipStreamWaitEvent(s, r->ev_free, 0));
+    pa_status st = write_head_slot(r, k, v, s);
     if (st != PA_OK) return st;
-    st = copy_tokens(r, r->v, v, tok0, r->cfg.tokens_per_frame, s);
-    if (st != PA_OK) return st;
-    const int64_t ev = r->frames_pushed >= r->cfg.num_slots ? r->frames_pushed - r->cfg.num_slots : -1;
-    r->frames_pushed += 1;
-    r->head = (r->head + 1) % r->cfg.num_slots;
-    r->count = r->count < r->cfg.num_slots ? r->count + 1 : r->cfg.num_slots;
+    PA_HIP(hipEventRecord(r->ev_staged, s));
+    r->staged = true;
+    return PA_OK;
+}
+
+extern "C" pa_status rb_commit_frame(rb_ring* ring, void* stream, int64_t* evicted) {
+    pa::clear_error();
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    PA_CHECK_ARG(r, PA_EINVAL, "rb_commit_frame: null argument");
+    PA_CHECK_ARG(r->staged, PA_ESTATE, "rb_commit_frame: no staged frame");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Everything enqueued on the consumer so far may read the slot this
+    // commit frees (the oldest of the window): the next stage waits for it.
+    PA_HIP(hipEventRecord(r->ev_free, s));
+    PA_HIP(hipStreamWaitEvent(s, r->ev_staged, 0));
+    r->free_recorded = true;
+    r->staged = false;
+    const int64_t ev = advance(r);
     if (evicted) *evicted = ev;
     return PA_OK;
 }
@@ -137,18 +192,25 @@ static size_t capsule_bytes_of(const Ring* r, int64_t ctok) {
     return (size_t)(2 * r->cfg.num_layers * ctok * r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes());
 }
 
-// Copy the valid region between the ring (layer pitch P + W*F tokens) and a
-// capsule (layer pitch ctok tokens), one 2-D copy per region and tensor.
-static pa_status capsule_copy(Ring* r, char* cap, int32_t pinned, int64_t count, bool to_capsule, hipStream_t s) {
+// Copy the valid region between the ring (layer pitch P + S*F tokens) and a
+// capsule (layer pitch ctok tokens), one 2-D copy per run and tensor: the
+// pinned tokens, then the window's slots in physical order, which with a
+// spare slot form up to two runs around slot `head`.
+static pa_status capsule_copy(Ring* r, char* cap, int32_t pinned, int64_t count, int32_t head, bool to_capsule,
+                              hipStream_t s) {
+    const int64_t F = r->cfg.tokens_per_frame, P = r->cfg.pin_capacity;
     const int64_t tok = (int64_t)r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes();
-    const int64_t ctok = pinned + count * r->cfg.tokens_per_frame;
+    const int64_t ctok = pinned + count * F;
     const size_t rpitch = (size_t)(r->seq_len() * tok), cpitch = (size_t)(ctok * tok);
     const size_t layers = (size_t)r->cfg.num_layers;
+    const int64_t n_win = count * F;
+    const int64_t skip = r->cfg.spare_slots ? (int64_t)head * F : n_win;   // window tokens before the spare
+    const int64_t run1 = skip < n_win ? skip : n_win;
     for (int t = 0; t < 2; ++t) {
         char* ring = static_cast<char*>(t == 0 ? r->k : r->v);
         char* c = cap + (size_t)t * layers * cpitch;
-        struct { int64_t ring_tok, cap_tok, n; } reg[2] = {
-            {0, 0, pinned}, {r->cfg.pin_capacity, pinned, count * r->cfg.tokens_per_frame}};
+        struct { int64_t ring_tok, cap_tok, n; } reg[3] = {
+            {0, 0, pinned}, {P, pinned, run1}, {P + run1 + F, pinned + run1, n_win - run1}};
         for (const auto& g : reg) {
             if (g.n == 0) continue;
             char* rp = ring + g.ring_tok * tok;
@@ -177,7 +239,8 @@ extern "C" pa_status rb_snapshot(const rb_ring* ring, void* capsule, size_t caps
     const size_t need = capsule_bytes_of(r, capsule_tokens(r));
     PA_CHECK_ARG(capsule || need == 0, PA_EINVAL, "rb_snapshot: null capsule");
     PA_CHECK_ARG(capsule_bytes >= need, PA_ERANGE, "rb_snapshot: capsule %zu bytes < %zu needed", capsule_bytes, need);
-    pa_status st = capsule_copy(r, static_cast<char*>(capsule), r->pinned, r->count, true, static_cast<hipStream_t>(stream));
+    pa_status st = capsule_copy(r, static_cast<char*>(capsule), r->pinned, r->count, r->head, true,
+                                static_cast<hipStream_t>(stream));
     if (st != PA_OK) return st;
     return rb_get_state(ring, state);
 }
@@ -187,18 +250,19 @@ extern "C" pa_status rb_restore(rb_ring* ring, const void* capsule, size_t capsu
     pa::clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r && state, PA_EINVAL, "rb_restore: null argument");
+    PA_CHECK_ARG(!r->staged, PA_ESTATE, "rb_restore: a staged frame is pending; commit it first");
     const int W = r->cfg.num_slots;
     const int64_t fp = state->frames_pushed;
     PA_CHECK_ARG(state->pinned >= 0 && state->pinned <= r->cfg.pin_capacity, PA_EINVAL,
                  "rb_restore: pinned %d not in [0, %d]", state->pinned, r->cfg.pin_capacity);
-    PA_CHECK_ARG(fp >= 0 && state->count == (fp < W ? fp : W) && state->head == (int32_t)(fp % W), PA_EINVAL,
+    PA_CHECK_ARG(fp >= 0 && state->count == (fp < W ? fp : W) && state->head == (int32_t)(fp % r->phys_slots()), PA_EINVAL,
                  "rb_restore: state (head %d, count %d, frames_pushed %lld) is not one a ring of %d slots reaches",
                  state->head, state->count, (long long)fp, W);
     const size_t need = capsule_bytes_of(r, state->pinned + (int64_t)state->count * r->cfg.tokens_per_frame);
     PA_CHECK_ARG(capsule || need == 0, PA_EINVAL, "rb_restore: null capsule");
     PA_CHECK_ARG(capsule_bytes >= need, PA_ERANGE, "rb_restore: capsule %zu bytes < %zu needed", capsule_bytes, need);
     pa_status st = capsule_copy(r, const_cast<char*>(static_cast<const char*>(capsule)), state->pinned, state->count,
-                                false, static_cast<hipStream_t>(stream));
+                                state->head, false, static_cast<hipStream_t>(stream));
     if (st != PA_OK) return st;
     r->head = state->head;
     r->count = state->count;

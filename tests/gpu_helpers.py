@@ -47,18 +47,19 @@ def max_abs(gpu: np.ndarray, ref: np.ndarray) -> float:
 class Scenario:
     """A ring on the GPU plus the oracle's model of it, fed the same frames."""
 
-    def __init__(self, s: Shape, pin_tokens: int | None = None, frame_fn=None):
+    def __init__(self, s: Shape, pin_tokens: int | None = None, frame_fn=None, spare_slots: int = 0):
         L = lib()
         self.s = s
         self.dt = L.PA_F32 if s.dtype == "f32" else L.PA_BF16
-        shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
+        seq = s.pin_tokens + (s.num_slots + spare_slots) * s.tokens_per_frame
+        shp = (s.num_layers, seq, s.n_kv_heads, s.head_dim)
         self.k_buf = torch.zeros(shp, dtype=tdtype(s.dtype), device="cuda")
         self.v_buf = torch.zeros(shp, dtype=tdtype(s.dtype), device="cuda")
         self.ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
-                                       s.tokens_per_frame, self.dt), self.k_buf, self.v_buf)
+                                       s.tokens_per_frame, self.dt, spare_slots), self.k_buf, self.v_buf)
         word = np.uint32 if s.dtype == "f32" else np.uint16
         self.model = RingModel(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
-                               s.tokens_per_frame, word)
+                               s.tokens_per_frame, word, spare_slots=spare_slots)
         self.frame_fn = frame_fn or (lambda f: synth.frame_kv(s, f))
         self.pin_k = self.pin_v = None
         n_pin = s.pin_tokens if pin_tokens is None else pin_tokens
@@ -76,9 +77,27 @@ class Scenario:
         ev = self.ring.push_frame(dev(k), dev(v))
         ev_model = self.model.push(self._words(k), self._words(v))
         assert ev == ev_model
+        self._enter(f, k, v)
+        return ev
+
+    def _enter(self, f, k, v):
         self.window.append((f, k, v))
         if len(self.window) > self.s.num_slots:
             self.window.pop(0)
+
+    def stage(self, f: int, stream):
+        """Stage frame f on `stream` (device tensors kept alive until the commit)."""
+        k, v = self.frame_fn(f)
+        self._staged = (f, k, v, dev(k), dev(v))
+        self.ring.stage_frame(self._staged[3], self._staged[4], stream)
+        self.model.stage(self._words(k), self._words(v))
+
+    def commit(self, stream) -> int:
+        f, k, v, _, _ = self._staged
+        ev = self.ring.commit_frame(stream)
+        assert ev == self.model.commit()
+        self._enter(f, k, v)
+        self._staged = None
         return ev
 
     def check_bytes(self):

@@ -157,3 +157,23 @@ def test_capsule_validation_without_device():
     assert r.state() == {"head": 0, "count": 0, "pinned": 0, "frames_pushed": 0}   # rejected restores change nothing
     r.close()
 
+
+
+def test_staging_guards_without_device():
+    """rb_stage_frame / rb_commit_frame reject misuse on the host, before any copy."""
+    from partitioned_kv_cache_amd import _lib as L
+    with pytest.raises(L.PattnError) as e:
+        L.Ring(L.rb_config(1, 1, 64, 4, 2, 8, L.PA_F32, spare_slots=2), _fake(1), _fake(2))
+    assert e.value.status == L.PA_EINVAL
+    classic = L.Ring(L.rb_config(1, 1, 64, 4, 2, 8, L.PA_F32), _fake(1), _fake(2))
+    with pytest.raises(L.PattnError) as e:
+        classic.stage_frame(_fake(3), _fake(4), stream=0)
+    assert e.value.status == L.PA_ESTATE and "spare" in str(e.value)
+    spare = L.Ring(L.rb_config(1, 1, 64, 4, 2, 8, L.PA_F32, spare_slots=1), _fake(1), _fake(2))
+    with pytest.raises(L.PattnError) as e:
+        spare.commit_frame(stream=0)
+    assert e.value.status == L.PA_ESTATE
+    # the spare slot adds one frame to the buffers' layout: capsule of an empty ring stays empty
+    assert spare.capsule_bytes() == 0 and spare.state()["head"] == 0
+    classic.close()
+    spare.close()

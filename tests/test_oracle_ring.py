@@ -83,8 +83,8 @@ def _replay(L, H, D, P, W, F, pin_n, n_frames):
 
 def _context(r):
     """Chronological [pin; window] K and V of every layer, read through the slot map."""
-    ks = [r.k[:, :r.pinned]] + [r.k[:, r.P + (g % r.W) * r.F:r.P + (g % r.W + 1) * r.F] for g in r.window_frames()]
-    vs = [r.v[:, :r.pinned]] + [r.v[:, r.P + (g % r.W) * r.F:r.P + (g % r.W + 1) * r.F] for g in r.window_frames()]
+    ks = [r.k[:, :r.pinned]] + [r.k[:, r.P + r.slot_of(g) * r.F:r.P + (r.slot_of(g) + 1) * r.F] for g in r.window_frames()]
+    vs = [r.v[:, :r.pinned]] + [r.v[:, r.P + r.slot_of(g) * r.F:r.P + (r.slot_of(g) + 1) * r.F] for g in r.window_frames()]
     return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
 
 
@@ -143,3 +143,72 @@ def test_restore_rejects_unreachable_states():
                 {"head": 0, "count": 0, "pinned": 5, "frames_pushed": 0}):
         with pytest.raises(ValueError):
             r.restore({"k": cap["k"], "v": cap["v"], "state": bad})
+
+
+# ----------------------------------------------------- spare slot (staging) ----
+# Reflex review, system architecture (Figure 3): a producer pushes frames while
+# the consumer denoises. The safety property of the spare slot: staging the
+# next frame never changes a byte the current window reads, and a commit is
+# exactly a push.
+
+@pytest.mark.parametrize("L,P,W,F", [(1, 4, 3, 2), (2, 0, 1, 3), (3, 5, 4, 1)])
+def test_spare_slot_window_against_deque(L, P, W, F):
+    H, D = 1, 2
+    ring = RingModel(L, H, D, P, W, F, spare_slots=1)
+    assert ring.S == W + 1 and ring.max_seq_len == P + (W + 1) * F
+    fifo = deque(maxlen=W)
+    for f in range(3 * (W + 1) + 2):
+        before = _context(ring)
+        ring.stage(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1))
+        assert ring.window_frames() == list(fifo)                    # staging changes no window
+        for a, b in zip(_context(ring), before):
+            assert np.array_equal(a, b)
+        assert all(ring.slot_of(g) != ring.head for g in fifo)       # the staged slot is outside the window
+        ev = ring.commit()
+        assert ev == (fifo[0] if len(fifo) == W else -1)
+        fifo.append(f)
+        assert ring.window_frames() == list(fifo) and ring.count == len(fifo)
+        assert ring.head == (f + 1) % (W + 1)
+        for g in fifo:
+            lo = P + (g % (W + 1)) * F
+            assert np.array_equal(ring.k[:, lo:lo + F], _frame(L, F, H, D, g, 0))
+
+
+def test_spare_slot_push_equals_stage_commit_and_guards():
+    L, H, D, P, W, F = 2, 1, 2, 3, 2, 2
+    a, b = RingModel(L, H, D, P, W, F, spare_slots=1), RingModel(L, H, D, P, W, F, spare_slots=1)
+    for f in range(7):
+        assert a.push(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1)) == \
+            (b.stage(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1)) or b.commit())
+        assert np.array_equal(a.k, b.k) and a.state() == b.state()
+    b.stage(_frame(L, F, H, D, 9, 0), _frame(L, F, H, D, 9, 1))
+    with pytest.raises(RuntimeError):
+        b.stage(_frame(L, F, H, D, 9, 0), _frame(L, F, H, D, 9, 1))
+    with pytest.raises(RuntimeError):
+        b.push(_frame(L, F, H, D, 9, 0), _frame(L, F, H, D, 9, 1))
+    b.commit()
+    with pytest.raises(RuntimeError):
+        b.commit()
+
+
+@pytest.mark.parametrize("t,more", [(2, 5), (7, 3)])
+def test_spare_slot_capsule_round_trip_equals_replay(t, more):
+    L, H, D, P, W, F = 2, 1, 2, 3, 3, 2
+
+    def replay(n):
+        r = RingModel(L, H, D, P, W, F, spare_slots=1)
+        r.pin(np.full((L, P, H, D), 7, np.uint16), np.full((L, P, H, D), 8, np.uint16))
+        for f in range(n):
+            r.push(_frame(L, F, H, D, f, 0), _frame(L, F, H, D, f, 1))
+        return r
+
+    live = replay(t)
+    cap = live.capsule()
+    assert cap["k"].shape[1] == P + min(t, W) * F
+    for f in range(t, t + more):
+        live.push(_frame(L, F, H, D, f + 50, 0), _frame(L, F, H, D, f + 50, 1))
+    live.restore(cap)
+    ref = replay(t)
+    assert live.state() == ref.state()
+    for a, b in zip(_context(live), _context(ref)):
+        assert np.array_equal(a, b)
