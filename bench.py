@@ -335,11 +335,13 @@ def bench_stack(args, torch, L, configs, synth):
     }
 
 
-def bench_shared_kv(args, torch, L, configs, synth):
-    """Shared-KV multi-reader frame: the long-history cache read by the action
-    suffix (10 denoising steps, 18 layers) and by 16 decode streams (one query
-    token each, one decode step per frame) with private tails of up to 30
-    appended tokens."""
+def bench_shared_kv(args, torch, L, configs, synth, budgets=(1, 5, 10), n_frames=20):
+    """Shared-KV multi-reader frames: the long-history cache read by the action
+    suffix (10 denoising steps, 18 layers) and by 16 decode streams, one query
+    token each, advancing k decode steps per frame (k swept over `budgets`).
+    Private tails start staggered at 2j mod 30 tokens, grow by one token per
+    decode step, and a stream whose tail reaches 30 tokens retires: its next
+    token starts a new request."""
     import numpy as np
     s = configs.SHARED_KV
     dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
@@ -359,43 +361,51 @@ def bench_shared_kv(args, torch, L, configs, synth):
     a_ws = torch.empty(a_wsb, dtype=torch.uint8, device="cuda")
     a_out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
     G, cap = s.n_streams, s.tail_capacity
-    d_args = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_BF16)
+    d_args = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_BF16, 0, 1)
     d_wsb = L.pattn_decode_workspace_bytes(ring, d_args)
     d_ws = torch.empty(d_wsb, dtype=torch.uint8, device="cuda")
     tail_k = torch.zeros((s.num_layers, G, cap, s.n_kv_heads, s.head_dim), dtype=torch.int16, device="cuda")
     tail_v = torch.zeros_like(tail_k)
-    tail_len = dev(np.array([(2 * j) % (cap - 10) for j in range(G)], dtype=np.int32))
-    dq = dev(synth.decode_q(s, 0, 0))
-    dk, dv = (dev(a) for a in synth.decode_kv(s, 0, 0))
+    dq = [dev(synth.decode_q(s, 0, t)) for t in range(2)]
+    dkv = [tuple(dev(a) for a in synth.decode_kv(s, 0, t)) for t in range(2)]
     d_out = torch.empty((s.num_layers, G, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
-    n_frames = 10           # tails stay below capacity: lengths start at most cap - 11
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    def frame(i, ev=None):
+    def frame(i, k_dec, ev=None):
         ring.push_frame(*pool[i % 4])
         for k in range(s.steps_per_frame):
             L.pattn_step(ring, a_args, *steps_in[k], a_out, a_ws, a_wsb)
         if ev is not None:
             ev[0].record()
-        L.pattn_append_private(ring, d_args, tail_k, tail_v, tail_len, dk, dv)
-        L.pattn_decode(ring, d_args, dq, tail_k, tail_v, tail_len, d_out, d_ws, d_wsb)
+        for t in range(k_dec):
+            L.pattn_append_private(ring, d_args, tail_k, tail_v, tail_len, *dkv[t % 2], ovf)
+            L.pattn_decode(ring, d_args, dq[t % 2], tail_k, tail_v, tail_len, d_out, d_ws, d_wsb)
         if ev is not None:
             ev[1].record()
 
-    frame(0)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_frames)]
-    t0 = time.perf_counter()
-    for i in range(n_frames):
-        frame(1 + i, evs[i])
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    dec_us = sum(a.elapsed_time(b) for a, b in evs) / n_frames * 1e3
+    sweep = {}
+    for k_dec in budgets:
+        tail_len = dev(np.array([(2 * j) % cap for j in range(G)], dtype=np.int32))
+        frame(0, k_dec)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_frames)]
+        t0 = time.perf_counter()
+        for i in range(n_frames):
+            frame(1 + i, k_dec, evs[i])
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        dec_us = sum(a.elapsed_time(b) for a, b in evs) / n_frames * 1e3 / k_dec
+        assert int(ovf.item()) == 0, "a private tail overflowed with retiring on"
+        sweep[k_dec] = {"frames_per_s": n_frames / el, "decode_tokens_per_s": G * k_dec * n_frames / el,
+                        "decode_step_us": dec_us, "frames_timed": n_frames}
     ring.close()
-    return {"workload": "shared_kv_multitask", "frames_per_s": n_frames / el,
-            "decode_tokens_per_s": G * n_frames / el, "decode_step_us": dec_us,
-            "frames_timed": n_frames,
+    k1 = sweep[budgets[0]]
+    return {"workload": "shared_kv_multitask", "frames_per_s": k1["frames_per_s"],
+            "decode_tokens_per_s": k1["decode_tokens_per_s"], "decode_step_us": k1["decode_step_us"],
+            "frames_timed": n_frames, "decode_budget_sweep": {f"k={k}": v for k, v in sweep.items()},
             "config": {"layers": 18, "cache": "256 + 8x768", "action_suffix": 51, "steps_per_frame": 10,
-                       "decode_streams": G, "tail_capacity": cap, "decode_steps_per_frame": 1}}
+                       "decode_streams": G, "tail_capacity": cap, "retire_at": cap,
+                       "decode_steps_per_frame": budgets[0]}}
 
 
 def cpu_baseline(budget_s):

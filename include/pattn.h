@@ -218,12 +218,17 @@ typedef struct {
     float   scale;
     int32_t out_dtype;
     int32_t num_splits;        /* 0 = library's choice */
+    int32_t retire_full;       /* 1: a full tail starts a new request at the next append (see below) */
 } pattn_decode_args;
 
 /* Append one token per stream, k_new/v_new [Lb][G][Hkv][D], at index
  * tail_len[g] of every layer, then tail_len[g] += 1 (on the device).
- * A stream whose tail is full is left unchanged and its bit is set in
- * *overflow_mask (device uint32, nullable; bit g%32). Retire a stream by
+ * A request ends at a maximum length (OxyGen review, method details): with
+ * args->retire_full = 1 a stream whose tail holds tail_capacity tokens has
+ * finished its request, and the next request starts in its place: the new
+ * token goes to index 0 and tail_len becomes 1. With retire_full = 0 a full
+ * stream is left unchanged and its bit is set in *overflow_mask (device
+ * uint32, nullable; bit g%32). A stream can also be retired at any time by
  * setting its tail_len to 0. tail_k, tail_v ([Lb][G][cap][Hkv][D]), k_new and
  * v_new must be 16-byte aligned (PA_EINVAL otherwise). */
 pa_status pattn_append_private(const rb_ring* ring, const pattn_decode_args* args,

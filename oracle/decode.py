@@ -14,7 +14,10 @@ Readings taken:
   appended tokens live in a private tail that no other reader sees, and the
   action suffix never sees any private tail;
 * a decode step first appends the stream's new token to its tail, then the
-  stream's single query token attends over [pin; window; tail].
+  stream's single query token attends over [pin; window; tail];
+* a request that reached the maximum length N (a full tail) has ended; when
+  retiring is on, the stream's next append starts a new request, whose tail
+  holds only that token.
 """
 
 from __future__ import annotations
@@ -34,9 +37,13 @@ class PrivateTails:
         self.length = np.zeros(n_streams, np.int64)
         self.capacity = capacity
 
-    def append(self, stream, k_tok, v_tok):
-        """Append one token ([Hkv][D]) to a stream's tail."""
+    def append(self, stream, k_tok, v_tok, retire_full=False):
+        """Append one token ([Hkv][D]) to a stream's tail; with retire_full a
+        full tail (a finished request) restarts with this token."""
         n = int(self.length[stream])
+        if n >= self.capacity and retire_full:
+            self.reset(stream)
+            n = 0
         if n >= self.capacity:
             raise ValueError("private tail full")
         self.k[stream, n] = k_tok

@@ -66,7 +66,7 @@ class PattnArgs(C.Structure):
 class PattnDecodeArgs(C.Structure):
     _fields_ = [("layer_begin", C.c_int32), ("num_layers", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_streams", C.c_int32), ("tail_capacity", C.c_int32), ("scale", C.c_float),
-                ("out_dtype", C.c_int32), ("num_splits", C.c_int32)]
+                ("out_dtype", C.c_int32), ("num_splits", C.c_int32), ("retire_full", C.c_int32)]
 
 
 class AdaMlp(C.Structure):
@@ -229,8 +229,9 @@ def pattn_step_timed(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, workspac
 
 
 def decode_args(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype=PA_F32,
-                num_splits=0) -> PattnDecodeArgs:
-    return PattnDecodeArgs(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype, num_splits)
+                num_splits=0, retire_full=0) -> PattnDecodeArgs:
+    return PattnDecodeArgs(layer_begin, num_layers, n_q_heads, n_streams, tail_capacity, scale, out_dtype, num_splits,
+                           retire_full)
 
 
 def pattn_append_private(ring: Ring, args: PattnDecodeArgs, tail_k, tail_v, tail_len, k_new, v_new,

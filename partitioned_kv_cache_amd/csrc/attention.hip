@@ -585,9 +585,10 @@ constexpr int APPEND_BATCH = 8;
 __global__ __launch_bounds__(256) void append_tail(uint4* __restrict__ tail_k, uint4* __restrict__ tail_v,
                                                    int32_t* tail_len, const uint4* __restrict__ k_new,
                                                    const uint4* __restrict__ v_new, int n_layers, int n_streams,
-                                                   int cap, int tok_chunks, uint32_t* overflow) {
+                                                   int cap, int tok_chunks, int retire_full, uint32_t* overflow) {
     const int strm = blockIdx.x;
-    const int n = tail_len[strm];
+    int n = tail_len[strm];
+    if (retire_full && n >= cap) n = 0;                 // the request ended: a new one starts here
     const bool ok = n >= 0 && n < cap;
     if (ok) {
         const int total = n_layers * tok_chunks;       // (layer, chunk) items of this stream
@@ -867,7 +868,8 @@ extern "C" pa_status pattn_append_private(const rb_ring* ring, const pattn_decod
     const int tok_chunks = (int)((size_t)r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes() / 16);
     append_tail<<<a->n_streams, 256, 0, s>>>(static_cast<uint4*>(tail_k), static_cast<uint4*>(tail_v), tail_len,
                                              static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
-                                             a->num_layers, a->n_streams, a->tail_capacity, tok_chunks, overflow);
+                                             a->num_layers, a->n_streams, a->tail_capacity, tok_chunks,
+                                             a->retire_full, overflow);
     PA_LAUNCHED();
     return PA_OK;
 }

@@ -210,6 +210,44 @@ def test_decode_empty_tail_is_shared_context_only():
         assert rel_err(got[l], full_attention(synth.widen(q[l]), ck, cv, s.scale)) <= BAR
 
 
+def test_decode_retire_full_restarts_the_request():
+    """With retire_full, a stream whose tail is full starts a new request at the
+    next append (tail of one token); other streams append as usual."""
+    L = lib()
+    s = configs.SHARED_KV.with_(name="dec_retire", cfg_id=52, num_layers=3, tokens_per_frame=64, n_streams=4,
+                                tail_capacity=5)
+    _banner("decode retire_full")
+    sc = Scenario(s)
+    for f in range(4):
+        sc.push(f)
+    G, cap, hkv, D = s.n_streams, s.tail_capacity, s.n_kv_heads, s.head_dim
+    lens0 = np.array([cap, 2, cap, 0], dtype=np.int32)
+    tk = synth.normal((s.num_layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILK, 3)
+    tv = synth.normal((s.num_layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILV, 3)
+    tk_d, tv_d, len_d = dev(tk), dev(tv), dev(lens0)
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_F32, 0, 1)
+    kn, vn = synth.decode_kv(s, 4, 0)
+    L.pattn_append_private(sc.ring, a, tk_d, tv_d, len_d, dev(kn), dev(vn), ovf)
+    q = synth.decode_q(s, 4, 0)
+    wsb = L.pattn_decode_workspace_bytes(sc.ring, a)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.num_layers, G, s.n_q_heads, D), dtype=torch.float32, device="cuda")
+    L.pattn_decode(sc.ring, a, dev(q), tk_d, tv_d, len_d, out, ws, wsb)
+    torch.cuda.synchronize()
+    assert list(host(len_d)) == [1, 3, 1, 1] and int(host(ovf)[0]) == 0
+    got = host(out).astype(np.float64)
+    for l in range(s.num_layers):
+        tails = decode.PrivateTails(G, cap, hkv, D)
+        for j in range(G):
+            for t in range(int(lens0[j])):
+                tails.append(j, synth.widen(tk[l, j, t]), synth.widen(tv[l, j, t]))
+            tails.append(j, synth.widen(kn[l, j]), synth.widen(vn[l, j]), retire_full=True)
+        ck, cv = sc.cached_context(l)
+        ref = decode.decode_attention(synth.widen(q[l]), ck, cv, tails, s.scale)
+        assert rel_err(got[l], ref) <= BAR
+
+
 # ------------------------------------------------------------ denoise step ---
 
 class StackRig:

@@ -111,3 +111,24 @@ def test_decode_tail_capacity_and_retire():
         tails.append(0, np.zeros((1, 2)), np.zeros((1, 2)))
     tails.reset(0)
     assert tails.length[0] == 0
+
+
+def test_retire_full_starts_a_new_request():
+    """OxyGen review, method details: a request ends at its maximum length. With
+    retiring on, a full stream's next token starts a new request: its query sees
+    the shared context plus that one token only (checked against the plain
+    definition, full attention over [shared; new token])."""
+    rng = np.random.default_rng(7)
+    shared_k, shared_v = rng.standard_normal((5, 1, 4)), rng.standard_normal((5, 1, 4))
+    tails = decode.PrivateTails(2, 3, 1, 4)
+    for _ in range(3):
+        tails.append(0, rng.standard_normal((1, 4)), rng.standard_normal((1, 4)))
+    tails.append(1, rng.standard_normal((1, 4)), rng.standard_normal((1, 4)))
+    kn, vn = rng.standard_normal((1, 4)), rng.standard_normal((1, 4))
+    tails.append(0, kn, vn, retire_full=True)          # full: a new request
+    tails.append(1, kn, vn, retire_full=True)          # not full: an ordinary append
+    assert list(tails.length) == [1, 2]
+    q = rng.standard_normal((2, 2, 4))
+    got = decode.decode_attention(q, shared_k, shared_v, tails, 0.5)
+    want0 = full_attention(q[0:1], np.concatenate([shared_k, kn[None]]), np.concatenate([shared_v, vn[None]]), 0.5)[0]
+    assert np.allclose(got[0], want0, rtol=1e-12, atol=1e-12)
