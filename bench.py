@@ -511,6 +511,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-KV multi-reader frame")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run only the cold-MALL headline step (for profiler passes)")
     ap.add_argument("--cold-rings", type=int, default=3,
                     help="independent rings served round-robin for the cold-MALL headline (3 x 118 MB > 256 MB)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -529,21 +531,26 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
         return
-    warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
-    log(f"long history, warm MALL: {warm['steps_per_s']:.1f} steps/s, partial kernel {warm['partial_us']:.1f} us")
+    if args.headline_only:
+        args.no_stack = args.no_shared = True
+        args.cpu_budget = 0
     lh = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings)
     log(f"long history, cold MALL ({args.cold_rings} rings): {lh['steps_per_s']:.1f} steps/s, partial kernel "
         f"{lh['partial_us']:.1f} us ({lh['partial_tflops']:.0f} TFLOP/s, {lh['partial_gbs']:.0f} GB/s)")
-    small = [bench_small(args, torch, L, c) for c in (configs.TINY, configs.PI05_1L)]
-    for sm in small:
-        log(f"{sm['workload']}: {sm['us_per_call']:.1f} us per call eager, {sm['us_per_call_graph']:.1f} in a graph")
+    warm = small = async_push = None
+    if not args.headline_only:
+        warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
+        log(f"long history, warm MALL: {warm['steps_per_s']:.1f} steps/s, partial kernel {warm['partial_us']:.1f} us")
+        small = [bench_small(args, torch, L, c) for c in (configs.TINY, configs.PI05_1L)]
+        for sm in small:
+            log(f"{sm['workload']}: {sm['us_per_call']:.1f} us per call eager, {sm['us_per_call_graph']:.1f} in a graph")
+        async_push = bench_async_push(args, torch, L, configs, synth)
+        log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
+            f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
     stack = None
     if not args.no_stack:
         stack = bench_stack(args, torch, L, configs, synth)
         log(f"pi05 18L stack: {stack['us_per_step']:.1f} us/step")
-    async_push = bench_async_push(args, torch, L, configs, synth)
-    log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
-        f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
     shared = None
     if not args.no_shared:
         shared = bench_shared_kv(args, torch, L, configs, synth)
@@ -582,16 +589,20 @@ def main():
                 "frac": round(lh["partial_gbs"] / HBM_PEAK_GBS, 4),
                 "kv_stream_gbs_whole_step": round(lh["kv_gbs_step"], 1)},
         "cpu_baseline": cpu,
-        "warm_mall": {"rings": 1, "steps_per_s": warm["steps_per_s"], "ms_per_step": warm["ms_per_step"],
-                      "partial_us": round(warm["partial_us"], 3),
-                      "partial_tflops": round(warm["partial_tflops"], 2),
-                      "kv_stream_gbs_whole_step": round(warm["kv_gbs_step"], 1)},
-        "small_configs": {sm["workload"]: {"us_per_call": round(sm["us_per_call"], 2),
-                                           "us_per_call_graph": round(sm["us_per_call_graph"], 2), "calls": sm["calls"],
-                                           "layers": sm["layers"], "cached_tokens": sm["cached_tokens"],
-                                           "suffix": sm["suffix"]} for sm in small},
     }
-    line["async_push"] = async_push
+    if warm is not None:
+        line["warm_mall"] = {"rings": 1, "steps_per_s": warm["steps_per_s"], "ms_per_step": warm["ms_per_step"],
+                             "partial_us": round(warm["partial_us"], 3),
+                             "partial_tflops": round(warm["partial_tflops"], 2),
+                             "kv_stream_gbs_whole_step": round(warm["kv_gbs_step"], 1)}
+    if small is not None:
+        line["small_configs"] = {sm["workload"]: {"us_per_call": round(sm["us_per_call"], 2),
+                                                  "us_per_call_graph": round(sm["us_per_call_graph"], 2),
+                                                  "calls": sm["calls"], "layers": sm["layers"],
+                                                  "cached_tokens": sm["cached_tokens"], "suffix": sm["suffix"]}
+                                 for sm in small}
+    if async_push is not None:
+        line["async_push"] = async_push
     if stack is not None:
         line["pi05_18L_full_step"] = stack
     if shared is not None:
