@@ -258,9 +258,11 @@ def bench_small(args, torch, L, cfg, n_calls=2000):
             "cached_tokens": cfg.max_seq_len, "suffix": cfg.n_dyn, "layers": cfg.num_layers}
 
 
-def bench_stack(args, torch, L, configs, synth):
-    """Whole 18-layer denoising step of the Pi0.5-like stack, graph-replayed."""
-    s = configs.PI05_18L
+def bench_stack(args, torch, L, configs, synth, full_layer=False):
+    """Whole 18-layer denoising step of the Pi0.5-like stack, graph-replayed;
+    with full_layer, every layer also runs the SwiGLU FFN block (its own
+    AdaRMSNorm gamma, gate/up 1024 -> 4096, down 4096 -> 1024)."""
+    s = configs.PI05_18L_FFN if full_layer else configs.PI05_18L
     dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
     import numpy as np
     shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
@@ -280,7 +282,18 @@ def bench_stack(args, torch, L, configs, synth):
     mw = [synth.mlp_weights(s, l) for l in range(s.num_layers)]
     mlp = L.ada_mlp(*(dev(np.stack([w[i] for w in mw])) for i in range(4)), s.num_layers, s.cond_emb,
                     s.state_dim, s.hidden_dim, s.model_dim)
-    st = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, wqkv, wo, s.eps, s.scale, 0.1)
+    ffn_keep, mlp_f, gamma_f = (None, None, None), None, None
+    if full_layer:
+        log("generating 18 layers of SwiGLU FFN weights")
+        fw = [synth.ffn_weights(s, l) for l in range(s.num_layers)]
+        ffn_keep = tuple(dev(np.stack([w[i] for w in fw])) for i in range(3))
+        del fw
+        mf = [synth.ffn_mlp_weights(s, l) for l in range(s.num_layers)]
+        mlp_f = L.ada_mlp(*(dev(np.stack([w[i] for w in mf])) for i in range(4)), s.num_layers, s.cond_emb,
+                          s.state_dim, s.hidden_dim, s.model_dim)
+        gamma_f = torch.empty((s.num_layers, s.steps_per_frame, s.model_dim), dtype=torch.float32, device="cuda")
+    st = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, wqkv, wo, s.eps, s.scale, 0.1, 0,
+                    s.ffn_dim, *ffn_keep)
     wsb = L.pa_denoise_step_workspace_bytes(ring, st)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     gamma = torch.empty((s.num_layers, s.steps_per_frame, s.model_dim), dtype=torch.float32, device="cuda")
@@ -298,12 +311,15 @@ def bench_stack(args, torch, L, configs, synth):
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=side):
         for k in range(s.steps_per_frame):
-            L.pa_denoise_step(ring, st, x, gamma[:, k], s.steps_per_frame * s.model_dim, flag, ws, wsb)
+            L.pa_denoise_step(ring, st, x, gamma[:, k], s.steps_per_frame * s.model_dim, flag, ws, wsb,
+                              gamma_ffn=None if gamma_f is None else gamma_f[:, k])
 
     def frame(i):
         ring.push_frame(*pool[i % 4])
         state.copy_(states[i % n_frames])
         L.ada_gamma(mlp, ts, state, gamma, gws, gwsb)
+        if mlp_f is not None:
+            L.ada_gamma(mlp_f, ts, state, gamma_f, gws, gwsb)
         x.copy_(xs[i % n_frames])
         g.replay()
 
@@ -323,7 +339,7 @@ def bench_stack(args, torch, L, configs, synth):
     el_steps = time.perf_counter() - t1
     ring.close()
     return {
-        "workload": "pi05_like_18L_stack",
+        "workload": s.name,
         "us_per_step": el_steps / (n_frames * s.steps_per_frame) * 1e6,
         "steps_per_s": n_frames * s.steps_per_frame / el_steps,
         "frames_per_s_incl_push_gamma": n_frames / el,
@@ -331,7 +347,8 @@ def bench_stack(args, torch, L, configs, synth):
         "frames_timed": n_frames,
         "nonfinite_flag": int(flag.item()),
         "config": {"layers": 18, "model_dim": 1024, "q_heads": 8, "kv_heads": 1, "head_dim": 256,
-                   "pin_tokens": 48, "window": "2x768", "suffix": 51, "steps_per_frame": 10},
+                   "pin_tokens": 48, "window": "2x768", "suffix": 51, "steps_per_frame": 10,
+                   "ffn": f"SwiGLU {s.ffn_dim}" if s.ffn_dim else "none"},
     }
 
 
@@ -547,10 +564,12 @@ def main():
         async_push = bench_async_push(args, torch, L, configs, synth)
         log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
             f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
-    stack = None
+    stack = full = None
     if not args.no_stack:
         stack = bench_stack(args, torch, L, configs, synth)
         log(f"pi05 18L stack: {stack['us_per_step']:.1f} us/step")
+        full = bench_stack(args, torch, L, configs, synth, full_layer=True)
+        log(f"pi05 18L full layer (with SwiGLU FFN): {full['us_per_step']:.1f} us/step")
     shared = None
     if not args.no_shared:
         shared = bench_shared_kv(args, torch, L, configs, synth)
@@ -605,6 +624,7 @@ def main():
         line["async_push"] = async_push
     if stack is not None:
         line["pi05_18L_full_step"] = stack
+        line["pi05_18L_full_layer_step"] = full
     if shared is not None:
         line["shared_kv_multitask"] = shared
     print(json.dumps(line), flush=True)

@@ -315,14 +315,38 @@ pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, 
                          int32_t model_dim, void* x, float dt, uint32_t* nonfinite, void* stream);
 
 /* ========================================================================
+ * FFN of the full action-expert layer. The pages name SwiGLU fusion,
+ * FlashNorm and FusedAdaLN among their fused operators (Reflex review, §2
+ * and the §3 system-optimisation row; Fig. 11) but do not give the layer.
+ * Reading: with its own AdaRMSNorm gamma,
+ *     y   = bf16(AdaRMSNorm(h, gamma))             (fused into the next GEMM)
+ *     act = bf16(SiLU(y W_gate^T) * (y W_up^T))     (FP32 products, SwiGLU in the epilogue)
+ *     h  <- bf16(h + act W_down^T)
+ * and, when x is not NULL, the Euler update x <- bf16(x - dt * h).
+ * h, x bf16 [rows][model_dim]; w_gate, w_up bf16 [ffn_dim][model_dim];
+ * w_down bf16 [model_dim][ffn_dim] (nn.Linear layouts, no biases);
+ * gamma f32 [model_dim]. rows <= 64; model_dim = 128 x {2, 4, 6, 8};
+ * ffn_dim = 1024 x {1, 2, 3, 4, 6, 8}. The workspace holds act
+ * (ffn_swiglu_workspace_bytes; 0 on unsupported sizes). Every pointer
+ * 16-byte aligned. *nonfinite (nullable) gets bit 0 if a normalised element,
+ * a new h or a new x is NaN or Inf.
+ * ====================================================================== */
+size_t ffn_swiglu_workspace_bytes(int32_t rows, int32_t model_dim, int32_t ffn_dim);
+pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_t ffn_dim, const float* gamma,
+                     float eps, const void* w_gate, const void* w_up, const void* w_down, void* x, float dt,
+                     uint32_t* nonfinite, void* workspace, size_t ws_bytes, void* stream);
+
+/* ========================================================================
  * One denoising step of the stack, all layers (the chain the pages'
  * denoising loop runs ten times per frame; Reflex review §6 Table 7):
  *   h = x
  *   for l in layers:  [q|k|v] = ada_rmsnorm_qkv(h, gamma[l])      (Eq. 2)
  *                     o = partitioned attention, layer l           (Eq. 1)
  *                     h = bf16(h + o W_o[l]^T)
+ *                     h = ffn_swiglu(h, gamma_ffn[l])             (when ffn_dim > 0)
  *   x = bf16(x - dt * h)
- * gamma: f32, gamma[l] at gamma + l * gamma_layer_stride, [model_dim] each.
+ * gamma, gamma_ffn: f32, layer l's vector at + l * gamma_layer_stride,
+ * [model_dim] each (gamma_ffn may be NULL when ffn_dim = 0).
  * x: bf16 [rows][model_dim], updated in place. Layers [0, num_layers) of
  * the ring; the ring's head_dim and KV heads define D and Hkv.
  * ====================================================================== */
@@ -337,12 +361,16 @@ typedef struct {
     float scale;               /* attention scale, applied once */
     float dt;                  /* Euler step */
     int32_t num_splits;        /* attention KV splits; 0 = library's choice */
+    int32_t ffn_dim;           /* 0: no FFN; else 1024 x {1, 2, 3, 4, 6, 8} (model_dim <= 1024) */
+    const void* w_gate;        /* bf16 [L][ffn_dim][model_dim] */
+    const void* w_up;          /* bf16 [L][ffn_dim][model_dim] */
+    const void* w_down;        /* bf16 [L][model_dim][ffn_dim] */
 } pa_stack;
 
 size_t pa_denoise_step_workspace_bytes(const rb_ring* ring, const pa_stack* stack);
 pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* stack, void* x, const float* gamma,
-                          int64_t gamma_layer_stride, uint32_t* nonfinite, void* workspace,
-                          size_t ws_bytes, void* stream);
+                          const float* gamma_ffn, int64_t gamma_layer_stride, uint32_t* nonfinite,
+                          void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

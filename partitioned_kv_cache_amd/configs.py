@@ -32,6 +32,7 @@ class Shape:
     cond_emb: int = 128
     state_dim: int = 32
     hidden_dim: int = 0
+    ffn_dim: int = 0         # SwiGLU FFN width of the full action-expert layer (0: none)
     eps: float = 1e-6
     # shared-KV decode streams (only the multi-reader workload)
     n_streams: int = 0
@@ -82,4 +83,8 @@ SHARED_KV = LONG_18L.with_(name="shared_kv_multitask", cfg_id=5, frames=100, n_s
 LONG_18L_FULL = LONG_18L.with_(name="long_history_18L_full_step", cfg_id=6, model_dim=1024,
                                hidden_dim=1024)
 
-ALL = {s.name: s for s in (TINY, PI05_1L, PI05_18L, LONG_18L, SHARED_KV, LONG_18L_FULL)}
+# The full action-expert layer: the 18-layer stack plus a SwiGLU FFN of
+# width 4 x model per layer.
+PI05_18L_FFN = PI05_18L.with_(name="pi05_like_18L_full_layer", cfg_id=7, ffn_dim=4096)
+
+ALL = {s.name: s for s in (TINY, PI05_1L, PI05_18L, LONG_18L, SHARED_KV, LONG_18L_FULL, PI05_18L_FFN)}

@@ -183,6 +183,78 @@ struct GemmOut {
     uint32_t* nonfinite;
 };
 
+// AdaRMSNorm formed on the fly as the A operand of a skinny GEMM over K =
+// GEMM_WAVES * KS * 16: the FP32 mean of squares of every row (wave w takes
+// rows w, w + 8, ..., all of its loads in flight before any is used), then
+// each lane's fragments bf16(x[m][k] * rsqrt(ms + eps) * gamma[k]) for rows
+// l32 and 32 + l32 and its k-range. Ends with every wave past a barrier.
+template <int KS>
+__device__ __forceinline__ void norm_fragments(const uint16_t* __restrict__ a, const float* __restrict__ gamma,
+                                               float eps, int rows, float* rinv_s, bf16x8 (&a0)[KS],
+                                               bf16x8 (&a1)[KS]) {
+    constexpr int K = GEMM_WAVES * KS * 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int k0 = wave * KS * 16 + 8 * hi;
+    const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+    constexpr int RPW = 64 / GEMM_WAVES;        // rows per wave
+    constexpr int LPR = (K + 511) / 512;        // 16-byte loads per lane and row
+    uint4 raw[RPW][LPR];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+        const int r = wave + rr * GEMM_WAVES;
+#pragma unroll
+        for (int c = 0; c < LPR; ++c)
+            raw[rr][c] = (r < rows && c * 512 + lane * 8 < K)
+                             ? *reinterpret_cast<const uint4*>(a + (long long)r * K + c * 512 + lane * 8)
+                             : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < LPR; ++c) {
+            const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][c]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float v = bf2f(e[u]);
+                ss += v * v;
+            }
+        }
+        ss = wsum(ss);
+        const int r = wave + rr * GEMM_WAVES;
+        if (lane == 0 && r < rows) rinv_s[r] = 1.f / sqrtf(ss / (float)K + eps);
+    }
+    __syncthreads();
+    const float ri0 = r0 ? rinv_s[l32] : 0.f, ri1 = r1 ? rinv_s[32 + l32] : 0.f;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        const int k = k0 + 16 * i;
+        const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
+        const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+        if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)l32 * K + k);
+        if (r1) x1 = *reinterpret_cast<const uint4*>(a + (long long)(32 + l32) * K + k);
+        const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
+        const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a0[i][u] = (__bf16)(bf2f(e0[u]) * ri0 * gg[u]);
+            a1[i][u] = (__bf16)(bf2f(e1[u]) * ri1 * gg[u]);
+        }
+    }
+}
+
+template <int KS>
+__device__ __forceinline__ void report_nonfinite(const bf16x8 (&a0)[KS], const bf16x8 (&a1)[KS], uint32_t* flag) {
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) bad |= !finite_f((float)a0[i][u]) || !finite_f((float)a1[i][u]);
+    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1u);
+}
+
 template <int MODE, int KS, bool NORM>
 __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t* __restrict__ a,
                                                                  const float* __restrict__ gamma, float eps,
@@ -209,65 +281,10 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
             a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
         }
     } else {
-        // mean of squares per row, FP32: wave w takes rows w, w + 8, ...; all
-        // of a wave's loads are issued before any is used
-        constexpr int RPW = 64 / GEMM_WAVES;        // rows per wave
-        constexpr int LPR = (K + 511) / 512;        // 16-byte loads per lane and row
-        uint4 raw[RPW][LPR];
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-            const int r = wave + rr * GEMM_WAVES;
-#pragma unroll
-            for (int c = 0; c < LPR; ++c)
-                raw[rr][c] = (r < rows && c * 512 + lane * 8 < K)
-                                 ? *reinterpret_cast<const uint4*>(a + (long long)r * K + c * 512 + lane * 8)
-                                 : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-            float ss = 0.f;
-#pragma unroll
-            for (int c = 0; c < LPR; ++c) {
-                const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][c]);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float v = bf2f(e[u]);
-                    ss += v * v;
-                }
-            }
-            ss = wsum(ss);
-            const int r = wave + rr * GEMM_WAVES;
-            if (lane == 0 && r < rows) rinv_s[r] = 1.f / sqrtf(ss / (float)K + eps);
-        }
-        __syncthreads();
-        const float ri0 = r0 ? rinv_s[l32] : 0.f, ri1 = r1 ? rinv_s[32 + l32] : 0.f;
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            const int k = k0 + 16 * i;
-            const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
-            const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
-            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-            uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-            if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)l32 * K + k);
-            if (r1) x1 = *reinterpret_cast<const uint4*>(a + (long long)(32 + l32) * K + k);
-            const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
-            const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                a0[i][u] = (__bf16)(bf2f(e0[u]) * ri0 * gg[u]);
-                a1[i][u] = (__bf16)(bf2f(e1[u]) * ri1 * gg[u]);
-            }
-        }
+        norm_fragments<KS>(a, gamma, eps, rows, rinv_s, a0, a1);
         // every workgroup forms the same normalised rows; the first reports
         // a non-finite element (padding rows are zeros)
-        if (blockIdx.x == 0 && out.nonfinite) {
-            bool bad = false;
-#pragma unroll
-            for (int i = 0; i < KS; ++i)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) bad |= !finite_f((float)a0[i][u]) || !finite_f((float)a1[i][u]);
-            if (__any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
-        }
+        if (blockIdx.x == 0 && out.nonfinite) report_nonfinite<KS>(a0, a1, out.nonfinite);
     }
 
     f32x16 c0 = f32x16{}, c1 = f32x16{};
@@ -315,6 +332,155 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
         }
     }
     if (MODE == GEMM_OPROJ && out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
+}
+
+// ----------------------------------------------------- FFN with SwiGLU -----
+// The FFN of the full action-expert layer: the pages name "SwiGLU fusion",
+// "FlashNorm" and "FusedAdaLN" among their fused operators (Reflex review,
+// §2 and the §3 system-optimisation row; ablated in Fig. 11) without giving
+// the layer. Reading: y = bf16(AdaRMSNorm(h, gamma_ffn)) with its own gamma,
+// act = bf16(SiLU(y W_gate^T) * (y W_up^T)) (FP32 products, one rounding),
+// h <- bf16(h + act W_down^T). The norm is fused into the gate/up GEMM and
+// SwiGLU into its epilogue, so y and the gate/up products never reach memory.
+//
+// gemm_gateup: a workgroup owns 32 act columns; its 8 waves split K = model
+// (KS k-steps of 16 each) and compute both products for those columns; the
+// gate and up partial sums meet in LDS one after the other.
+template <int KS>
+__global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ gamma, float eps,
+                                                                  const uint16_t* __restrict__ w_gate,
+                                                                  const uint16_t* __restrict__ w_up, int rows, int F,
+                                                                  uint16_t* __restrict__ act, uint32_t* nonfinite) {
+    constexpr int K = GEMM_WAVES * KS * 16;
+    __shared__ float red[GEMM_WAVES][2][16][64];
+    __shared__ float rinv_s[64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int n0 = blockIdx.x * 32;
+    const int k0 = wave * KS * 16 + 8 * hi;
+    bf16x8 wg[KS], wu[KS];
+    const long long wrow = (long long)(n0 + l32) * K + k0;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        wg[i] = *reinterpret_cast<const bf16x8*>(w_gate + wrow + 16 * i);
+        wu[i] = *reinterpret_cast<const bf16x8*>(w_up + wrow + 16 * i);
+    }
+    bf16x8 a0[KS], a1[KS];
+    norm_fragments<KS>(x, gamma, eps, rows, rinv_s, a0, a1);
+    if (blockIdx.x == 0 && nonfinite) report_nonfinite<KS>(a0, a1, nonfinite);
+    const bool two = rows > 32;
+    f32x16 g0 = f32x16{}, g1 = f32x16{}, u0 = f32x16{}, u1 = f32x16{};
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wg[i], g0, 0, 0, 0);
+        u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wu[i], u0, 0, 0, 0);
+        if (two) {
+            g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wg[i], g1, 0, 0, 0);
+            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wu[i], u1, 0, 0, 0);
+        }
+    }
+    // wave w finishes 4 of the 32 (row block, register) pairs: the gate sums first
+    float gs[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        red[wave][0][r][lane] = g0[r];
+        red[wave][1][r][lane] = g1[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int uix = 0; uix < 4; ++uix) {
+        const int idx = wave * 4 + uix, blk = idx >> 4, r = idx & 15;
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        gs[uix] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        red[wave][0][r][lane] = u0[r];
+        red[wave][1][r][lane] = u1[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int uix = 0; uix < 4; ++uix) {
+        const int idx = wave * 4 + uix, blk = idx >> 4, r = idx & 15;
+        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (m >= rows) continue;
+        float u = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) u += red[ww][blk][r][lane];
+        const float g = gs[uix];
+        act[(long long)m * F + n0 + l32] = f2bf(g / (1.f + __expf(-g)) * u);
+    }
+}
+
+// gemm_down: h <- bf16(h + A W^T) (and the Euler update of x when x is not
+// null) for a long K = KC * 1024: the K range is walked in KC chunks of
+// KS = 8 k-steps per wave, the next chunk's loads in flight while the
+// current chunk's products run.
+template <int KC>
+__global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_down(const uint16_t* __restrict__ a,
+                                                                const uint16_t* __restrict__ w, int rows, int N,
+                                                                GemmOut out) {
+    constexpr int KS = 8, KCH = GEMM_WAVES * KS * 16, K = KC * KCH;
+    __shared__ float red[GEMM_WAVES][2][16][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int n0 = blockIdx.x * 32;
+    const int k0 = wave * KS * 16 + 8 * hi;
+    const bool r0 = l32 < rows, r1 = 32 + l32 < rows, two = rows > 32;
+    const uint16_t* wp = w + (long long)(n0 + l32) * K + k0;
+    const uint16_t* ap0 = a + (long long)l32 * K + k0;
+    const uint16_t* ap1 = a + (long long)(32 + l32) * K + k0;
+    bf16x8 wf[2][KS], a0[2][KS], a1[2][KS];
+    auto load = [&](int c, int buf) {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            const int off = c * KCH + 16 * i;
+            wf[buf][i] = *reinterpret_cast<const bf16x8*>(wp + off);
+            a0[buf][i] = r0 ? *reinterpret_cast<const bf16x8*>(ap0 + off) : bf16x8{};
+            a1[buf][i] = r1 ? *reinterpret_cast<const bf16x8*>(ap1 + off) : bf16x8{};
+        }
+    };
+    f32x16 c0 = f32x16{}, c1 = f32x16{};
+    load(0, 0);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        if (c + 1 < KC) load(c + 1, (c + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[c & 1][i], wf[c & 1][i], c0, 0, 0, 0);
+            if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[c & 1][i], wf[c & 1][i], c1, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        red[wave][0][r][lane] = c0[r];
+        red[wave][1][r][lane] = c1[r];
+    }
+    __syncthreads();
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
+        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int n = n0 + l32;
+        if (m >= rows) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        uint16_t* hp = out.h + (long long)m * N + n;
+        const float hn = bf2f(f2bf(bf2f(*hp) + v));
+        *hp = f2bf(hn);
+        bad |= !finite_f(hn);
+        if (out.x) {
+            uint16_t* xp = out.x + (long long)m * N + n;
+            const float xn = bf2f(*xp) - out.dt * hn;
+            bad |= !finite_f(xn);
+            *xp = f2bf(xn);
+        }
+    }
+    if (out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
 }
 
 // K = 128 * KS; the k-step counts the library is built for.
@@ -490,3 +656,62 @@ extern "C" pa_status oproj_residual(const void* o, const void* w_o, void* h, int
     PA_CHECK_ARG(e == hipSuccess, PA_EDEVICE, "oproj_residual: launch failed: %s", hipGetErrorString(e));
     return PA_OK;
 }
+
+// ---------------------------------------------------------------- FFN -------
+static bool ffn_dims_ok(int model_dim, int ffn_dim) {
+    const int ks = model_dim / 128, kc = ffn_dim / 1024;
+    return model_dim % 128 == 0 && (ks == 2 || ks == 4 || ks == 6 || ks == 8) && ffn_dim % 1024 == 0 &&
+           (kc == 1 || kc == 2 || kc == 3 || kc == 4 || kc == 6 || kc == 8);
+}
+
+extern "C" size_t ffn_swiglu_workspace_bytes(int32_t rows, int32_t model_dim, int32_t ffn_dim) {
+    if (rows < 1 || rows > 64 || !ffn_dims_ok(model_dim, ffn_dim)) return 0;
+    return align_up((size_t)rows * ffn_dim * sizeof(uint16_t), 256);
+}
+
+extern "C" pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_t ffn_dim, const float* gamma,
+                                float eps, const void* w_gate, const void* w_up, const void* w_down, void* x, float dt,
+                                uint32_t* nonfinite, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    PA_CHECK_ARG(h && gamma && w_gate && w_up && w_down && ws, PA_EINVAL, "ffn_swiglu: null argument");
+    PA_CHECK_ARG(al16(h) && al16(gamma) && al16(w_gate) && al16(w_up) && al16(w_down) && al16(ws), PA_EINVAL,
+                 "ffn_swiglu: h, gamma, the weights and the workspace must be 16-byte aligned");
+    PA_CHECK_ARG(rows >= 1 && rows <= 64, PA_ESHAPE, "ffn_swiglu: rows %d not in [1, 64]", rows);
+    PA_CHECK_ARG(ffn_dims_ok(model_dim, ffn_dim), PA_ESHAPE,
+                 "ffn_swiglu: model_dim must be 128 x {2, 4, 6, 8} and ffn_dim 1024 x {1, 2, 3, 4, 6, 8} (got %d, %d)",
+                 model_dim, ffn_dim);
+    PA_CHECK_ARG(eps >= 0.f && isfinite(dt), PA_EINVAL, "ffn_swiglu: eps must be >= 0 and dt finite");
+    const size_t need = ffn_swiglu_workspace_bytes(rows, model_dim, ffn_dim);
+    PA_CHECK_ARG(ws_bytes >= need, PA_ERANGE, "ffn_swiglu: workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t* act = static_cast<uint16_t*>(ws);
+    const uint16_t* xin = static_cast<const uint16_t*>(h);
+    const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
+    const uint16_t* wu = static_cast<const uint16_t*>(w_up);
+    const dim3 block(GEMM_WAVES * 64);
+    switch (model_dim / 128) {
+        case 2: gemm_gateup<2><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        case 4: gemm_gateup<4><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        case 6: gemm_gateup<6><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        default: gemm_gateup<8><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+    }
+    PA_LAUNCHED();
+    GemmOut o{};
+    o.h = static_cast<uint16_t*>(h);
+    o.x = static_cast<uint16_t*>(x);
+    o.dt = dt;
+    o.nonfinite = nonfinite;
+    const uint16_t* wd = static_cast<const uint16_t*>(w_down);
+    const dim3 grid(model_dim / 32);
+    switch (ffn_dim / 1024) {
+        case 1: gemm_down<1><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
+        case 2: gemm_down<2><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
+        case 3: gemm_down<3><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
+        case 4: gemm_down<4><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
+        case 6: gemm_down<6><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
+        default: gemm_down<8><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
+    }
+    PA_LAUNCHED();
+    return PA_OK;
+}
+

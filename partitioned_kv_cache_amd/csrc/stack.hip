@@ -6,9 +6,10 @@
 // while the cached regions are only read (§3 Eq. 1 text). Per layer the
 // chain is AdaRMSNorm fused into the packed QKV projection (§3 Eq. 2; §2/§4
 // fused operators), partitioned attention (Eq. 1), and a residual
-// out-projection; the Euler update of the flow state is fused into the last
-// out-projection. The out-projection, the velocity (last layer's stream) and
-// the Euler step are readings: the pages give no layer glue.
+// out-projection, optionally followed by the SwiGLU FFN; the Euler update of
+// the flow state is fused into the last projection of the last layer. The
+// out-projection, the FFN, the velocity (last layer's stream) and the Euler
+// step are readings: the pages give no layer glue.
 //
 // Everything is enqueued on one stream with no host synchronisation and no
 // allocation, so a caller can capture the whole step in a graph and replay
@@ -19,7 +20,7 @@
 namespace pa {
 
 struct StackWs {
-    size_t h, q, k, v, o, attn, total;
+    size_t h, q, k, v, o, attn, ffn, total;
 };
 
 static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes) {
@@ -37,6 +38,7 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
     w.v = take(n * hkv * d * 2);
     w.o = take(n * st->n_q_heads * d * 2);
     w.attn = take(attn_bytes);
+    w.ffn = take(st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0);
     w.total = off;
     return w;
 }
@@ -53,6 +55,11 @@ static pa_status check_stack(const Ring* r, const pa_stack* st) {
                  "pa_denoise_step: n_q_heads must be a multiple of num_kv_heads");
     PA_CHECK_ARG((st->n_q_heads * r->cfg.head_dim) % 256 == 0, PA_ESHAPE,
                  "pa_denoise_step: n_q_heads * head_dim must be a multiple of 256");
+    if (st->ffn_dim) {
+        PA_CHECK_ARG(st->w_gate && st->w_up && st->w_down, PA_EINVAL, "pa_denoise_step: null FFN weights");
+        PA_CHECK_ARG(ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) > 0, PA_ESHAPE,
+                     "pa_denoise_step: FFN needs model_dim 128 x {2, 4, 6, 8} and ffn_dim 1024 x {1, 2, 3, 4, 6, 8}");
+    }
     return PA_OK;
 }
 
@@ -82,13 +89,13 @@ extern "C" size_t pa_denoise_step_workspace_bytes(const rb_ring* ring, const pa_
 }
 
 extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, void* x, const float* gamma,
-                                     int64_t gamma_layer_stride, uint32_t* nonfinite, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     const float* gamma_ffn, int64_t gamma_layer_stride, uint32_t* nonfinite,
+                                     void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     pa_status s = check_stack(r, st);
     if (s != PA_OK) return s;
-    PA_CHECK_ARG(x && gamma && ws, PA_EINVAL, "pa_denoise_step: null argument");
+    PA_CHECK_ARG(x && gamma && ws && (gamma_ffn || !st->ffn_dim), PA_EINVAL, "pa_denoise_step: null argument");
     PA_CHECK_ARG(gamma_layer_stride >= st->model_dim, PA_ESHAPE, "pa_denoise_step: gamma stride below model_dim");
     const pattn_args a0 = attn_args(st, 0);
     const size_t attn = pattn_workspace_bytes(ring, &a0);
@@ -98,6 +105,7 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
     char* base = static_cast<char*>(ws);
     void *h = base + w.h, *q = base + w.q, *k = base + w.k, *v = base + w.v, *o = base + w.o;
     void* aws = base + w.attn;
+    void* fws = base + w.ffn;
     hipStream_t strm = static_cast<hipStream_t>(stream);
     const size_t xbytes = (size_t)st->rows * st->model_dim * 2;
     PA_HIP(hipMemcpyAsync(h, x, xbytes, hipMemcpyDeviceToDevice, strm));
@@ -105,7 +113,10 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
     const int in_dim = st->n_q_heads * d;
     const size_t wqkv_layer = (size_t)(st->n_q_heads + 2 * hkv) * d * st->model_dim;
     const size_t wo_layer = (size_t)st->model_dim * in_dim;
+    const size_t wf_layer = (size_t)st->ffn_dim * st->model_dim;
+    const size_t fws_bytes = st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0;
     for (int l = 0; l < st->num_layers; ++l) {
+        const bool last = l + 1 == st->num_layers;
         const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
         const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
         s = ada_rmsnorm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq, st->n_q_heads,
@@ -114,9 +125,18 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
         const pattn_args a = attn_args(st, l);
         s = pattn_step(ring, &a, q, k, v, o, aws, attn, stream);
         if (s != PA_OK) return s;
-        s = oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, l + 1 == st->num_layers ? x : nullptr, st->dt,
+        // the Euler update rides on the layer's last projection
+        s = oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr, st->dt,
                            nonfinite, stream);
         if (s != PA_OK) return s;
+        if (st->ffn_dim) {
+            s = ffn_swiglu(h, st->rows, st->model_dim, st->ffn_dim, gamma_ffn + l * gamma_layer_stride, st->eps,
+                           static_cast<const uint16_t*>(st->w_gate) + l * wf_layer,
+                           static_cast<const uint16_t*>(st->w_up) + l * wf_layer,
+                           static_cast<const uint16_t*>(st->w_down) + l * wf_layer, last ? x : nullptr, st->dt,
+                           nonfinite, fws, fws_bytes, stream);
+            if (s != PA_OK) return s;
+        }
     }
     return PA_OK;
 }

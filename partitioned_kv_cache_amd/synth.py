@@ -24,6 +24,7 @@ from .configs import Shape
 T_Q, T_KPIN, T_VPIN, T_KFRAME, T_VFRAME, T_KDYN, T_VDYN = 1, 2, 3, 4, 5, 6, 7
 T_X, T_STATE, T_W1, T_B1, T_W2, T_B2, T_WQKV, T_WO = 8, 9, 10, 11, 12, 13, 14, 15
 T_TAILK, T_TAILV, T_DECQ = 16, 17, 18
+T_WGATE, T_WUP, T_WDOWN, T_W1F, T_B1F, T_W2F, T_B2F = 19, 20, 21, 22, 23, 24, 25
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -118,6 +119,26 @@ def proj_weights(s: Shape, layer: int):
     hd = s.n_q_heads * s.head_dim
     wo = uniform((s.model_dim, hd), 1.0 / np.sqrt(hd), "bf16", s.cfg_id, T_WO, layer)
     return wq, wo
+
+
+def ffn_weights(s: Shape, layer: int):
+    """SwiGLU FFN weights of one layer (bf16 bits): W_gate and W_up
+    [ffn][model], W_down [model][ffn], U(+-1/sqrt(fan_in))."""
+    bm, bf = 1.0 / np.sqrt(s.model_dim), 1.0 / np.sqrt(s.ffn_dim)
+    return (uniform((s.ffn_dim, s.model_dim), bm, "bf16", s.cfg_id, T_WGATE, layer),
+            uniform((s.ffn_dim, s.model_dim), bm, "bf16", s.cfg_id, T_WUP, layer),
+            uniform((s.model_dim, s.ffn_dim), bf, "bf16", s.cfg_id, T_WDOWN, layer))
+
+
+def ffn_mlp_weights(s: Shape, layer: int):
+    """The FFN norm's own gamma-MLP weights (same shapes as mlp_weights)."""
+    cond = s.cond_emb + s.state_dim
+    b1 = 1.0 / np.sqrt(cond)
+    b2 = 1.0 / np.sqrt(s.hidden_dim)
+    return (uniform((s.hidden_dim, cond), b1, "bf16", s.cfg_id, T_W1F, layer),
+            uniform((s.hidden_dim,), b1, "bf16", s.cfg_id, T_B1F, layer),
+            uniform((s.model_dim, s.hidden_dim), b2, "bf16", s.cfg_id, T_W2F, layer),
+            uniform((s.model_dim,), b2, "bf16", s.cfg_id, T_B2F, layer))
 
 
 # -- shared-KV decode streams ------------------------------------------------------

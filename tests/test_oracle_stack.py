@@ -132,3 +132,65 @@ def test_retire_full_starts_a_new_request():
     got = decode.decode_attention(q, shared_k, shared_v, tails, 0.5)
     want0 = full_attention(q[0:1], np.concatenate([shared_k, kn[None]]), np.concatenate([shared_v, vn[None]]), 0.5)[0]
     assert np.allclose(got[0], want0, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------- SwiGLU FFN ----
+# The FFN block is a reading (the pages name "SwiGLU fusion" among the fused
+# operators but give no layer): pinned against torch's own rms_norm, silu,
+# matmul and bf16 conversion in float64, plus identities.
+
+def _torch_ffn(h, gamma, eps, wg, wu, wd):
+    import torch
+    t = lambda a: torch.tensor(a, dtype=torch.float64)          # noqa: E731
+    bf = lambda v: v.to(torch.bfloat16).to(torch.float64)       # noqa: E731
+    y = bf(torch.nn.functional.rms_norm(t(h), (h.shape[1],), weight=t(gamma), eps=eps))
+    act = bf(torch.nn.functional.silu(y @ t(wg).T) * (y @ t(wu).T))
+    return bf(t(h) + act @ t(wd).T).numpy(), act.numpy()
+
+
+@pytest.mark.parametrize("n,d,f", [(5, 8, 16), (51, 64, 256)])
+def test_ffn_swiglu_against_torch(n, d, f):
+    rng = np.random.default_rng(11 + n)
+    h = round_bf16(rng.standard_normal((n, d)))
+    gamma = 1.0 + 0.1 * rng.standard_normal(d)
+    wg, wu = rng.uniform(-1, 1, (f, d)) / np.sqrt(d), rng.uniform(-1, 1, (f, d)) / np.sqrt(d)
+    wd = rng.uniform(-1, 1, (d, f)) / np.sqrt(f)
+    wg, wu, wd = round_bf16(wg), round_bf16(wu), round_bf16(wd)
+    got = stack.ffn_swiglu(h, gamma, 1e-6, wg, wu, wd)
+    want_h, want_act = _torch_ffn(h, gamma, 1e-6, wg, wu, wd)
+    assert np.array_equal(got["act"], want_act) or np.max(np.abs(got["act"] - want_act)) <= 2.0 ** -7 * np.max(np.abs(want_act))
+    assert np.max(np.abs(got["h"] - want_h)) <= 2.0 ** -7 * np.max(np.abs(want_h))
+    # gate and up are not interchangeable: swapping them changes the result
+    swapped = stack.ffn_swiglu(h, gamma, 1e-6, wu, wg, wd)
+    assert not np.allclose(swapped["act"], got["act"])
+
+
+def test_ffn_swiglu_identities():
+    rng = np.random.default_rng(3)
+    h = round_bf16(rng.standard_normal((4, 8)))
+    gamma = np.ones(8)
+    wg, wu, wd = rng.standard_normal((16, 8)), rng.standard_normal((16, 8)), rng.standard_normal((8, 16))
+    for g_, u_, d_ in ((wg, wu, 0 * wd), (0 * wg, wu, wd), (wg, 0 * wu, wd)):
+        r = stack.ffn_swiglu(h, gamma, 1e-6, g_, u_, d_)
+        assert np.array_equal(r["h"], h)            # a zero factor leaves the stream alone
+    # SiLU(g) * u with one-hot rows: act = silu(y_i) * y_j exactly before rounding
+    e = np.eye(8)
+    r = stack.ffn_swiglu(h, gamma, 1e-6, e[[0, 1]], e[[2, 3]], np.zeros((8, 2)))
+    y = r["y2"]
+    want = round_bf16(y[:, [0, 1]] / (1 + np.exp(-y[:, [0, 1]])) * y[:, [2, 3]])
+    assert np.array_equal(r["act"], want)
+
+
+def test_layer_with_ffn_chains_after_the_attention_residual():
+    rng = np.random.default_rng(5)
+    n, d, hd = 3, 256, 64
+    h = round_bf16(rng.standard_normal((n, d)))
+    wqkv = round_bf16(rng.uniform(-1, 1, ((4 + 2) * hd, d)) / 16)
+    wo = round_bf16(rng.uniform(-1, 1, (d, 4 * hd)) / 16)
+    ck, cv = rng.standard_normal((5, 1, hd)), rng.standard_normal((5, 1, hd))
+    ffn = (np.ones(d), round_bf16(rng.uniform(-1, 1, (512, d)) / 16), round_bf16(rng.uniform(-1, 1, (512, d)) / 16),
+           round_bf16(rng.uniform(-1, 1, (d, 512)) / 22))
+    r = stack.layer(h, np.ones(d), 1e-6, wqkv, ck, cv, wo, 0.125, 4, 1, hd, ffn=ffn)
+    plain = stack.layer(h, np.ones(d), 1e-6, wqkv, ck, cv, wo, 0.125, 4, 1, hd)
+    assert np.array_equal(r["h_attn"], plain["h"])
+    assert np.array_equal(r["h"], stack.ffn_swiglu(plain["h"], *ffn[:1], 1e-6, *ffn[1:])["h"])
