@@ -388,6 +388,9 @@ def bench_shared_kv(args, torch, L, configs, synth, budgets=(1, 5, 10), n_frames
     d_out = torch.empty((s.num_layers, G, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
     ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
 
+    f_wsb = L.pattn_fused_workspace_bytes(ring, a_args, d_args)
+    f_ws = torch.empty(f_wsb, dtype=torch.uint8, device="cuda")
+
     def frame(i, k_dec, ev=None):
         ring.push_frame(*pool[i % 4])
         for k in range(s.steps_per_frame):
@@ -400,7 +403,18 @@ def bench_shared_kv(args, torch, L, configs, synth, budgets=(1, 5, 10), n_frames
         if ev is not None:
             ev[1].record()
 
-    sweep = {}
+    def frame_fused(i, k_dec, ev=None):
+        # decode step t rides on action step t: one pass over the shared cache for both
+        ring.push_frame(*pool[i % 4])
+        for k in range(s.steps_per_frame):
+            if k < k_dec:
+                L.pattn_append_private(ring, d_args, tail_k, tail_v, tail_len, *dkv[k % 2], ovf)
+                L.pattn_fused_step(ring, a_args, *steps_in[k], a_out, d_args, dq[k % 2], tail_k, tail_v, tail_len,
+                                   d_out, f_ws, f_wsb)
+            else:
+                L.pattn_step(ring, a_args, *steps_in[k], a_out, a_ws, a_wsb)
+
+    sweep, sweep_fused = {}, {}
     for k_dec in budgets:
         tail_len = dev(np.array([(2 * j) % cap for j in range(G)], dtype=np.int32))
         frame(0, k_dec)
@@ -415,11 +429,24 @@ def bench_shared_kv(args, torch, L, configs, synth, budgets=(1, 5, 10), n_frames
         assert int(ovf.item()) == 0, "a private tail overflowed with retiring on"
         sweep[k_dec] = {"frames_per_s": n_frames / el, "decode_tokens_per_s": G * k_dec * n_frames / el,
                         "decode_step_us": dec_us, "frames_timed": n_frames}
+        if k_dec <= s.steps_per_frame:
+            tail_len = dev(np.array([(2 * j) % cap for j in range(G)], dtype=np.int32))
+            frame_fused(0, k_dec)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(n_frames):
+                frame_fused(1 + i, k_dec)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            assert int(ovf.item()) == 0, "a private tail overflowed with retiring on"
+            sweep_fused[k_dec] = {"frames_per_s": n_frames / el, "decode_tokens_per_s": G * k_dec * n_frames / el,
+                                  "frames_timed": n_frames}
     ring.close()
     k1 = sweep[budgets[0]]
     return {"workload": "shared_kv_multitask", "frames_per_s": k1["frames_per_s"],
             "decode_tokens_per_s": k1["decode_tokens_per_s"], "decode_step_us": k1["decode_step_us"],
             "frames_timed": n_frames, "decode_budget_sweep": {f"k={k}": v for k, v in sweep.items()},
+            "fused_decode_budget_sweep": {f"k={k}": v for k, v in sweep_fused.items()},
             "config": {"layers": 18, "cache": "256 + 8x768", "action_suffix": 51, "steps_per_frame": 10,
                        "decode_streams": G, "tail_capacity": cap, "retire_at": cap,
                        "decode_steps_per_frame": budgets[0]}}

@@ -245,6 +245,26 @@ pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* args, const
                        const void* tail_k, const void* tail_v, const int32_t* tail_len,
                        void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* One pass for the action suffix and the decode streams together (OxyGen
+ * review, core method: one shared cache read by the action expert and the
+ * language expert, whose requests are batched per frame). The action rows
+ * (args->n_dyn tokens x Hq heads) and the decode rows (dec->n_streams x Hq)
+ * are stacked into one query matrix per layer and KV head, so the shared
+ * [pin; window] keys stream once for both. Results equal pattn_step(args,
+ * q, k_dyn, v_dyn, out) and pattn_decode(dec, q_dec, tails, out_dec) up to
+ * rounding order: the action rows see the suffix keys and never a tail; each
+ * decode row sees [pin; window; its own tail] and never the suffix. Append
+ * the decode tokens first (pattn_append_private). bf16 rings only;
+ * args and dec must agree on the layer range, Hq and scale (PA_EINVAL).
+ * Buffers as in pattn_step and pattn_decode, all 16-byte aligned. */
+size_t pattn_fused_workspace_bytes(const rb_ring* ring, const pattn_args* args,
+                                   const pattn_decode_args* dec);
+pa_status pattn_fused_step(const rb_ring* ring, const pattn_args* args, const void* q,
+                           const void* k_dyn, const void* v_dyn, void* out,
+                           const pattn_decode_args* dec, const void* q_dec, const void* tail_k,
+                           const void* tail_v, const int32_t* tail_len, void* out_dec,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 /* ========================================================================
  * AdaRMSNorm (Reflex review §3 Eq. 2 and component table; §5 module):
  *     y = x / sqrt(mean(x^2) + eps) * gamma,   gamma = 1 + MLP(c),

@@ -36,7 +36,8 @@ EXPORTS = (
     "pattn_decode", "ada_gamma_workspace_bytes", "ada_gamma", "ada_rmsnorm_workspace_bytes", "ada_rmsnorm",
     "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
     "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
-    "rb_stage_frame", "rb_commit_frame", "ffn_swiglu_workspace_bytes", "ffn_swiglu",
+    "rb_stage_frame", "rb_commit_frame", "ffn_swiglu_workspace_bytes", "ffn_swiglu", "pattn_fused_workspace_bytes",
+    "pattn_fused_step",
 )
 
 
@@ -112,6 +113,9 @@ _sig("ffn_swiglu", _i32, _vp, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _
 _sig("pattn_append_private", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _sig("pattn_decode_workspace_bytes", _sz, _vp, C.POINTER(PattnDecodeArgs))
 _sig("pattn_decode", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("pattn_fused_workspace_bytes", _sz, _vp, C.POINTER(PattnArgs), C.POINTER(PattnDecodeArgs))
+_sig("pattn_fused_step", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp,
+     _vp, _vp, _vp, _sz, _vp)
 _sig("ada_gamma_workspace_bytes", _sz, C.POINTER(AdaMlp), _i32)
 _sig("ada_gamma", _i32, C.POINTER(AdaMlp), C.POINTER(C.c_float), _i32, _vp, _vp, _vp, _sz, _vp)
 _sig("ada_rmsnorm_workspace_bytes", _sz, C.POINTER(AdaMlp))
@@ -331,3 +335,16 @@ def ffn_swiglu(h, rows: int, model_dim: int, ffn_dim: int, gamma, eps: float, w_
 def raw():
     """The ctypes CDLL itself (for the symbol-export test)."""
     return _lib
+
+
+def pattn_fused_workspace_bytes(ring: Ring, args: PattnArgs, dec: PattnDecodeArgs) -> int:
+    return _lib.pattn_fused_workspace_bytes(ring.handle, C.byref(args), C.byref(dec))
+
+
+def pattn_fused_step(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, dec: PattnDecodeArgs, q_dec, tail_k, tail_v,
+                     tail_len, out_dec, workspace, ws_bytes: int, stream=None):
+    """The action suffix and the decode streams in one pass over the shared cache (pattn_fused_step)."""
+    _check(_lib.pattn_fused_step(ring.handle, C.byref(args), ptr(q), ptr(k_dyn), ptr(v_dyn), ptr(out), C.byref(dec),
+                                 ptr(q_dec), ptr(tail_k), ptr(tail_v), ptr(tail_len), ptr(out_dec), ptr(workspace),
+                                 ws_bytes, _stream(stream)), "pattn_fused_step")
+

@@ -256,14 +256,19 @@ __device__ __forceinline__ f32x16 qk_scores(const char* kb, int koff0, int koff1
 // Online softmax of one tile's scores: updates the running (m, l), rescales
 // O when the reference max moves, and returns P in bf16 in the B-operand
 // layout of the PV product.
-template <int D>
+// With FUSED, rows differ in how many keys they see (k_lim per lane, the
+// wave's smallest in k_lim_wave): a row can have every key of a tile masked
+// while its running max is still -inf, which the rescale and the exponent
+// must then treat as "nothing yet" instead of producing NaN.
+template <int D, bool FUSED = false>
 __device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int hi, float scale_log2,
-                                             f32x16 (&acc)[D / 32], float& m_run, float& l_run, bf16x8 (&pf)[2]) {
+                                             f32x16 (&acc)[D / 32], float& m_run, float& l_run, bf16x8 (&pf)[2],
+                                             int k_lim_wave = 0) {
     constexpr int DB = D / 32;
     // Row max on the raw scores (scale > 0 keeps the order); keys past the
     // split's end exist only in its last tile and are masked there alone.
     float rmax = -INFINITY;
-    if (base + KT <= k_end) {
+    if (base + KT <= (FUSED ? k_lim_wave : k_end)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
     } else {
@@ -284,7 +289,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int 
     // reference); probabilities stay below 2^RESCALE_SLACK.
     if (__any(tmax > m_run + RESCALE_SLACK)) {
         const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = FUSED && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b) acc[b] *= alpha;
@@ -292,10 +297,11 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int 
     }
     // p = 2^(scale log2e s - m): one FMA and the hardware exp2 (v_exp_f32);
     // results below 2^-126 flush to zero, far below what a bf16 P can carry.
+    const float m_e = FUSED ? fmaxf(m_run, -3.0e38f) : m_run;   // a row with nothing yet: p = 0
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_e));
         psum += p;
         pf[r >> 3][r & 7] = (__bf16)p;
     }
@@ -336,12 +342,17 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int D>
+// FUSED: rows [0, m1) are the action suffix's (queries from q, keys
+// [pin | window | suffix]); rows [m1, m_rows) are decode streams' (queries
+// from q2, keys [pin | window] only: the suffix keys are masked for them).
+template <int D, bool FUSED = false>
 __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
                                                                           long long q_layer, int hq, int group,
                                                                           int m_rows, KvSource src, int chunk,
                                                                           float scale_log2, Partials part, int parts,
-                                                                          int row_blocks) {
+                                                                          int row_blocks,
+                                                                          const uint16_t* __restrict__ q2 = nullptr,
+                                                                          long long q2_layer = 0, int m1 = 0) {
     constexpr int KD = D / 16;               // k-steps over the head dimension
     constexpr int DB = D / 32;               // 32-wide output blocks = planes
     constexpr int PLANE = KT * 64;           // bytes per plane (KT keys x 32 dims x 2 B)
@@ -366,7 +377,10 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
 
     bf16x8 qf[KD];
     if (row < m_rows) {
-        const uint16_t* qp = q + lb * q_layer + ((long long)(row / group) * hq + g * group + row % group) * D + 8 * hi;
+        const bool second = FUSED && row >= m1;
+        const int r = second ? row - m1 : row;
+        const uint16_t* qp = (second ? q2 + lb * q2_layer : q + lb * q_layer) +
+                             ((long long)(r / group) * hq + g * group + r % group) * D + 8 * hi;
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
     } else {
@@ -375,6 +389,17 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     }
 
     const int k_begin = split * chunk, k_end = min(k_begin + chunk, src.total());
+    // FUSED: this lane's key limit (decode rows stop before the suffix) and the wave's smallest
+    const int k_lim = FUSED && row >= m1 ? min(k_end, src.pinned + src.n_slide) : k_end;
+    int k_lim_wave = k_lim;
+    if (FUSED) {
+        k_lim_wave = min(k_lim_wave, __shfl_xor(k_lim_wave, 16));
+        k_lim_wave = min(k_lim_wave, __shfl_xor(k_lim_wave, 8));
+        k_lim_wave = min(k_lim_wave, __shfl_xor(k_lim_wave, 4));
+        k_lim_wave = min(k_lim_wave, __shfl_xor(k_lim_wave, 2));
+        k_lim_wave = min(k_lim_wave, __shfl_xor(k_lim_wave, 1));
+        k_lim_wave = __builtin_amdgcn_readfirstlane(k_lim_wave);
+    }
 
     // Base pointers of this (layer, KV head), hoisted so that choosing between
     // the ring and the suffix buffer is a register select, not a memory load.
@@ -444,7 +469,7 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
         if (active) {
             bf16x8 pf[2];
             const f32x16 sc = qk_scores<D>(lds_buffer<J, TILE>(), koff0, koff1, qf);
-            softmax_tile<D>(sc, k_begin + t * KT, k_end, hi, scale_log2, acc, m_run, l_run, pf);
+            softmax_tile<D, FUSED>(sc, k_begin + t * KT, k_lim, hi, scale_log2, acc, m_run, l_run, pf, k_lim_wave);
             pv_tile<D>(lds_buffer<NBUF + J, TILE>(), voff, pf, acc);
         }
     };
@@ -474,13 +499,14 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
 
 // ---------------------------------------------------------------------------
 // Private-tail partial of the decode readers: one wave per (stream, head)
-// row over that stream's own appended tokens. Writes partial slot `slot`.
+// row over that stream's own appended tokens. Writes partial slot `slot`,
+// partial row row_base + row.
 // grid (ceil(M / 4), Lb * Hkv), block 256.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void partial_tail(const T* q, long long q_layer, int hq, int group, int m_rows,
                                                     const T* tail_k, const T* tail_v, const int32_t* tail_len,
                                                     int n_streams, int cap, int hkv, float scale_log2, int slot,
-                                                    Partials part) {
+                                                    Partials part, int row_base) {
     __shared__ __attribute__((aligned(16))) float qs[VALU_ROWS][D];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lg = blockIdx.y, lb = lg / hkv, g = lg % hkv;
@@ -497,7 +523,7 @@ __global__ __launch_bounds__(256) void partial_tail(const T* q, long long q_laye
     float m = -INFINITY, l = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     valu_row<T, D>(qs[wave], 0, n, scale_log2, row_of, m, l, o);
-    if (row_ok) store_row_partial<T>(part, slot, lg, row, D, m, l, o);
+    if (row_ok) store_row_partial<T>(part, slot, lg, row_base + row, D, m, l, o);
 }
 
 // Four consecutive outputs of one row: one 8-byte (bf16) or 16-byte (f32) store.
@@ -518,17 +544,18 @@ __device__ __forceinline__ float4 ld4(const uint16_t* p) {
                        __uint_as_float(u.y & 0xffff0000u));
 }
 
+// Merges partial rows [row_lo, row_hi); output row index row - row_lo.
 template <typename TO, int D, typename PO>
-__global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m_rows, int group, int hq, int hkv,
-                                               long long out_layer, TO* out) {
+__global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int row_lo, int row_hi, int group, int hq,
+                                               int hkv, long long out_layer, TO* out) {
     constexpr int DB = D / 32;
     // one wave per (32-row block, 32-dim block): 1 KB contiguous per split
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int unit = blockIdx.x * 4 + wave, lg = blockIdx.y;
-    const int row0 = (unit / DB) * 32, b = unit % DB;
-    if (row0 >= m_rows) return;
+    const int row0 = (row_lo & ~31) + (unit / DB) * 32, b = unit % DB;
+    if (row0 >= row_hi) return;
     const int row = row0 + l32;
-    const bool ok = row < m_rows;
+    const bool ok = row >= row_lo && row < row_hi;
     const int lb = lg / hkv, g = lg % hkv;
     // Online merge over batches of splits: (mx, lsum, acc) is the merge of
     // the splits seen so far, referenced to mx.
@@ -569,7 +596,8 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int m
     }
     if (!ok) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    TO* orow = out + lb * out_layer + ((long long)(row / group) * hq + g * group + row % group) * D + 32 * b + 4 * hi;
+    const int r = row - row_lo;
+    TO* orow = out + lb * out_layer + ((long long)(r / group) * hq + g * group + r % group) * D + 32 * b + 4 * hi;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         st4(orow + 8 * j, make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv));
@@ -722,7 +750,8 @@ static KvSource source_for(const Ring* r, int layer_begin, const void* k_dyn, co
 }
 
 static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, long long q_layer, int hq,
-                                 const KvSource& src, float scale, const Partials& part, hipStream_t stream) {
+                                 const KvSource& src, float scale, const Partials& part, hipStream_t stream,
+                                 const void* q2 = nullptr, long long q2_layer = 0, int m1 = 0) {
     if (p.parts == 0) return PA_OK;
     const float scale_log2 = scale * 1.4426950408889634f;
     const int d = r->cfg.head_dim;
@@ -731,15 +760,21 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
         const int units = p.parts * p.lg_count;
         const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
-        if (d == 256)
-            partial_mfma<256><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk,
-                                                                   scale_log2, part, p.parts, row_blocks);
-        else if (d == 128)
-            partial_mfma<128><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk,
-                                                                   scale_log2, part, p.parts, row_blocks);
-        else
-            partial_mfma<64><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk,
-                                                                  scale_log2, part, p.parts, row_blocks);
+        const uint16_t* qq2 = static_cast<const uint16_t*>(q2);
+#define PA_MFMA(DD, FU)                                                                                       \
+    partial_mfma<DD, FU><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
+                                                               scale_log2, part, p.parts, row_blocks, qq2,       \
+                                                               q2_layer, m1)
+        if (q2) {
+            if (d == 256) PA_MFMA(256, true);
+            else if (d == 128) PA_MFMA(128, true);
+            else PA_MFMA(64, true);
+        } else {
+            if (d == 256) PA_MFMA(256, false);
+            else if (d == 128) PA_MFMA(128, false);
+            else PA_MFMA(64, false);
+        }
+#undef PA_MFMA
     } else {
         dim3 grid(p.parts, valu_row_blocks(p.m_rows), p.lg_count);
         const float* qf = static_cast<const float*>(q);
@@ -756,18 +791,20 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
 }
 
 static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int hq, long long out_layer, void* out,
-                                int out_dtype, const Partials& part, hipStream_t stream) {
+                                int out_dtype, const Partials& part, hipStream_t stream, int row_lo = 0,
+                                int row_hi = -1) {
     const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
-    const int units = (p.m_rows + 31) / 32 * (d / 32);          // (32-row, 32-dim) blocks, one wave each
+    if (row_hi < 0) row_hi = p.m_rows;
+    const int units = (row_hi - (row_lo & ~31) + 31) / 32 * (d / 32);   // (32-row, 32-dim) blocks, one wave each
     const dim3 grid((units + 3) / 4, p.lg_count);
 #define PA_COMBINE(TO, DD)                                                                                  \
     do {                                                                                                    \
         if (p.o_bytes == 2)                                                                                 \
-            combine<TO, DD, uint16_t><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv,  \
-                                                                out_layer, static_cast<TO*>(out));          \
+            combine<TO, DD, uint16_t><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
+                                                                hkv, out_layer, static_cast<TO*>(out));     \
         else                                                                                                \
-            combine<TO, DD, float><<<grid, 256, 0, stream>>>(part, n_parts, p.m_rows, p.group, hq, hkv,     \
-                                                             out_layer, static_cast<TO*>(out));             \
+            combine<TO, DD, float><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,    \
+                                                             hkv, out_layer, static_cast<TO*>(out));        \
     } while (0)
     if (out_dtype == PA_F32) {
         if (d == 256) PA_COMBINE(float, 256);
@@ -882,6 +919,33 @@ extern "C" size_t pattn_decode_workspace_bytes(const rb_ring* ring, const pattn_
     return partial_bytes(p, r->cfg.head_dim);
 }
 
+// Private-tail partials of decode rows [row_base, row_base + G * group) into slot `slot`.
+static pa_status launch_tails(const Ring* r, const Plan& p, const void* q, long long q_layer, int hq, const void* tail_k,
+                              const void* tail_v, const int32_t* tail_len, int n_streams, int cap, float scale,
+                              int slot, const Partials& part, int row_base, hipStream_t s) {
+    const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
+    const int m_rows = n_streams * p.group;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    dim3 grid(valu_row_blocks(m_rows), p.lg_count);
+#define PA_TAIL(T, DD)                                                                                           \
+    partial_tail<T, DD><<<grid, 256, 0, s>>>(static_cast<const T*>(q), q_layer, hq, p.group, m_rows,               \
+                                             static_cast<const T*>(tail_k), static_cast<const T*>(tail_v), tail_len, \
+                                             n_streams, cap, hkv, scale_log2, slot, part, row_base)
+    if (r->cfg.dtype == PA_F32) {
+        if (d == 256) PA_TAIL(float, 256);
+        else if (d == 128) PA_TAIL(float, 128);
+        else if (d == 64) PA_TAIL(float, 64);
+        else PA_TAIL(float, 32);
+    } else {
+        if (d == 256) PA_TAIL(uint16_t, 256);
+        else if (d == 128) PA_TAIL(uint16_t, 128);
+        else PA_TAIL(uint16_t, 64);
+    }
+#undef PA_TAIL
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
 extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* a, const void* q, const void* tail_k,
                                   const void* tail_v, const int32_t* tail_len, void* out, void* ws, size_t ws_bytes,
                                   void* stream) {
@@ -906,23 +970,79 @@ extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* 
     const long long q_layer = (long long)a->n_streams * a->n_q_heads * d;
     st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s);
     if (st != PA_OK) return st;
-    const float scale_log2 = a->scale * 1.4426950408889634f;
-    dim3 grid(valu_row_blocks(p.m_rows), p.lg_count);
-#define PA_TAIL(T, DD)                                                                                          \
-    partial_tail<T, DD><<<grid, 256, 0, s>>>(static_cast<const T*>(q), q_layer, a->n_q_heads, p.group, p.m_rows, \
-                                             static_cast<const T*>(tail_k), static_cast<const T*>(tail_v), tail_len, \
-                                             a->n_streams, a->tail_capacity, hkv, scale_log2, p.parts, part)
-    if (r->cfg.dtype == PA_F32) {
-        if (d == 256) PA_TAIL(float, 256);
-        else if (d == 128) PA_TAIL(float, 128);
-        else if (d == 64) PA_TAIL(float, 64);
-        else PA_TAIL(float, 32);
-    } else {
-        if (d == 256) PA_TAIL(uint16_t, 256);
-        else if (d == 128) PA_TAIL(uint16_t, 128);
-        else PA_TAIL(uint16_t, 64);
-    }
-#undef PA_TAIL
-    PA_LAUNCHED();
+    st = launch_tails(r, p, q, q_layer, a->n_q_heads, tail_k, tail_v, tail_len, a->n_streams, a->tail_capacity,
+                      a->scale, p.parts, part, 0, s);
+    if (st != PA_OK) return st;
     return launch_combine(r, p, p.parts + 1, a->n_q_heads, q_layer, out, a->out_dtype, part, s);
 }
+
+// ---------------------------------------------------------------------------
+// One pass for both kinds of reader (OxyGen review, core method: the action
+// expert and the language expert read one shared cache; this build's f3
+// fuses their rows): the action suffix's rows and the decode streams' rows
+// stacked into one query matrix per (layer, KV head), so the shared
+// [pin | window] keys stream through the chip once for both.
+
+static pa_status check_fused(const Ring* r, const pattn_args* a, const pattn_decode_args* d) {
+    pa_status st = check_decode(r, d);
+    if (st != PA_OK) return st;
+    PA_CHECK_ARG(a, PA_EINVAL, "pattn_fused_step: null argument");
+    PA_CHECK_ARG(r->cfg.dtype == PA_BF16, PA_EINVAL, "pattn_fused_step: needs a bf16 ring");
+    PA_CHECK_ARG(a->layer_begin == d->layer_begin && a->num_layers == d->num_layers && a->n_q_heads == d->n_q_heads &&
+                     a->scale == d->scale,
+                 PA_EINVAL, "pattn_fused_step: action and decode arguments must agree on layers, heads and scale");
+    PA_CHECK_ARG(a->out_dtype == PA_F32 || a->out_dtype == PA_BF16, PA_EINVAL, "pattn_fused_step: bad out_dtype");
+    PA_CHECK_ARG(a->n_dyn >= 1, PA_ESHAPE, "pattn_fused_step: n_dyn must be >= 1");
+    return PA_OK;
+}
+
+extern "C" size_t pattn_fused_workspace_bytes(const rb_ring* ring, const pattn_args* a, const pattn_decode_args* d) {
+    clear_error();
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    if (!r || check_fused(r, a, d) != PA_OK) return 0;
+    Plan p;
+    if (plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_dyn + d->n_streams, a->n_dyn, a->num_splits, 1,
+                 &p) != PA_OK)
+        return 0;
+    return partial_bytes(p, r->cfg.head_dim);
+}
+
+extern "C" pa_status pattn_fused_step(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
+                                      const void* v_dyn, void* out, const pattn_decode_args* d, const void* q_dec,
+                                      const void* tail_k, const void* tail_v, const int32_t* tail_len, void* out_dec,
+                                      void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    PA_CHECK_ARG(r, PA_EINVAL, "pattn_fused_step: null ring");
+    pa_status st = check_fused(r, a, d);
+    if (st != PA_OK) return st;
+    PA_CHECK_ARG(q && k_dyn && v_dyn && out && q_dec && tail_k && tail_v && tail_len && out_dec && ws, PA_EINVAL,
+                 "pattn_fused_step: null argument");
+    PA_CHECK_ARG(aligned16(q) && aligned16(k_dyn) && aligned16(v_dyn) && aligned16(out) && aligned16(q_dec) &&
+                     aligned16(tail_k) && aligned16(tail_v) && aligned16(out_dec) && aligned16(ws) &&
+                     aligned16(r->k) && aligned16(r->v),
+                 PA_EINVAL, "pattn_fused_step: every buffer must be 16-byte aligned");
+    Plan p;
+    st = plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_dyn + d->n_streams, a->n_dyn, a->num_splits, 1,
+                  &p);
+    if (st != PA_OK) return st;
+    PA_CHECK_ARG(!(r->cfg.pin_capacity > 0 && r->pinned == 0), PA_ESTATE, "pattn_fused_step: the prefix is not pinned yet");
+    const size_t need = partial_bytes(p, r->cfg.head_dim);
+    PA_CHECK_ARG(ws_bytes >= need, PA_ERANGE, "pattn_fused_step: workspace %zu bytes < %zu needed", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const KvSource src = source_for(r, a->layer_begin, k_dyn, v_dyn, a->n_dyn);
+    const Partials part = partials_in(ws, p, r->cfg.head_dim);
+    const int D = r->cfg.head_dim;
+    const int m_act = a->n_dyn * p.group;                       // action rows first, then decode rows
+    const long long qa_layer = (long long)a->n_dyn * a->n_q_heads * D;
+    const long long qd_layer = (long long)d->n_streams * a->n_q_heads * D;
+    st = launch_partials(r, p, q, qa_layer, a->n_q_heads, src, a->scale, part, s, q_dec, qd_layer, m_act);
+    if (st != PA_OK) return st;
+    st = launch_tails(r, p, q_dec, qd_layer, a->n_q_heads, tail_k, tail_v, tail_len, d->n_streams, d->tail_capacity,
+                      a->scale, p.parts, part, m_act, s);
+    if (st != PA_OK) return st;
+    st = launch_combine(r, p, p.parts, a->n_q_heads, qa_layer, out, a->out_dtype, part, s, 0, m_act);
+    if (st != PA_OK) return st;
+    return launch_combine(r, p, p.parts + 1, a->n_q_heads, qd_layer, out_dec, d->out_dtype, part, s, m_act, p.m_rows);
+}
+
