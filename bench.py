@@ -292,9 +292,23 @@ def bench_stack(args, torch, L, configs, synth, full_layer=False):
         mlp_f = L.ada_mlp(*(dev(np.stack([w[i] for w in mf])) for i in range(4)), s.num_layers, s.cond_emb,
                           s.state_dim, s.hidden_dim, s.model_dim)
         gamma_f = torch.empty((s.num_layers, s.steps_per_frame, s.model_dim), dtype=torch.float32, device="cuda")
-    st = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, wqkv, wo, s.eps, s.scale, 0.1, 0,
-                    s.ffn_dim, *ffn_keep)
-    wsb = L.pa_denoise_step_workspace_bytes(ring, st)
+    st_plain = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, wqkv, wo, s.eps, s.scale, 0.1, 0,
+                          s.ffn_dim, *ffn_keep)
+
+    # the product path: the same weights in the fragment-packed order
+    def packed(w, n, k):
+        out = torch.empty_like(w)
+        L.pa_pack_weight(w, n, k, out)
+        return out
+
+    nl, hd, fd = s.num_layers, s.n_q_heads * s.head_dim, s.ffn_dim
+    pk_keep = (None, None, None)
+    if full_layer:
+        pk_keep = (packed(ffn_keep[0], nl * fd, s.model_dim), packed(ffn_keep[1], nl * fd, s.model_dim),
+                   packed(ffn_keep[2], nl * s.model_dim, fd))
+    st = L.pa_stack(s.num_layers, s.n_dyn, s.model_dim, s.n_q_heads, packed(wqkv, nl * s.qkv_out, s.model_dim),
+                    packed(wo, nl * s.model_dim, hd), s.eps, s.scale, 0.1, 0, s.ffn_dim, *pk_keep, packed=1)
+    wsb = max(L.pa_denoise_step_workspace_bytes(ring, st), L.pa_denoise_step_workspace_bytes(ring, st_plain))
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     gamma = torch.empty((s.num_layers, s.steps_per_frame, s.model_dim), dtype=torch.float32, device="cuda")
     gwsb = L.ada_gamma_workspace_bytes(mlp, s.steps_per_frame)
@@ -312,6 +326,11 @@ def bench_stack(args, torch, L, configs, synth, full_layer=False):
     with torch.cuda.graph(g, stream=side):
         for k in range(s.steps_per_frame):
             L.pa_denoise_step(ring, st, x, gamma[:, k], s.steps_per_frame * s.model_dim, flag, ws, wsb,
+                              gamma_ffn=None if gamma_f is None else gamma_f[:, k])
+    g_plain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_plain, stream=side):
+        for k in range(s.steps_per_frame):
+            L.pa_denoise_step(ring, st_plain, x, gamma[:, k], s.steps_per_frame * s.model_dim, flag, ws, wsb,
                               gamma_ffn=None if gamma_f is None else gamma_f[:, k])
 
     def frame(i):
@@ -337,10 +356,20 @@ def bench_stack(args, torch, L, configs, synth, full_layer=False):
         g.replay()
     torch.cuda.synchronize()
     el_steps = time.perf_counter() - t1
+    # the same ten steps on the unpacked (nn.Linear layout) weights
+    g_plain.replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(n_frames):
+        g_plain.replay()
+    torch.cuda.synchronize()
+    el_plain = time.perf_counter() - t2
     ring.close()
     return {
         "workload": s.name,
         "us_per_step": el_steps / (n_frames * s.steps_per_frame) * 1e6,
+        "weights": "fragment-packed (pa_pack_weight)",
+        "us_per_step_unpacked_weights": el_plain / (n_frames * s.steps_per_frame) * 1e6,
         "steps_per_s": n_frames * s.steps_per_frame / el_steps,
         "frames_per_s_incl_push_gamma": n_frames / el,
         "us_per_frame_incl_push_gamma": el / n_frames * 1e6,

@@ -385,7 +385,26 @@ typedef struct {
     const void* w_gate;        /* bf16 [L][ffn_dim][model_dim] */
     const void* w_up;          /* bf16 [L][ffn_dim][model_dim] */
     const void* w_down;        /* bf16 [L][model_dim][ffn_dim] */
+    int32_t packed;            /* 1: all five weights are fragment-packed (pa_pack_weight) */
 } pa_stack;
+
+/* Fragment-packed weights for the stack (pa_stack.packed = 1).
+ * The projections of the stack have 51-64 rows and stream one weight matrix
+ * each, so they are bound by how many memory requests their loads take.
+ * pa_pack_weight rewrites an nn.Linear weight W bf16 [n][k] once, at setup,
+ * into the order the matrix cores read it: 32-row blocks, and inside a block
+ * 16-k steps of 64 lanes x 8 elements, so that every wave load is 1 KB
+ * contiguous. Element (r, c) lands at
+ *     (((r / 32) * (k / 16) + c / 16) * 64 + ((c / 8) % 2) * 32 + r % 32) * 8 + c % 8.
+ * The packed matrix has the size of the input. Because n is a multiple of
+ * 32, packing a per-layer stack [L][n][k] as one [L * n][k] matrix packs
+ * each layer in place, so layer l still starts at l * n * k elements.
+ * w and w_packed: device, 16-byte aligned, distinct, caller-owned; n a
+ * multiple of 32, k a multiple of 16. Asynchronous on `stream`.
+ * With packed = 1 the stack also needs model_dim in {512, 1024},
+ * Hq * D = 1024 x {1, 2, 3, 4, 6, 8} and ffn_dim (when set) likewise; its
+ * results are bit-identical to the unpacked stack's. */
+pa_status pa_pack_weight(const void* w, int32_t n, int32_t k, void* w_packed, void* stream);
 
 size_t pa_denoise_step_workspace_bytes(const rb_ring* ring, const pa_stack* stack);
 pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* stack, void* x, const float* gamma,

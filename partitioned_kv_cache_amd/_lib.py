@@ -37,7 +37,7 @@ EXPORTS = (
     "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
     "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
     "rb_stage_frame", "rb_commit_frame", "ffn_swiglu_workspace_bytes", "ffn_swiglu", "pattn_fused_workspace_bytes",
-    "pattn_fused_step",
+    "pattn_fused_step", "pa_pack_weight",
 )
 
 
@@ -80,7 +80,7 @@ class PaStack(C.Structure):
     _fields_ = [("num_layers", C.c_int32), ("rows", C.c_int32), ("model_dim", C.c_int32), ("n_q_heads", C.c_int32),
                 ("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("eps", C.c_float), ("scale", C.c_float),
                 ("dt", C.c_float), ("num_splits", C.c_int32), ("ffn_dim", C.c_int32), ("w_gate", C.c_void_p),
-                ("w_up", C.c_void_p), ("w_down", C.c_void_p)]
+                ("w_up", C.c_void_p), ("w_down", C.c_void_p), ("packed", C.c_int32)]
 
 
 _vp, _i32, _f32, _sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
@@ -110,6 +110,7 @@ _sig("pa_denoise_step_workspace_bytes", _sz, _vp, C.POINTER(PaStack))
 _sig("pa_denoise_step", _i32, _vp, C.POINTER(PaStack), _vp, _vp, _vp, C.c_int64, _vp, _vp, _sz, _vp)
 _sig("ffn_swiglu_workspace_bytes", _sz, _i32, _i32, _i32)
 _sig("ffn_swiglu", _i32, _vp, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp)
+_sig("pa_pack_weight", _i32, _vp, _i32, _i32, _vp, _vp)
 _sig("pattn_append_private", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _sig("pattn_decode_workspace_bytes", _sz, _vp, C.POINTER(PattnDecodeArgs))
 _sig("pattn_decode", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
@@ -304,9 +305,9 @@ def oproj_residual(o, w_o, h, rows, in_dim, model_dim, x=None, dt=0.1, nonfinite
 # ----------------------------------------------------------- denoise step ----
 
 def pa_stack(num_layers, rows, model_dim, n_q_heads, w_qkv, w_o, eps, scale, dt, num_splits=0, ffn_dim=0,
-             w_gate=None, w_up=None, w_down=None) -> PaStack:
+             w_gate=None, w_up=None, w_down=None, packed=0) -> PaStack:
     st = PaStack(num_layers, rows, model_dim, n_q_heads, ptr(w_qkv), ptr(w_o), eps, scale, dt, num_splits, ffn_dim,
-                 ptr(w_gate), ptr(w_up), ptr(w_down))
+                 ptr(w_gate), ptr(w_up), ptr(w_down), int(packed))
     st._keep = (w_qkv, w_o, w_gate, w_up, w_down)
     return st
 
@@ -319,6 +320,11 @@ def pa_denoise_step(ring: Ring, st: PaStack, x, gamma, gamma_layer_stride: int, 
                     stream=None, gamma_ffn=None):
     _check(_lib.pa_denoise_step(ring.handle, C.byref(st), ptr(x), ptr(gamma), ptr(gamma_ffn), gamma_layer_stride,
                                 ptr(nonfinite), ptr(workspace), ws_bytes, _stream(stream)), "pa_denoise_step")
+
+
+def pa_pack_weight(w, n: int, k: int, w_packed, stream=None):
+    """Rewrite an nn.Linear weight bf16 [n][k] into the fragment-packed order (pa_pack_weight)."""
+    _check(_lib.pa_pack_weight(ptr(w), n, k, ptr(w_packed), _stream(stream)), "pa_pack_weight")
 
 
 def ffn_swiglu_workspace_bytes(rows: int, model_dim: int, ffn_dim: int) -> int:

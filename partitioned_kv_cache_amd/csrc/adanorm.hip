@@ -21,17 +21,13 @@
 
 #include <math.h>
 
-#include "internal.h"
+#include "gemm.h"
 
 namespace pa {
 
 constexpr int MAX_T = 16;            // timesteps per ada_gamma call
 struct TArr { float t[MAX_T]; };
 
-__device__ __forceinline__ float wsum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
 
 __device__ __forceinline__ float bf_round(float v) { return bf2f(f2bf(v)); }
 
@@ -173,15 +169,6 @@ __global__ __launch_bounds__(256) void rmsnorm_rows(const uint16_t* x, const flo
 // bf16(x[m][k] * rsqrt(mean_k x[m]^2 + eps) * gamma[k]), the mean of
 // squares taken in FP32 by the workgroup before the products.
 enum GemmMode { GEMM_QKV = 0, GEMM_OPROJ = 1 };
-constexpr int GEMM_WAVES = 8;
-
-struct GemmOut {
-    // GEMM_QKV: columns [0, nq) -> q, [nq, nq+nk) -> k, [nq+nk, nq+2nk) -> v
-    uint16_t* q; uint16_t* k; uint16_t* v; int nq; int nk;
-    // GEMM_OPROJ: h += C (rounded to bf16); x -= dt * h when x != null
-    uint16_t* h; uint16_t* x; float dt;
-    uint32_t* nonfinite;
-};
 
 // AdaRMSNorm formed on the fly as the A operand of a skinny GEMM over K =
 // GEMM_WAVES * KS * 16: the FP32 mean of squares of every row (wave w takes
@@ -301,37 +288,26 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
     }
     __syncthreads();
     // wave w finishes 4 of the 32 (block, register) pairs
-    bool bad = false;
+    if (MODE == GEMM_QKV) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
-        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int n = n0 + l32;
-        if (m >= rows) continue;
-        float v = 0.f;
+        for (int u = 0; u < 4; ++u) {
+            const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
+            const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const int n = n0 + l32;
+            if (m >= rows) continue;
+            float v = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
-        if (MODE == GEMM_QKV) {
+            for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
             if (n < out.nq)
                 out.q[(long long)m * out.nq + n] = f2bf(v);
             else if (n < out.nq + out.nk)
                 out.k[(long long)m * out.nk + (n - out.nq)] = f2bf(v);
             else
                 out.v[(long long)m * out.nk + (n - out.nq - out.nk)] = f2bf(v);
-        } else {
-            uint16_t* hp = out.h + (long long)m * N + n;
-            const float hn = bf2f(f2bf(bf2f(*hp) + v));
-            *hp = f2bf(hn);
-            bad |= !finite_f(hn);
-            if (out.x) {
-                uint16_t* xp = out.x + (long long)m * N + n;
-                const float xn = bf2f(*xp) - out.dt * hn;
-                bad |= !finite_f(xn);
-                *xp = f2bf(xn);
-            }
         }
+    } else {
+        residual_epilogue(red, n0, rows, N, out);
     }
-    if (MODE == GEMM_OPROJ && out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
 }
 
 // ----------------------------------------------------- FFN with SwiGLU -----
@@ -459,28 +435,7 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_down(const uint16_t* 
         red[wave][1][r][lane] = c1[r];
     }
     __syncthreads();
-    bool bad = false;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
-        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int n = n0 + l32;
-        if (m >= rows) continue;
-        float v = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
-        uint16_t* hp = out.h + (long long)m * N + n;
-        const float hn = bf2f(f2bf(bf2f(*hp) + v));
-        *hp = f2bf(hn);
-        bad |= !finite_f(hn);
-        if (out.x) {
-            uint16_t* xp = out.x + (long long)m * N + n;
-            const float xn = bf2f(*xp) - out.dt * hn;
-            bad |= !finite_f(xn);
-            *xp = f2bf(xn);
-        }
-    }
-    if (out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
+    residual_epilogue(red, n0, rows, N, out);
 }
 
 // K = 128 * KS; the k-step counts the library is built for.

@@ -23,7 +23,7 @@
 
 #include <type_traits>
 
-#include "internal.h"
+#include "gemm.h"
 
 namespace pa {
 
@@ -545,7 +545,9 @@ __device__ __forceinline__ float4 ld4(const uint16_t* p) {
 }
 
 // Merges partial rows [row_lo, row_hi); output row index row - row_lo.
-template <typename TO, int D, typename PO>
+// APK: the output (bf16, one layer) goes to the fragment-packed activation
+// layout of the out-projection's operand (token m < 64, column head * D + d).
+template <typename TO, int D, typename PO, bool APK = false>
 __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int row_lo, int row_hi, int group, int hq,
                                                int hkv, long long out_layer, TO* out) {
     constexpr int DB = D / 32;
@@ -597,6 +599,14 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     if (!ok) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const int r = row - row_lo;
+    if (APK) {
+        const int col = (g * group + r % group) * D + 32 * b + 4 * hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            st4(out + apack_index(r / group, col + 8 * j),
+                make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv));
+        return;
+    }
     TO* orow = out + lb * out_layer + ((long long)(r / group) * hq + g * group + r % group) * D + 32 * b + 4 * hi;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -653,7 +663,6 @@ __global__ __launch_bounds__(256) void append_tail(uint4* __restrict__ tail_k, u
 
 // ================================================================ host side ==
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 struct Plan {
     int group, m_rows, mpad, lg_count, total, chunk, parts, max_parts;
@@ -790,6 +799,9 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
     return PA_OK;
 }
 
+// out_dtype PA_BF16_APACKED: bf16 in the packed activation layout (one layer).
+constexpr int PA_BF16_APACKED = -1;
+
 static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int hq, long long out_layer, void* out,
                                 int out_dtype, const Partials& part, hipStream_t stream, int row_lo = 0,
                                 int row_hi = -1) {
@@ -806,7 +818,22 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
             combine<TO, DD, float><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,    \
                                                              hkv, out_layer, static_cast<TO*>(out));        \
     } while (0)
-    if (out_dtype == PA_F32) {
+#define PA_COMBINE_APK(DD)                                                                                   \
+    do {                                                                                                     \
+        if (p.o_bytes == 2)                                                                                  \
+            combine<uint16_t, DD, uint16_t, true><<<grid, 256, 0, stream>>>(                                 \
+                part, n_parts, row_lo, row_hi, p.group, hq, hkv, out_layer, static_cast<uint16_t*>(out));    \
+        else                                                                                                 \
+            combine<uint16_t, DD, float, true><<<grid, 256, 0, stream>>>(                                    \
+                part, n_parts, row_lo, row_hi, p.group, hq, hkv, out_layer, static_cast<uint16_t*>(out));    \
+    } while (0)
+    if (out_dtype == PA_BF16_APACKED) {
+        if (d == 256) PA_COMBINE_APK(256);
+        else if (d == 128) PA_COMBINE_APK(128);
+        else if (d == 64) PA_COMBINE_APK(64);
+        else if (d == 32) PA_COMBINE_APK(32);
+        else return fail(PA_ESHAPE, "combine: head_dim %d must be 32, 64, 128 or 256", d);
+    } else if (out_dtype == PA_F32) {
         if (d == 256) PA_COMBINE(float, 256);
         else if (d == 128) PA_COMBINE(float, 128);
         else if (d == 64) PA_COMBINE(float, 64);
@@ -820,6 +847,7 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
         else return fail(PA_ESHAPE, "combine: head_dim %d must be 32, 64, 128 or 256", d);
     }
 #undef PA_COMBINE
+#undef PA_COMBINE_APK
     PA_LAUNCHED();
     return PA_OK;
 }
@@ -839,7 +867,7 @@ extern "C" size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* a
 
 static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
                            const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream, void* ev_begin,
-                           void* ev_end) {
+                           void* ev_end, bool apacked = false) {
     clear_error();
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     PA_CHECK_ARG(r && a && q && k_dyn && v_dyn && out && ws, PA_EINVAL, "pattn_step: null argument");
@@ -864,7 +892,16 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
     st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s);
     if (st != PA_OK) return st;
     if (ev_end) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_end), s));
-    return launch_combine(r, p, p.parts, a->n_q_heads, q_layer, out, a->out_dtype, part, s);
+    return launch_combine(r, p, p.parts, a->n_q_heads, q_layer, out, apacked ? PA_BF16_APACKED : a->out_dtype, part,
+                          s);
+}
+
+pa_status pa::pattn_step_apacked(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
+                                 const void* v_dyn, void* out_p, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    PA_CHECK_ARG(a && a->num_layers == 1 && a->n_dyn <= 64 && a->out_dtype == PA_BF16, PA_EINVAL,
+                 "pattn_step (packed output): one layer, at most 64 suffix tokens, bf16 output");
+    return step_impl(ring, a, q, k_dyn, v_dyn, out_p, ws, ws_bytes, stream, nullptr, nullptr, true);
 }
 
 extern "C" pa_status pattn_step(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
@@ -966,7 +1003,7 @@ extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const KvSource src = source_for(r, a->layer_begin, nullptr, nullptr, 0);
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
-    const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
+    const int d = r->cfg.head_dim;
     const long long q_layer = (long long)a->n_streams * a->n_q_heads * d;
     st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s);
     if (st != PA_OK) return st;

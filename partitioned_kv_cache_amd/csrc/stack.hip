@@ -15,7 +15,7 @@
 // allocation, so a caller can capture the whole step in a graph and replay
 // it while frames are pushed into the ring between replays.
 
-#include "internal.h"
+#include "gemm.h"
 
 namespace pa {
 
@@ -36,9 +36,13 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
     w.q = take(n * st->n_q_heads * d * 2);
     w.k = take(n * hkv * d * 2);
     w.v = take(n * hkv * d * 2);
-    w.o = take(n * st->n_q_heads * d * 2);
+    // packed activations always span the 64 row slots of the operand
+    w.o = take((st->packed ? 64 : n) * st->n_q_heads * d * 2);
     w.attn = take(attn_bytes);
-    w.ffn = take(st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0);
+    if (st->packed)
+        w.ffn = take(st->ffn_dim ? (size_t)64 * st->ffn_dim * 2 : 0);
+    else
+        w.ffn = take(st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0);
     w.total = off;
     return w;
 }
@@ -59,6 +63,18 @@ static pa_status check_stack(const Ring* r, const pa_stack* st) {
         PA_CHECK_ARG(st->w_gate && st->w_up && st->w_down, PA_EINVAL, "pa_denoise_step: null FFN weights");
         PA_CHECK_ARG(ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) > 0, PA_ESHAPE,
                      "pa_denoise_step: FFN needs model_dim 128 x {2, 4, 6, 8} and ffn_dim 1024 x {1, 2, 3, 4, 6, 8}");
+    }
+    PA_CHECK_ARG(st->packed == 0 || st->packed == 1, PA_EINVAL, "pa_denoise_step: packed must be 0 or 1");
+    if (st->packed) {
+        PA_CHECK_ARG(packed_norm_supported(st->model_dim), PA_ESHAPE,
+                     "pa_denoise_step: packed weights need model_dim 512 or 1024 (got %d)", st->model_dim);
+        PA_CHECK_ARG(packed_residual_supported(st->n_q_heads * r->cfg.head_dim, st->model_dim), PA_ESHAPE,
+                     "pa_denoise_step: packed weights need Hq * D = 1024 x {1, 2, 3, 4, 6, 8}");
+        PA_CHECK_ARG(!st->ffn_dim || packed_residual_supported(st->ffn_dim, st->model_dim), PA_ESHAPE,
+                     "pa_denoise_step: packed weights need ffn_dim = 1024 x {1, 2, 3, 4, 6, 8}");
+        const void* ws[5] = {st->w_qkv, st->w_o, st->w_gate, st->w_up, st->w_down};
+        for (int i = 0; i < (st->ffn_dim ? 5 : 2); ++i)
+            PA_CHECK_ARG(aligned16(ws[i]), PA_EINVAL, "pa_denoise_step: packed weights must be 16-byte aligned");
     }
     return PA_OK;
 }
@@ -115,6 +131,34 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
     const size_t wo_layer = (size_t)st->model_dim * in_dim;
     const size_t wf_layer = (size_t)st->ffn_dim * st->model_dim;
     const size_t fws_bytes = st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0;
+    if (st->packed) {
+        // Same chain on fragment-packed weights; the attention output and the
+        // SwiGLU activation are written packed by their producers.
+        for (int l = 0; l < st->num_layers; ++l) {
+            const bool last = l + 1 == st->num_layers;
+            const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
+            const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
+            s = packed_norm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq,
+                                st->n_q_heads, hkv, d, q, k, v, nonfinite, strm);
+            if (s != PA_OK) return s;
+            const pattn_args a = attn_args(st, l);
+            s = pattn_step_apacked(ring, &a, q, k, v, o, aws, attn, stream);
+            if (s != PA_OK) return s;
+            s = packed_residual(o, wo, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr,
+                                st->dt, nonfinite, true, strm);
+            if (s != PA_OK) return s;
+            if (st->ffn_dim) {
+                s = packed_norm_gateup(h, st->rows, st->model_dim, st->ffn_dim, gamma_ffn + l * gamma_layer_stride,
+                                       st->eps, static_cast<const uint16_t*>(st->w_gate) + l * wf_layer,
+                                       static_cast<const uint16_t*>(st->w_up) + l * wf_layer, fws, nonfinite, strm);
+                if (s != PA_OK) return s;
+                s = packed_residual(fws, static_cast<const uint16_t*>(st->w_down) + l * wf_layer, h, st->rows,
+                                    st->ffn_dim, st->model_dim, last ? x : nullptr, st->dt, nonfinite, false, strm);
+                if (s != PA_OK) return s;
+            }
+        }
+        return PA_OK;
+    }
     for (int l = 0; l < st->num_layers; ++l) {
         const bool last = l + 1 == st->num_layers;
         const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;

@@ -177,3 +177,38 @@ def test_staging_guards_without_device():
     assert spare.capsule_bytes() == 0 and spare.state()["head"] == 0
     classic.close()
     spare.close()
+
+
+def test_pack_weight_validation_without_device():
+    from partitioned_kv_cache_amd import _lib as L
+    for args, status in [((None, 64, 64, _fake(2)), L.PA_EINVAL), ((_fake(1), 64, 64, _fake(1)), L.PA_EINVAL),
+                         ((_fake(1) + 8, 64, 64, _fake(2)), L.PA_EINVAL), ((_fake(1), 48, 64, _fake(2)), L.PA_ESHAPE),
+                         ((_fake(1), 64, 24, _fake(2)), L.PA_ESHAPE), ((_fake(1), 0, 64, _fake(2)), L.PA_ESHAPE)]:
+        with pytest.raises(L.PattnError) as e:
+            L.pa_pack_weight(*args, stream=0)
+        assert e.value.status == status
+
+
+def test_packed_stack_workspace_and_shape_checks_without_device():
+    from partitioned_kv_cache_amd import _lib as L
+    r = L.Ring(L.rb_config(18, 1, 256, 48, 2, 768, L.PA_BF16), _fake(1), _fake(2))
+    w = [_fake(3 + i) for i in range(5)]
+    full = dict(ffn_dim=4096, w_gate=w[2], w_up=w[3], w_down=w[4])
+    plain = L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 8, w[0], w[1], 1e-6, 1 / 16, 0.1, **full))
+    packed = L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 8, w[0], w[1], 1e-6, 1 / 16, 0.1,
+                                                             packed=1, **full))
+    # packed operands span all 64 row slots: the attention output (Hq D = 2048)
+    # and the SwiGLU activation (4096) each take 13 more rows of bf16
+    up = lambda b: (b + 255) // 256 * 256
+    assert packed - plain == up(64 * 2048 * 2) - up(51 * 2048 * 2) + up(64 * 4096 * 2) - up(51 * 4096 * 2)
+    for kw in (dict(packed=2), dict(packed=1, model_dim=768), dict(packed=1, ffn_dim=5120)):
+        md = kw.pop("model_dim", 1024)
+        f = dict(full, ffn_dim=kw.pop("ffn_dim", 4096))
+        assert L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, md, 8, w[0], w[1], 1e-6, 1 / 16, 0.1,
+                                                               **f, **kw)) == 0
+    # 4 query heads of 256: Hq D = 1024 is a packed size; 3 heads (768) is not
+    assert L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 4, w[0], w[1], 1e-6, 1 / 16, 0.1,
+                                                           packed=1)) > 0
+    assert L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 3, w[0], w[1], 1e-6, 1 / 16, 0.1,
+                                                           packed=1)) == 0
+    r.close()
