@@ -533,16 +533,25 @@ __device__ __forceinline__ void st4(uint16_t* p, float4 v) {
 }
 
 // Splits merged per batch: every load of a batch is issued before the first
-// one is used, so a batch costs one memory round trip.
-constexpr int COMBINE_BATCH = 8;
-
-// Four consecutive partial-O elements as floats.
-__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 ld4(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                       __uint_as_float(u.y & 0xffff0000u));
-}
+// one is used, so a batch costs one memory round trip. bf16 partials are held
+// as raw words until used (two registers per four values), so their batch is
+// twice as long: up to 16 splits in one round trip.
+template <typename PO> struct CombineRaw;
+template <> struct CombineRaw<float> {
+    using T = float4;
+    static constexpr int BATCH = 8;
+    __device__ __forceinline__ static T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ static float4 widen(T v) { return v; }
+};
+template <> struct CombineRaw<uint16_t> {
+    using T = uint2;
+    static constexpr int BATCH = 16;
+    __device__ __forceinline__ static T load(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ static float4 widen(T u) {
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+};
 
 // Merges partial rows [row_lo, row_hi); output row index row - row_lo.
 // APK: the output (bf16, one layer) goes to the fragment-packed activation
@@ -565,33 +574,37 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     float4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < n_parts; s0 += COMBINE_BATCH) {
-        float2 ml[COMBINE_BATCH];
-        float4 v[COMBINE_BATCH][4];
+    using R = CombineRaw<PO>;
+    constexpr int BATCH = R::BATCH;
+    for (int s0 = 0; s0 < n_parts; s0 += BATCH) {
+        float2 ml[BATCH];
+        typename R::T v[BATCH][4];
 #pragma unroll
-        for (int i = 0; i < COMBINE_BATCH; ++i) {
-            const int s = min(s0 + i, n_parts - 1);     // past the end: a valid split, weighed 0 below
-            ml[i] = ok && s0 + i < n_parts ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
+        for (int i = 0; i < BATCH; ++i) {
+            const bool has = s0 + i < n_parts;         // uniform: slots past the end load nothing, weigh 0
+            const int s = has ? s0 + i : 0;
+            ml[i] = ok && has ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
             const PO* op = part.optr<PO>() + part.oblock(s, lg, row0) + (b * 4) * 256 + lane * 4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[i][j] = ld4(op + j * 256);
+            for (int j = 0; j < 4; ++j) v[i][j] = has ? R::load(op + j * 256) : typename R::T{};
         }
         float bm = mx;
 #pragma unroll
-        for (int i = 0; i < COMBINE_BATCH; ++i) bm = fmaxf(bm, ml[i].x);
+        for (int i = 0; i < BATCH; ++i) bm = fmaxf(bm, ml[i].x);
         if (bm == -INFINITY) continue;                  // nothing non-empty yet
         const float sc = exp2f(mx - bm);                // 0 while mx is -inf
         lsum *= sc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) { acc[j].x *= sc; acc[j].y *= sc; acc[j].z *= sc; acc[j].w *= sc; }
 #pragma unroll
-        for (int i = 0; i < COMBINE_BATCH; ++i) {
+        for (int i = 0; i < BATCH; ++i) {
             const float w = ml[i].x == -INFINITY ? 0.f : exp2f(ml[i].x - bm);   // an empty partial weighs 0
             lsum += w * ml[i].y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                acc[j].x += w * v[i][j].x; acc[j].y += w * v[i][j].y;
-                acc[j].z += w * v[i][j].z; acc[j].w += w * v[i][j].w;
+                const float4 vv = R::widen(v[i][j]);
+                acc[j].x += w * vv.x; acc[j].y += w * vv.y;
+                acc[j].z += w * vv.z; acc[j].w += w * vv.w;
             }
         }
         mx = bm;
@@ -677,7 +690,7 @@ static int valu_row_blocks(int m) { return (m + VALU_ROWS - 1) / VALU_ROWS; }
 static int default_splits(int lg_count, int row_blocks, int max_keys) {
     const int base = lg_count * row_blocks;
     int s = 256 * MFMA_OCC / base;
-    int by_len = max_keys / 128;
+    int by_len = max_keys / 96;    // at least three 32-key tiles per split
     if (by_len < 1) by_len = 1;
     if (s > by_len) s = by_len;
     if (s > 64) s = 64;
