@@ -7,10 +7,35 @@
 
 namespace pa {
 
+// Sum over the 64 lanes of a wave, the same value in every lane. Partners at
+// lane distance 1, 2 (quad permutes), 4 (half-row mirror), 8 (row mirror),
+// 16 (a swizzled shuffle) and 32 (permlane32 swap): vector ALU steps, except
+// the one at 16, instead of six LDS permutes. Each step adds the same pair in
+// every lane of the pair, so all lanes end with bit-identical sums.
 __device__ __forceinline__ float wsum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+#define PA_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false))
+    v += PA_DPP(v, 0xB1);    // quad_perm [1, 0, 3, 2]
+    v += PA_DPP(v, 0x4E);    // quad_perm [2, 3, 0, 1]
+    v += PA_DPP(v, 0x141);   // row_half_mirror
+    v += PA_DPP(v, 0x140);   // row_mirror
+#undef PA_DPP
+    v += __shfl_xor(v, 16);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
+
+// Two floats to packed bf16 words (round to nearest even), low word first.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
+}
+
+// Non-finite test on two packed bf16 words: an all-ones exponent (0x7F80)
+// carries into the word's top bit when 0x80 is added to the masked exponent,
+// and no other exponent does. OR the results; test with nonfinite_seen().
+__device__ __forceinline__ uint32_t nonfinite_bits(uint32_t w) { return (w & 0x7F807F80u) + 0x00800080u; }
+__device__ __forceinline__ bool nonfinite_seen(uint32_t acc) { return (acc & 0x80008000u) != 0; }
 
 constexpr int GEMM_WAVES = 8;
 

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
     constexpr int SMEM = 64 * XS * 2 > RED ? 64 * XS * 2 : RED;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: row choices are scalar branches
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int nb = blockIdx.x, n0 = nb * 32;
 
     // this wave's weight blocks: KS consecutive 1 KB blocks
@@ -81,10 +82,16 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
             raw[rr][c] = r < rows ? *reinterpret_cast<const uint4*>(x + (long long)r * K + c * 512 + lane * 8)
                                   : make_uint4(0, 0, 0, 0);
     }
-    bool bad = false;
+    uint32_t bad = 0;                  // nonfinite_bits of every rounded operand, as the MFMA sees it
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
-        const int r = wave + rr * GEMM_WAVES;
+        const int r = wave + rr * GEMM_WAVES;          // wave-uniform
+        if (r >= rows) {                               // padding rows are zeros
+#pragma unroll
+            for (int c = 0; c < LPR; ++c)
+                *reinterpret_cast<uint4*>(xs + r * XS + c * 512 + lane * 8) = make_uint4(0, 0, 0, 0);
+            continue;
+        }
         float ss = 0.f;
 #pragma unroll
         for (int c = 0; c < LPR; ++c) {
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
             }
         }
         ss = wsum(ss);
-        const float rinv = r < rows ? 1.f / sqrtf(ss / (float)K + eps) : 0.f;
+        const float rinv = 1.f / sqrtf(ss / (float)K + eps);
 #pragma unroll
         for (int c = 0; c < LPR; ++c) {
             const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][c]);
@@ -104,15 +111,13 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
             uint32_t pk[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint16_t b0 = f2bf(bf2f(e[2 * u]) * rinv * gg[2 * u]);
-                const uint16_t b1 = f2bf(bf2f(e[2 * u + 1]) * rinv * gg[2 * u + 1]);
-                bad |= !finite_f(bf2f(b0)) || !finite_f(bf2f(b1));   // the rounded operand, as the MFMA sees it
-                pk[u] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+                pk[u] = pack2_bf16(bf2f(e[2 * u]) * rinv * gg[2 * u], bf2f(e[2 * u + 1]) * rinv * gg[2 * u + 1]);
+                bad |= nonfinite_bits(pk[u]);
             }
             *reinterpret_cast<uint4*>(xs + r * XS + c * 512 + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
     }
-    if (blockIdx.x == 0 && out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
+    if (blockIdx.x == 0 && out.nonfinite && __any(nonfinite_seen(bad)) && lane == 0) atomicOr(out.nonfinite, 1u);
     __syncthreads();
     const int k0 = wave * KS * 16 + 8 * hi;
     bf16x8 a0[KS], a1[KS];
