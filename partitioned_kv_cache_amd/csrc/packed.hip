@@ -55,15 +55,6 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
     const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int nb = blockIdx.x, n0 = nb * 32;
 
-    // this wave's weight blocks: KS consecutive 1 KB blocks
-    bf16x8 w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
-    const long long wb = ((long long)nb * S + wave * KS) * 512 + lane * 8;
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-        w1[i] = *reinterpret_cast<const bf16x8*>(wp1 + wb + i * 512);
-        if (MODE == PK_GATEUP) w2[i] = *reinterpret_cast<const bf16x8*>(wp2 + wb + i * 512);
-    }
-
     // normalise rows w, w + 8, ... into LDS (rows >= `rows` are zeros)
     static_assert(K % 512 == 0, "rows are staged in 1 KB pieces");
     float4 g[LPR][2];
@@ -82,6 +73,18 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
             raw[rr][c] = r < rows ? *reinterpret_cast<const uint4*>(x + (long long)r * K + c * 512 + lane * 8)
                                   : make_uint4(0, 0, 0, 0);
     }
+    // Then this wave's weight blocks (KS consecutive 1 KB blocks): issued after
+    // x, so the normalisation waits only for x (loads return in issue order)
+    // while the weights stream in.
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
+    const long long wb = ((long long)nb * S + wave * KS) * 512 + lane * 8;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        w1[i] = *reinterpret_cast<const bf16x8*>(wp1 + wb + i * 512);
+        if (MODE == PK_GATEUP) w2[i] = *reinterpret_cast<const bf16x8*>(wp2 + wb + i * 512);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t bad = 0;                  // nonfinite_bits of every rounded operand, as the MFMA sees it
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
