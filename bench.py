@@ -46,6 +46,49 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class KernelEvents:
+    """HIP timing events created without the system-scope fence
+    (hipEventDisableSystemFence), from the HIP runtime torch has loaded.
+    A default timing event writes back and invalidates the caches when it is
+    recorded: around the partial kernel that adds the write-back of its
+    27 MB of partials and a cold start to the measurement. These events time
+    the launch as it runs between unmarked steps."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes as C
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.C, self.hip = C, C.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.made = []
+
+    def pair(self):
+        evs = []
+        for _ in range(2):
+            ev = self.C.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(self.C.byref(ev), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            evs.append(ev.value)
+            self.made.append(ev.value)
+        return tuple(evs)
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.C.c_float()
+        rc = self.hip.hipEventElapsedTime(self.C.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ev)
+        self.made = []
+
+
 def attention_work(s, cached_tokens):
     """Algorithmic bytes and flops of one partial-kernel launch over all layers.
 
@@ -102,28 +145,25 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1):
         if ev is None:
             L.pattn_step(rings[r], args_, q, kd, vd, out, ws, wsb, stream)
         else:
-            L.pattn_step_timed(rings[r], args_, q, kd, vd, out, ws, wsb, stream, ev[0].cuda_event, ev[1].cuda_event)
+            L.pattn_step_timed(rings[r], args_, q, kd, vd, out, ws, wsb, stream, ev[0], ev[1])
 
     for i in range(args.warmup):
         one_step(i)
     # The partial kernel is timed on one step of every frame (the middle
-    # one): an event pair on every launch would add several microseconds of
-    # dispatch latency to every step of the timed loop.
+    # one): an event pair on every launch would add dispatch latency to every
+    # step of the timed loop.
     half = s.steps_per_frame // 2
     sampled = [i for i in range(args.steps) if ((args.warmup + i) // n_rings) % s.steps_per_frame == half]
-    events = {}
-    for i in sampled:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        b.record(stream)        # creates the events; the library re-records them
-        events[i] = (a, b)
+    kev = KernelEvents()
+    events = {i: kev.pair() for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         one_step(args.warmup + i, events.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in events.values()]
+    kern_ms = [kev.elapsed_ms(a, b) for a, b in events.values()]
+    kev.close()
     avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
     cached = s.pin_tokens + s.num_slots * s.tokens_per_frame
     algo_bytes, flops, kv_bytes = attention_work(s, cached)
