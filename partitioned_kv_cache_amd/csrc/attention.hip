@@ -345,7 +345,11 @@ __device__ __forceinline__ void wait_vmem() {
 // FUSED: rows [0, m1) are the action suffix's (queries from q, keys
 // [pin | window | suffix]); rows [m1, m_rows) are decode streams' (queries
 // from q2, keys [pin | window] only: the suffix keys are masked for them).
-template <int D, bool FUSED = false>
+// QPK: q is already in the B-operand order of the S = K Q^T product,
+// [call layer x KV head][32-row block][D / 16][64 lanes][8] (rows padded to
+// whole blocks), so each Q load is 1 KB contiguous across the wave instead of
+// 32 B from each of 32 rows. The stack's QKV projection writes it that way.
+template <int D, bool FUSED = false, bool QPK = false>
 __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
                                                                           long long q_layer, int hq, int group,
                                                                           int m_rows, KvSource src, int chunk,
@@ -376,7 +380,12 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     const bool active = row0 < m_rows;       // wave-uniform
 
     bf16x8 qf[KD];
-    if (row < m_rows) {
+    if (QPK) {
+        static_assert(!(QPK && FUSED), "packed Q is for the single-reader step");
+        const uint16_t* qp = q + ((long long)(lg * (part.mpad >> 5) + (row0 >> 5)) * KD) * 512 + lane * 8;
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) qf[kk] = active ? *reinterpret_cast<const bf16x8*>(qp + kk * 512) : bf16x8{};
+    } else if (row < m_rows) {
         const bool second = FUSED && row >= m1;
         const int r = second ? row - m1 : row;
         const uint16_t* qp = (second ? q2 + lb * q2_layer : q + lb * q_layer) +
@@ -773,7 +782,8 @@ static KvSource source_for(const Ring* r, int layer_begin, const void* k_dyn, co
 
 static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, long long q_layer, int hq,
                                  const KvSource& src, float scale, const Partials& part, hipStream_t stream,
-                                 const void* q2 = nullptr, long long q2_layer = 0, int m1 = 0) {
+                                 const void* q2 = nullptr, long long q2_layer = 0, int m1 = 0,
+                                 bool q_packed = false) {
     if (p.parts == 0) return PA_OK;
     const float scale_log2 = scale * 1.4426950408889634f;
     const int d = r->cfg.head_dim;
@@ -783,18 +793,22 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
         const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         const uint16_t* qq2 = static_cast<const uint16_t*>(q2);
-#define PA_MFMA(DD, FU)                                                                                       \
-    partial_mfma<DD, FU><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
-                                                               scale_log2, part, p.parts, row_blocks, qq2,       \
-                                                               q2_layer, m1)
-        if (q2) {
-            if (d == 256) PA_MFMA(256, true);
-            else if (d == 128) PA_MFMA(128, true);
-            else PA_MFMA(64, true);
+#define PA_MFMA(DD, FU, QP)                                                                                      \
+    partial_mfma<DD, FU, QP><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
+                                                                   scale_log2, part, p.parts, row_blocks, qq2,       \
+                                                                   q2_layer, m1)
+        if (q_packed) {
+            if (d == 256) PA_MFMA(256, false, true);
+            else if (d == 128) PA_MFMA(128, false, true);
+            else PA_MFMA(64, false, true);
+        } else if (q2) {
+            if (d == 256) PA_MFMA(256, true, false);
+            else if (d == 128) PA_MFMA(128, true, false);
+            else PA_MFMA(64, true, false);
         } else {
-            if (d == 256) PA_MFMA(256, false);
-            else if (d == 128) PA_MFMA(128, false);
-            else PA_MFMA(64, false);
+            if (d == 256) PA_MFMA(256, false, false);
+            else if (d == 128) PA_MFMA(128, false, false);
+            else PA_MFMA(64, false, false);
         }
 #undef PA_MFMA
     } else {
@@ -880,7 +894,7 @@ extern "C" size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* a
 
 static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
                            const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream, void* ev_begin,
-                           void* ev_end, bool apacked = false) {
+                           void* ev_end, bool apacked = false, bool q_packed = false) {
     clear_error();
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     PA_CHECK_ARG(r && a && q && k_dyn && v_dyn && out && ws, PA_EINVAL, "pattn_step: null argument");
@@ -902,7 +916,7 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
     const long long q_layer = (long long)a->n_dyn * a->n_q_heads * r->cfg.head_dim;
     if (ev_begin) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_begin), s));
-    st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s);
+    st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s, nullptr, 0, 0, q_packed);
     if (st != PA_OK) return st;
     if (ev_end) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_end), s));
     return launch_combine(r, p, p.parts, a->n_q_heads, q_layer, out, apacked ? PA_BF16_APACKED : a->out_dtype, part,
@@ -910,11 +924,14 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
 }
 
 pa_status pa::pattn_step_apacked(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
-                                 const void* v_dyn, void* out_p, void* ws, size_t ws_bytes, void* stream) {
+                                 const void* v_dyn, void* out_p, void* ws, size_t ws_bytes, void* stream,
+                                 bool q_packed) {
     clear_error();
     PA_CHECK_ARG(a && a->num_layers == 1 && a->n_dyn <= 64 && a->out_dtype == PA_BF16, PA_EINVAL,
                  "pattn_step (packed output): one layer, at most 64 suffix tokens, bf16 output");
-    return step_impl(ring, a, q, k_dyn, v_dyn, out_p, ws, ws_bytes, stream, nullptr, nullptr, true);
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    PA_CHECK_ARG(!q_packed || (r && r->cfg.dtype == PA_BF16), PA_EINVAL, "pattn_step (packed Q): bf16 rings only");
+    return step_impl(ring, a, q, k_dyn, v_dyn, out_p, ws, ws_bytes, stream, nullptr, nullptr, true, q_packed);
 }
 
 extern "C" pa_status pattn_step(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,

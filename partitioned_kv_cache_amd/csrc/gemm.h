@@ -42,6 +42,9 @@ constexpr int GEMM_WAVES = 8;
 struct GemmOut {
     // GEMM_QKV: columns [0, nq) -> q, [nq, nq+nk) -> k, [nq+nk, nq+2nk) -> v
     uint16_t* q; uint16_t* k; uint16_t* v; int nq; int nk;
+    // q_nrb > 0: q goes to the attention kernel's B-operand order (qpack_index),
+    // q_nrb 32-row blocks per KV head, q_group query heads per KV head, head dim q_d
+    int q_nrb, q_group, q_d;
     // GEMM_OPROJ: h += C (rounded to bf16); x -= dt * h when x != null
     uint16_t* h; uint16_t* x; float dt;
     uint32_t* nonfinite;
@@ -95,14 +98,23 @@ __device__ __forceinline__ void residual_epilogue(const float (&red)[GEMM_WAVES]
 __host__ __device__ inline long long wpack_index(int n, int k, int K) {
     return (((long long)(n >> 5) * (K >> 4) + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 + (n & 31)) * 8 + (k & 7);
 }
+// Query (token m, head h, dim d) in the attention kernel's Q operand order:
+// row r = m * group + h % group of KV head g = h / group, in 32-row blocks.
+__host__ __device__ inline long long qpack_index(int m, int h, int d, int group, int nrb, int D) {
+    const int g = h / group, r = m * group + h % group;
+    return ((((long long)g * nrb + (r >> 5)) * (D >> 4) + (d >> 4)) * 64 + ((d >> 3) & 1) * 32 + (r & 31)) * 8 + (d & 7);
+}
 __host__ __device__ inline long long apack_index(int m, int k) {
     return (((long long)(k >> 4) * 2 + (m >> 5)) * 64 + ((k >> 3) & 1) * 32 + (m & 31)) * 8 + (k & 7);
 }
 
 // Stack-internal GEMMs on packed operands (rows <= 64).
-//   q|k|v = bf16(AdaRMSNorm(x, gamma)) W_qkv^T           (W_qkv packed)
+//   q|k|v = bf16(AdaRMSNorm(x, gamma)) W_qkv^T           (W_qkv packed; q in operand order when q_packed)
 pa_status packed_norm_qkv(const void* x, int rows, int model_dim, const float* gamma, float eps, const void* w_qkv_p,
-                          int hq, int hkv, int d, void* q, void* k, void* v, uint32_t* nonfinite, hipStream_t s);
+                          int hq, int hkv, int d, void* q, void* k, void* v, uint32_t* nonfinite, bool q_packed,
+                          hipStream_t s);
+// 32-row blocks per KV head of the packed Q of `rows` tokens
+inline int qpack_blocks(int rows, int hq, int hkv) { return (rows * (hq / hkv) + 31) / 32; }
 //   act_p = packed bf16(SiLU(y W_gate^T) * (y W_up^T)), y = bf16(AdaRMSNorm(h, gamma))
 pa_status packed_norm_gateup(const void* h, int rows, int model_dim, int ffn_dim, const float* gamma, float eps,
                              const void* w_gate_p, const void* w_up_p, void* act_p, uint32_t* nonfinite,
@@ -115,8 +127,10 @@ bool packed_residual_supported(int K, int N);
 bool packed_norm_supported(int model_dim);
 
 // pattn_step writing its bf16 output in the packed activation layout
-// [K = Hq * D] for the out-projection (rows = suffix tokens <= 64).
+// [K = Hq * D] for the out-projection (rows = suffix tokens <= 64); with
+// q_packed, q is in the attention kernel's operand order (qpack_index).
 pa_status pattn_step_apacked(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
-                             const void* v_dyn, void* out_p, void* ws, size_t ws_bytes, void* stream);
+                             const void* v_dyn, void* out_p, void* ws, size_t ws_bytes, void* stream,
+                             bool q_packed);
 
 }  // namespace pa

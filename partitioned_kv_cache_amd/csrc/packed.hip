@@ -171,6 +171,14 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
         const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
         const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
         const int n = n0 + l32;
+        if (MODE == PK_QKV && out.q_nrb && n < out.nq) {
+            // packed q: the padding rows of its last 32-row block are written
+            // too (they are zero rows of the product)
+            const int h = n / out.q_d;
+            if (m * out.q_group + h % out.q_group < out.q_nrb * 32)
+                out.q[qpack_index(m, h, n % out.q_d, out.q_group, out.q_nrb, out.q_d)] = f2bf(cs[u]);
+            continue;
+        }
         if (m >= rows) continue;
         if (MODE == PK_QKV) {
             const float v = cs[u];
@@ -249,8 +257,14 @@ bool packed_residual_supported(int K, int N) {
 }
 
 pa_status packed_norm_qkv(const void* x, int rows, int model_dim, const float* gamma, float eps, const void* w_p,
-                          int hq, int hkv, int d, void* q, void* k, void* v, uint32_t* nonfinite, hipStream_t s) {
+                          int hq, int hkv, int d, void* q, void* k, void* v, uint32_t* nonfinite, bool q_packed,
+                          hipStream_t s) {
     GemmOut o{};
+    if (q_packed) {
+        o.q_nrb = qpack_blocks(rows, hq, hkv);
+        o.q_group = hq / hkv;
+        o.q_d = d;
+    }
     o.q = static_cast<uint16_t*>(q);
     o.k = static_cast<uint16_t*>(k);
     o.v = static_cast<uint16_t*>(v);

@@ -33,7 +33,9 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
         return at;
     };
     w.h = take(n * m * 2);
-    w.q = take(n * st->n_q_heads * d * 2);
+    // packed Q (operand order) pads each KV head's rows to whole 32-row blocks
+    const size_t qpk = st->packed ? (size_t)qpack_blocks(st->rows, st->n_q_heads, (int)hkv) * 32 * hkv * d : 0;
+    w.q = take((qpk > n * st->n_q_heads * d ? qpk : n * st->n_q_heads * d) * 2);
     w.k = take(n * hkv * d * 2);
     w.v = take(n * hkv * d * 2);
     // packed activations always span the 64 row slots of the operand
@@ -139,10 +141,10 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
             const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
             const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
             s = packed_norm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq,
-                                st->n_q_heads, hkv, d, q, k, v, nonfinite, strm);
+                                st->n_q_heads, hkv, d, q, k, v, nonfinite, true, strm);
             if (s != PA_OK) return s;
             const pattn_args a = attn_args(st, l);
-            s = pattn_step_apacked(ring, &a, q, k, v, o, aws, attn, stream);
+            s = pattn_step_apacked(ring, &a, q, k, v, o, aws, attn, stream, true);
             if (s != PA_OK) return s;
             s = packed_residual(o, wo, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr,
                                 st->dt, nonfinite, true, strm);

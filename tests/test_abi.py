@@ -198,9 +198,11 @@ def test_packed_stack_workspace_and_shape_checks_without_device():
     packed = L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 8, w[0], w[1], 1e-6, 1 / 16, 0.1,
                                                              packed=1, **full))
     # packed operands span all 64 row slots: the attention output (Hq D = 2048)
-    # and the SwiGLU activation (4096) each take 13 more rows of bf16
+    # and the SwiGLU activation (4096) each take 13 more rows of bf16; packed Q
+    # pads 51 x 8 = 408 query rows to 13 blocks of 32 (416 rows of D = 256)
     up = lambda b: (b + 255) // 256 * 256
-    assert packed - plain == up(64 * 2048 * 2) - up(51 * 2048 * 2) + up(64 * 4096 * 2) - up(51 * 4096 * 2)
+    assert packed - plain == (up(64 * 2048 * 2) - up(51 * 2048 * 2) + up(64 * 4096 * 2) - up(51 * 4096 * 2)
+                              + up(416 * 256 * 2) - up(408 * 256 * 2))
     for kw in (dict(packed=2), dict(packed=1, model_dim=768), dict(packed=1, ffn_dim=5120)):
         md = kw.pop("model_dim", 1024)
         f = dict(full, ffn_dim=kw.pop("ffn_dim", 4096))
