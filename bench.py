@@ -105,7 +105,7 @@ def attention_work(s, cached_tokens):
     return kv_cached + q_bytes + dyn, flops, kv_cached
 
 
-def bench_long_history(args, torch, L, configs, synth, n_rings=1):
+def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0):
     """The headline step. With n_rings > 1, that many independent rings (one
     per session) are served round-robin, one step each in turn; three rings
     hold 354 MB of K/V, more than the 256 MB last-level cache (MALL), so
@@ -129,7 +129,15 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1):
             ring.push_frame(*pool[(f + r) % 4])
         rings.append(ring)
         bufs.append((k_buf, v_buf))
-    args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits)
+    args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits, q_layout)
+    if q_layout == L.PA_Q_OPERAND:
+        # Q in the kernel's operand order, as a producer that writes Q (the
+        # stack's QKV projection) lays it out; converted once, before timing
+        def operand(q):
+            qo = torch.empty(L.pattn_operand_q_bytes(rings[0], args_) // 2, dtype=torch.int16, device="cuda")
+            L.pattn_pack_q(rings[0], args_, q, qo)
+            return qo
+        steps_in = [(operand(q), kd, vd) for q, kd, vd in steps_in]
     wsb = L.pattn_workspace_bytes(rings[0], args_)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
@@ -180,6 +188,7 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1):
         "flops": flops,
         "splits": args.splits,
         "rings": n_rings,
+        "q_layout": "operand" if q_layout else "token_major",
     }
     for ring in rings:
         ring.close()
@@ -650,6 +659,9 @@ def main():
     lh = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings)
     log(f"long history, cold MALL ({args.cold_rings} rings): {lh['steps_per_s']:.1f} steps/s, partial kernel "
         f"{lh['partial_us']:.1f} us ({lh['partial_tflops']:.0f} TFLOP/s, {lh['partial_gbs']:.0f} GB/s)")
+    lh_op = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings, q_layout=L.PA_Q_OPERAND)
+    log(f"long history, cold MALL, Q in operand order: {lh_op['steps_per_s']:.1f} steps/s, partial kernel "
+        f"{lh_op['partial_us']:.1f} us")
     warm = small = async_push = None
     if not args.headline_only:
         warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
@@ -704,6 +716,12 @@ def main():
                 "frac": round(lh["partial_gbs"] / HBM_PEAK_GBS, 4),
                 "kv_stream_gbs_whole_step": round(lh["kv_gbs_step"], 1)},
         "cpu_baseline": cpu,
+        # the same cold step with Q already in the kernel's operand order
+        # (PA_Q_OPERAND): what a producer that writes Q in that order gets
+        "cold_q_operand_order": {"steps_per_s": lh_op["steps_per_s"], "ms_per_step": lh_op["ms_per_step"],
+                                 "partial_us": round(lh_op["partial_us"], 3),
+                                 "partial_tflops": round(lh_op["partial_tflops"], 2),
+                                 "frac": round(lh_op["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
     if warm is not None:
         line["warm_mall"] = {"rings": 1, "steps_per_s": warm["steps_per_s"], "ms_per_step": warm["ms_per_step"],

@@ -175,12 +175,36 @@ typedef struct {
     float   scale;             /* the 1/sqrt(d) of Eq. 1, applied once */
     int32_t out_dtype;         /* PA_F32 or PA_BF16 */
     int32_t num_splits;        /* KV splits per layer, 0..127; 0 = library's choice */
+    int32_t q_layout;          /* PA_Q_TOKEN_MAJOR or PA_Q_OPERAND (bf16 rings) */
 } pattn_args;
+
+/* Layouts of q for pattn_step / pattn_step_timed.
+ * PA_Q_TOKEN_MAJOR: [Lb][N][Hq][D], the pages' layout.
+ * PA_Q_OPERAND: the order in which the matrix-core kernel consumes Q. Query
+ *   row r of KV head g is (token r / G, head g*G + r % G), G = Hq / Hkv; rows
+ *   come in blocks of 32 (padded, nb = ceil(N*G / 32) blocks), and within a
+ *   block the 16-dim step s holds 64 lanes x 8 dims, lane = 32 * ((d / 8) % 2)
+ *   + r % 32. Element (row r, dim d) of call layer l, KV head g sits at
+ *     ((((l*Hkv + g)*nb + r/32)*(D/16) + d/16)*64 + ((d/8)%2)*32 + r%32)*8 + d%8.
+ *   Every wave load of Q is then 1 KB contiguous instead of 32 B from each of
+ *   32 rows; a producer that writes Q (the stack's QKV projection does) can
+ *   write this order at no cost. Padding rows must hold finite values (zeros
+ *   from pattn_pack_q). bf16 rings only; pattn_fused_step and pattn_decode
+ *   take token-major queries. */
+#define PA_Q_TOKEN_MAJOR 0
+#define PA_Q_OPERAND 1
 
 /* Workspace needed by pattn_step for these arguments (0 on invalid input). */
 size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* args);
 
-/* q     [Lb][N][Hq][D]    ring dtype
+/* Bytes of q in PA_Q_OPERAND order for these arguments (0 on invalid input
+ * or an f32 ring), and the conversion from token-major q (device buffers,
+ * 16-byte aligned, not overlapping; asynchronous on `stream`). */
+size_t pattn_operand_q_bytes(const rb_ring* ring, const pattn_args* args);
+pa_status pattn_pack_q(const rb_ring* ring, const pattn_args* args, const void* q, void* q_operand,
+                       void* stream);
+
+/* q     [Lb][N][Hq][D]    ring dtype (or PA_Q_OPERAND order, args->q_layout)
  * k_dyn [Lb][N][Hkv][D]   ring dtype: K_dyn(k) of this step
  * v_dyn [Lb][N][Hkv][D]   ring dtype
  * out   [Lb][N][Hq][D]    args->out_dtype

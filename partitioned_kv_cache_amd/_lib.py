@@ -27,6 +27,7 @@ _lib = C.CDLL(LIB_PATH)
 
 PA_OK, PA_EINVAL, PA_ESHAPE, PA_ESTATE, PA_EDEVICE, PA_ERANGE = range(6)
 PA_F32, PA_BF16 = 0, 1
+PA_Q_TOKEN_MAJOR, PA_Q_OPERAND = 0, 1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_ESHAPE", 3: "PA_ESTATE", 4: "PA_EDEVICE", 5: "PA_ERANGE"}
 
 # every symbol the header declares
@@ -37,7 +38,7 @@ EXPORTS = (
     "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
     "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
     "rb_stage_frame", "rb_commit_frame", "ffn_swiglu_workspace_bytes", "ffn_swiglu", "pattn_fused_workspace_bytes",
-    "pattn_fused_step", "pa_pack_weight",
+    "pattn_fused_step", "pa_pack_weight", "pattn_operand_q_bytes", "pattn_pack_q",
 )
 
 
@@ -61,7 +62,8 @@ class RbState(C.Structure):
 
 class PattnArgs(C.Structure):
     _fields_ = [("layer_begin", C.c_int32), ("num_layers", C.c_int32), ("n_q_heads", C.c_int32),
-                ("n_dyn", C.c_int32), ("scale", C.c_float), ("out_dtype", C.c_int32), ("num_splits", C.c_int32)]
+                ("n_dyn", C.c_int32), ("scale", C.c_float), ("out_dtype", C.c_int32), ("num_splits", C.c_int32),
+                ("q_layout", C.c_int32)]
 
 
 class PattnDecodeArgs(C.Structure):
@@ -111,6 +113,8 @@ _sig("pa_denoise_step", _i32, _vp, C.POINTER(PaStack), _vp, _vp, _vp, C.c_int64,
 _sig("ffn_swiglu_workspace_bytes", _sz, _i32, _i32, _i32)
 _sig("ffn_swiglu", _i32, _vp, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp)
 _sig("pa_pack_weight", _i32, _vp, _i32, _i32, _vp, _vp)
+_sig("pattn_operand_q_bytes", _sz, _vp, C.POINTER(PattnArgs))
+_sig("pattn_pack_q", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp)
 _sig("pattn_append_private", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _sig("pattn_decode_workspace_bytes", _sz, _vp, C.POINTER(PattnDecodeArgs))
 _sig("pattn_decode", _i32, _vp, C.POINTER(PattnDecodeArgs), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
@@ -216,8 +220,18 @@ def rb_config(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, token
 
 # ------------------------------------------------------------ attention ------
 
-def pattn_args(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype=PA_F32, num_splits=0) -> PattnArgs:
-    return PattnArgs(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype, num_splits)
+def pattn_args(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype=PA_F32, num_splits=0,
+               q_layout=0) -> PattnArgs:
+    return PattnArgs(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype, num_splits, q_layout)
+
+
+def pattn_operand_q_bytes(ring: Ring, args: PattnArgs) -> int:
+    return _lib.pattn_operand_q_bytes(ring.handle, C.byref(args))
+
+
+def pattn_pack_q(ring: Ring, args: PattnArgs, q, q_operand, stream=None):
+    """Token-major q -> the PA_Q_OPERAND order pattn_step reads with q_layout = PA_Q_OPERAND."""
+    _check(_lib.pattn_pack_q(ring.handle, C.byref(args), ptr(q), ptr(q_operand), _stream(stream)), "pattn_pack_q")
 
 
 def pattn_workspace_bytes(ring: Ring, args: PattnArgs) -> int:

@@ -780,6 +780,30 @@ static KvSource source_for(const Ring* r, int layer_begin, const void* k_dyn, co
     return s;
 }
 
+// Token-major q [Lb][N][Hq][D] (bf16) into the matrix-core kernel's operand
+// order (PA_Q_OPERAND): one thread per 16-byte chunk of the output; padding
+// rows of the last 32-row block are zeros.
+__global__ __launch_bounds__(256) void pack_q(const uint4* __restrict__ q, uint4* __restrict__ qo, int n_tok, int hq,
+                                              int hkv, int d, int nrb, long long chunks) {
+    const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    const int lane = (int)(c & 63), kd = d >> 4, group = hq / hkv;
+    long long blk = c >> 6;
+    const int kk = (int)(blk % kd);
+    blk /= kd;
+    const int rb = (int)(blk % nrb);
+    const long long lg = blk / nrb;
+    const long long lb = lg / hkv;
+    const int g = (int)(lg % hkv);
+    const int r = rb * 32 + (lane & 31), d0 = kk * 16 + (lane >> 5) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < n_tok * group) {
+        const int t = r / group, h = g * group + r % group;
+        v = q[((lb * n_tok + t) * hq + h) * (d >> 3) + (d0 >> 3)];
+    }
+    qo[c] = v;
+}
+
 static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, long long q_layer, int hq,
                                  const KvSource& src, float scale, const Partials& part, hipStream_t stream,
                                  const void* q2 = nullptr, long long q2_layer = 0, int m1 = 0,
@@ -902,6 +926,8 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
                      aligned16(r->k) && aligned16(r->v),
                  PA_EINVAL, "pattn_step: every buffer must be 16-byte aligned");
     PA_CHECK_ARG(a->out_dtype == PA_F32 || a->out_dtype == PA_BF16, PA_EINVAL, "pattn_step: bad out_dtype");
+    PA_CHECK_ARG(a->q_layout == PA_Q_TOKEN_MAJOR || (a->q_layout == PA_Q_OPERAND && r->cfg.dtype == PA_BF16),
+                 PA_EINVAL, "pattn_step: q_layout must be PA_Q_TOKEN_MAJOR, or PA_Q_OPERAND on a bf16 ring");
     PA_CHECK_ARG(a->scale > 0.f && a->scale < 1e30f, PA_EINVAL, "pattn_step: scale must be positive and finite");
     PA_CHECK_ARG(a->n_dyn >= 1, PA_ESHAPE, "pattn_step: n_dyn must be >= 1");
     Plan p;
@@ -916,7 +942,8 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
     const long long q_layer = (long long)a->n_dyn * a->n_q_heads * r->cfg.head_dim;
     if (ev_begin) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_begin), s));
-    st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s, nullptr, 0, 0, q_packed);
+    st = launch_partials(r, p, q, q_layer, a->n_q_heads, src, a->scale, part, s, nullptr, 0, 0,
+                         q_packed || a->q_layout == PA_Q_OPERAND);
     if (st != PA_OK) return st;
     if (ev_end) PA_HIP(hipEventRecord(static_cast<hipEvent_t>(ev_end), s));
     return launch_combine(r, p, p.parts, a->n_q_heads, q_layer, out, apacked ? PA_BF16_APACKED : a->out_dtype, part,
@@ -943,6 +970,40 @@ extern "C" pa_status pattn_step_timed(const rb_ring* ring, const pattn_args* a, 
                                       const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream,
                                       void* ev_begin, void* ev_end) {
     return step_impl(ring, a, q, k_dyn, v_dyn, out, ws, ws_bytes, stream, ev_begin, ev_end);
+}
+
+// Chunks of 16 bytes in the PA_Q_OPERAND form of q, 0 if not applicable.
+static long long operand_q_chunks(const Ring* r, const pattn_args* a) {
+    if (!r || !a || r->cfg.dtype != PA_BF16 || a->num_layers < 1 || a->n_dyn < 1 || a->n_q_heads < 1 ||
+        a->n_q_heads % r->cfg.num_kv_heads)
+        return 0;
+    const long long group = a->n_q_heads / r->cfg.num_kv_heads;
+    const long long nrb = (a->n_dyn * group + 31) / 32;
+    return (long long)a->num_layers * r->cfg.num_kv_heads * nrb * 32 * r->cfg.head_dim / 8;
+}
+
+extern "C" size_t pattn_operand_q_bytes(const rb_ring* ring, const pattn_args* a) {
+    return (size_t)operand_q_chunks(reinterpret_cast<const Ring*>(ring), a) * 16;
+}
+
+extern "C" pa_status pattn_pack_q(const rb_ring* ring, const pattn_args* a, const void* q, void* q_operand,
+                                  void* stream) {
+    clear_error();
+    const Ring* r = reinterpret_cast<const Ring*>(ring);
+    PA_CHECK_ARG(r && a && q && q_operand, PA_EINVAL, "pattn_pack_q: null argument");
+    PA_CHECK_ARG(r->cfg.dtype == PA_BF16, PA_EINVAL, "pattn_pack_q: the operand order is for bf16 rings");
+    PA_CHECK_ARG(aligned16(q) && aligned16(q_operand), PA_EINVAL, "pattn_pack_q: buffers must be 16-byte aligned");
+    const long long chunks = operand_q_chunks(r, a);
+    PA_CHECK_ARG(chunks > 0, PA_ESHAPE, "pattn_pack_q: need layers >= 1, n_dyn >= 1 and Hq a multiple of Hkv");
+    const int hkv = r->cfg.num_kv_heads, d = r->cfg.head_dim, nrb = (a->n_dyn * (a->n_q_heads / hkv) + 31) / 32;
+    const char* qb = static_cast<const char*>(q);
+    const char* ob = static_cast<const char*>(q_operand);
+    const long long in_bytes = (long long)a->num_layers * a->n_dyn * a->n_q_heads * d * 2;
+    PA_CHECK_ARG(ob + chunks * 16 <= qb || qb + in_bytes <= ob, PA_EINVAL, "pattn_pack_q: buffers overlap");
+    pack_q<<<(unsigned)((chunks + 255) / 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint4*>(q), static_cast<uint4*>(q_operand), a->n_dyn, a->n_q_heads, hkv, d, nrb, chunks);
+    PA_LAUNCHED();
+    return PA_OK;
 }
 
 // ------------------------------------------------------------ decode readers --
@@ -1060,6 +1121,7 @@ static pa_status check_fused(const Ring* r, const pattn_args* a, const pattn_dec
                  PA_EINVAL, "pattn_fused_step: action and decode arguments must agree on layers, heads and scale");
     PA_CHECK_ARG(a->out_dtype == PA_F32 || a->out_dtype == PA_BF16, PA_EINVAL, "pattn_fused_step: bad out_dtype");
     PA_CHECK_ARG(a->n_dyn >= 1, PA_ESHAPE, "pattn_fused_step: n_dyn must be >= 1");
+    PA_CHECK_ARG(a->q_layout == PA_Q_TOKEN_MAJOR, PA_EINVAL, "pattn_fused_step: queries are token-major");
     return PA_OK;
 }
 

@@ -214,3 +214,26 @@ def test_packed_stack_workspace_and_shape_checks_without_device():
     assert L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 3, w[0], w[1], 1e-6, 1 / 16, 0.1,
                                                            packed=1)) == 0
     r.close()
+
+
+def test_operand_q_validation_without_device():
+    from partitioned_kv_cache_amd import _lib as L
+    r = L.Ring(L.rb_config(18, 1, 256, 256, 8, 768, L.PA_BF16), _fake(1), _fake(2))
+    a = L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_BF16, 0, L.PA_Q_OPERAND)
+    # 51 tokens x 8 heads = 408 rows -> 13 blocks of 32, 18 layers, D = 256, bf16
+    assert L.pattn_operand_q_bytes(r, a) == 18 * 13 * 32 * 256 * 2
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_pack_q(r, a, _fake(3), _fake(3), stream=0)        # in place
+    assert e.value.status == L.PA_EINVAL
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_step(r, L.pattn_args(0, 18, 8, 51, 1 / 16, L.PA_BF16, 0, 2), _fake(3), _fake(4), _fake(5), _fake(6),
+                     _fake(7), 1 << 30, 0)
+    assert e.value.status == L.PA_EINVAL and "q_layout" in str(e.value)
+    r.close()
+    rf = L.Ring(L.rb_config(1, 1, 64, 16, 4, 16, L.PA_F32), _fake(1), _fake(2))
+    af = L.pattn_args(0, 1, 1, 8, 1 / 8, L.PA_F32, 0, L.PA_Q_OPERAND)
+    assert L.pattn_operand_q_bytes(rf, af) == 0                         # f32 rings take token-major q
+    with pytest.raises(L.PattnError) as e:
+        L.pattn_pack_q(rf, af, _fake(3), _fake(4), stream=0)
+    assert e.value.status == L.PA_EINVAL
+    rf.close()
