@@ -636,6 +636,92 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
 }
 
 // ---------------------------------------------------------------------------
+// Private-tail partial on the matrix cores (bf16 rings): one wave per (stream,
+// call layer x KV head). The G = Hq / Hkv query heads of the stream are the
+// columns of S^T = K_tail . Q^T, so each tail key is read once for all of
+// them. The wave streams its tail in 32-key tiles through its own LDS buffers
+// in the partial kernel's layout (direct-to-LDS loads, K plane rotation) and
+// runs the same per-tile arithmetic (qk_scores, softmax_tile, pv_tile).
+// Partial rows row_base + stream * G + c go to slot `slot`.
+// grid (ceil(streams / TAIL_WAVES), Lb * Hkv), block TAIL_WAVES * 64.
+constexpr int TAIL_WAVES = 4;
+
+template <int D>
+__global__ __launch_bounds__(TAIL_WAVES * 64) void partial_tail_mfma(
+    const uint16_t* __restrict__ q, long long q_layer, int hq, int group, const uint16_t* __restrict__ tail_k,
+    const uint16_t* __restrict__ tail_v, const int32_t* __restrict__ tail_len, int n_streams, int cap, int hkv,
+    float scale_log2, int slot, Partials part, int row_base) {
+    constexpr int KD = D / 16, DB = D / 32, PLANE = KT * 64, TILE = DB * PLANE, NBLK = TILE / 1024;
+    __shared__ __attribute__((aligned(1024))) char lds[TAIL_WAVES][2][TILE];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int strm = blockIdx.x * TAIL_WAVES + wave, lg = blockIdx.y, lb = lg / hkv, g = lg % hkv;
+    if (strm >= n_streams) return;                                  // whole wave; no barriers below
+    char* kbuf = lds[wave][0];
+    char* vbuf = lds[wave][1];
+    int n = tail_len[strm];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+
+    // B operand: column c = l32 is query head g * G + c of this stream (c < G)
+    bf16x8 qf[KD];
+    const bool col_ok = l32 < group;
+    const uint16_t* qp = q + lb * q_layer + ((long long)strm * hq + g * group + (col_ok ? l32 : 0)) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) qf[kk] = col_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
+
+    const long long tok_base = ((long long)lb * n_streams + strm) * cap;
+    const int stride = hkv * D;
+    const uint16_t* tk = tail_k + tok_base * stride + g * D;
+    const uint16_t* tv = tail_v + tok_base * stride + g * D;
+    // direct-to-LDS copy of one tile: block b = plane b / 2, keys 16 (b % 2) .. + 15
+    const int dma_key = lane >> 2, dma_pos = lane & 3;
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
+            const int key = 16 * (b & 1) + dma_key;
+            const int j = min(t * KT + key, n - 1);                 // past the tail: a valid key, masked later
+            const int kchunk = (dma_pos ^ ((key >> 2) & 3)) << 3;   // K plane rotation
+            const uint16_t* row_k = tk + (long long)j * stride + (b >> 1) * 32;
+            const uint16_t* row_v = tv + (long long)j * stride + (b >> 1) * 32;
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(row_k + kchunk), (LDS_AS void*)(kbuf + b * 1024), 16,
+                                             0, 0);
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(row_v + (dma_pos << 3)),
+                                             (LDS_AS void*)(vbuf + b * 1024), 16, 0, 0);
+        }
+    };
+    // LDS read offsets of the partial kernel
+    const int prow = (l32 & ~0xC) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+    const int koff0 = prow * 64 + (((0 + hi) ^ ((prow >> 2) & 3)) << 4);
+    const int koff1 = prow * 64 + (((2 + hi) ^ ((prow >> 2) & 3)) << 4);
+    const int gi = lane >> 4, li = lane & 15;
+    const int voff = (8 * (gi >> 1) + (li >> 2)) * 64 + ((2 * (gi & 1) + ((li & 3) >> 1)) << 4) + ((li & 1) << 3);
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    for (int t = 0; t * KT < n; ++t) {
+        load_tile(t);           // the previous tile's LDS reads were consumed by its MFMAs already
+        wait_vmem<0>();
+        bf16x8 pf[2];
+        const f32x16 sc = qk_scores<D>(kbuf, koff0, koff1, qf);
+        softmax_tile<D>(sc, t * KT, n, hi, scale_log2, acc, m_run, l_run, pf);
+        pv_tile<D>(vbuf, voff, pf, acc);
+    }
+    l_run += __shfl_xor(l_run, 32);
+    if (!col_ok) return;
+    const int row = row_base + strm * group + l32;
+    uint16_t* op = part.optr<uint16_t>() + part.oblock(slot, lg, row) + ((row & 31) + 32 * hi) * 4;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<uint2*>(op + (b * 4 + j) * 256) =
+                make_uint2(pack_bf16(acc[b][4 * j], acc[b][4 * j + 1]), pack_bf16(acc[b][4 * j + 2], acc[b][4 * j + 3]));
+    if (hi == 0) part.ml[part.idx(slot, lg, row)] = make_float2(m_run, l_run);
+}
+
+// ---------------------------------------------------------------------------
 // Append one token per decode stream to its private tail, in every layer.
 // 16-byte chunks; each thread copies up to APPEND_BATCH chunks (of any
 // layers) with every load issued before the first store.
@@ -1064,6 +1150,17 @@ static pa_status launch_tails(const Ring* r, const Plan& p, const void* q, long 
         else if (d == 128) PA_TAIL(float, 128);
         else if (d == 64) PA_TAIL(float, 64);
         else PA_TAIL(float, 32);
+    } else if (p.group <= 32) {
+        // bf16: the stream's query heads are the columns of one MFMA tile
+        const dim3 tgrid((n_streams + TAIL_WAVES - 1) / TAIL_WAVES, p.lg_count);
+#define PA_TAIL_MFMA(DD)                                                                                        \
+    partial_tail_mfma<DD><<<tgrid, TAIL_WAVES * 64, 0, s>>>(                                                    \
+        static_cast<const uint16_t*>(q), q_layer, hq, p.group, static_cast<const uint16_t*>(tail_k),            \
+        static_cast<const uint16_t*>(tail_v), tail_len, n_streams, cap, hkv, scale_log2, slot, part, row_base)
+        if (d == 256) PA_TAIL_MFMA(256);
+        else if (d == 128) PA_TAIL_MFMA(128);
+        else PA_TAIL_MFMA(64);
+#undef PA_TAIL_MFMA
     } else {
         if (d == 256) PA_TAIL(uint16_t, 256);
         else if (d == 128) PA_TAIL(uint16_t, 128);
