@@ -9,6 +9,8 @@ call needs a derived input (gamma for the fused kernel) the oracle's value is
 what it is fed.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -185,6 +187,49 @@ def test_decode_readers_private_tails():
         worst = max(worst, rel_err(got[l], ref))
     _banner(f"decode worst rel {worst:.3e}")
     assert worst <= BAR
+
+
+TAIL_SHAPES = [
+    # (D, Hq, Hkv, streams, cap, layers): tails longer than one 32-key tile, grouped heads, odd counts
+    (128, 4, 2, 5, 70, 2),
+    (64, 8, 1, 3, 33, 2),
+    (256, 2, 2, 7, 96, 1),
+]
+
+
+@pytest.mark.parametrize("D,hq,hkv,G,cap,layers", TAIL_SHAPES)
+def test_decode_multi_tile_tails(D, hq, hkv, G, cap, layers):
+    """Private tails of several 32-key tiles (lengths 0, 1, 31, 32, 33, ..., cap)."""
+    L = lib()
+    s = configs.SHARED_KV.with_(name="tails", cfg_id=300 + D + cap, num_layers=layers, n_q_heads=hq, n_kv_heads=hkv,
+                                head_dim=D, pin_tokens=24, num_slots=2, tokens_per_frame=80, n_streams=G,
+                                tail_capacity=cap, scale=1 / math.sqrt(D))
+    _banner(f"decode tails D={D} hq={hq} hkv={hkv} streams={G} cap={cap}")
+    sc = Scenario(s)
+    for f in range(3):
+        sc.push(f)
+    choice = [0, 1, 31, 32, 33, cap - 1, cap]
+    lens = np.array([min(choice[j % len(choice)], cap) for j in range(G)], dtype=np.int32)
+    tk = synth.normal((layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILK, 7)
+    tv = synth.normal((layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILV, 7)
+    a = L.decode_args(0, layers, hq, G, cap, s.scale, L.PA_F32)
+    q = synth.decode_q(s, 3, 0)
+    wsb = L.pattn_decode_workspace_bytes(sc.ring, a)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((layers, G, hq, D), dtype=torch.float32, device="cuda")
+    L.pattn_decode(sc.ring, a, dev(q), dev(tk), dev(tv), dev(lens), out, ws, wsb)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    for l in range(layers):
+        tails = decode.PrivateTails(G, cap, hkv, D)
+        for j in range(G):
+            for t in range(int(lens[j])):
+                tails.append(j, synth.widen(tk[l, j, t]), synth.widen(tv[l, j, t]))
+        ck, cv = sc.cached_context(l)
+        ref = decode.decode_attention(synth.widen(q[l]), ck, cv, tails, s.scale)
+        err = rel_err(got[l], ref)
+        _banner(f"  layer {l} rel {err:.3e}")
+        assert err <= BAR
 
 
 def test_decode_empty_tail_is_shared_context_only():
