@@ -642,7 +642,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is built for a "
-              "single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "single MI355X; nothing here shards across GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
     from partitioned_kv_cache_amd import _lib as L, configs, synth

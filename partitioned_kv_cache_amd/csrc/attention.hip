@@ -1203,9 +1203,9 @@ extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* 
 
 // ---------------------------------------------------------------------------
 // One pass for both kinds of reader (OxyGen review, core method: the action
-// expert and the language expert read one shared cache; this build's f3
-// fuses their rows): the action suffix's rows and the decode streams' rows
-// stacked into one query matrix per (layer, KV head), so the shared
+// expert and the language expert read one shared cache): the action
+// suffix's rows and the decode streams' rows stacked into one query matrix
+// per (layer, KV head), so the shared
 // [pin | window] keys stream through the chip once for both.
 
 static pa_status check_fused(const Ring* r, const pattn_args* a, const pattn_decode_args* d) {

@@ -1,6 +1,6 @@
 """GPU parity of the fused reader pass (pattn_fused_step): the action
 suffix's rows and the decode streams' rows in one pass over the shared
-[pin; window] keys (OxyGen review, core method; this build's row f3).
+[pin; window] keys (OxyGen review, core method).
 
 Expected values come from the oracle: the action rows attend over
 [pin; window; suffix] (Eq. 1), each decode row over [pin; window; its own
