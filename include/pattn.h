@@ -370,10 +370,12 @@ pa_status oproj_residual(const void* o, const void* w_o, void* h, int32_t rows, 
  * h, x bf16 [rows][model_dim]; w_gate, w_up bf16 [ffn_dim][model_dim];
  * w_down bf16 [model_dim][ffn_dim] (nn.Linear layouts, no biases);
  * gamma f32 [model_dim]. rows <= 64; model_dim = 128 x {2, 4, 6, 8};
- * ffn_dim = 1024 x {1, 2, 3, 4, 6, 8}. The workspace holds act
- * (ffn_swiglu_workspace_bytes; 0 on unsupported sizes). Every pointer
- * 16-byte aligned. *nonfinite (nullable) gets bit 0 if a normalised element,
- * a new h or a new x is NaN or Inf.
+ * ffn_dim = 1024 x {1, 2, 3, 4, 6, 8}. The down projection is split over
+ * ffn_dim: each 512-wide chunk is summed into FP32 partials, which a second
+ * kernel adds in chunk order before the residual. The workspace holds act
+ * and those partials (ffn_swiglu_workspace_bytes; 0 on unsupported sizes).
+ * Every pointer 16-byte aligned. *nonfinite (nullable) gets bit 0 if a
+ * normalised element, a new h or a new x is NaN or Inf.
  * ====================================================================== */
 size_t ffn_swiglu_workspace_bytes(int32_t rows, int32_t model_dim, int32_t ffn_dim);
 pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_t ffn_dim, const float* gamma,
@@ -389,6 +391,9 @@ pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_t ffn_dim, 
  *                     h = bf16(h + o W_o[l]^T)
  *                     h = ffn_swiglu(h, gamma_ffn[l])             (when ffn_dim > 0)
  *   x = bf16(x - dt * h)
+ * When Hq * D is a multiple of 512 the out-projection is summed like the
+ * FFN's down projection (512-wide chunks of FP32 partials, added in chunk
+ * order), so it can differ from oproj_residual in the last bf16 bit.
  * gamma, gamma_ffn: f32, layer l's vector at + l * gamma_layer_stride,
  * [model_dim] each (gamma_ffn may be NULL when ffn_dim = 0).
  * x: bf16 [rows][model_dim], updated in place. Layers [0, num_layers) of

@@ -391,53 +391,6 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
     }
 }
 
-// gemm_down: h <- bf16(h + A W^T) (and the Euler update of x when x is not
-// null) for a long K = KC * 1024: the K range is walked in KC chunks of
-// KS = 8 k-steps per wave, the next chunk's loads in flight while the
-// current chunk's products run.
-template <int KC>
-__global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_down(const uint16_t* __restrict__ a,
-                                                                const uint16_t* __restrict__ w, int rows, int N,
-                                                                GemmOut out) {
-    constexpr int KS = 8, KCH = GEMM_WAVES * KS * 16, K = KC * KCH;
-    __shared__ float red[GEMM_WAVES][2][16][64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int n0 = blockIdx.x * 32;
-    const int k0 = wave * KS * 16 + 8 * hi;
-    const bool r0 = l32 < rows, r1 = 32 + l32 < rows, two = rows > 32;
-    const uint16_t* wp = w + (long long)(n0 + l32) * K + k0;
-    const uint16_t* ap0 = a + (long long)l32 * K + k0;
-    const uint16_t* ap1 = a + (long long)(32 + l32) * K + k0;
-    bf16x8 wf[2][KS], a0[2][KS], a1[2][KS];
-    auto load = [&](int c, int buf) {
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            const int off = c * KCH + 16 * i;
-            wf[buf][i] = *reinterpret_cast<const bf16x8*>(wp + off);
-            a0[buf][i] = r0 ? *reinterpret_cast<const bf16x8*>(ap0 + off) : bf16x8{};
-            a1[buf][i] = r1 ? *reinterpret_cast<const bf16x8*>(ap1 + off) : bf16x8{};
-        }
-    };
-    f32x16 c0 = f32x16{}, c1 = f32x16{};
-    load(0, 0);
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-        if (c + 1 < KC) load(c + 1, (c + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[c & 1][i], wf[c & 1][i], c0, 0, 0, 0);
-            if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[c & 1][i], wf[c & 1][i], c1, 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        red[wave][0][r][lane] = c0[r];
-        red[wave][1][r][lane] = c1[r];
-    }
-    __syncthreads();
-    residual_epilogue(red, n0, rows, N, out);
-}
-
 // K = 128 * KS; the k-step counts the library is built for.
 static bool gemm_k_supported(int K) {
     if (K % 128) return false;
@@ -621,7 +574,8 @@ static bool ffn_dims_ok(int model_dim, int ffn_dim) {
 
 extern "C" size_t ffn_swiglu_workspace_bytes(int32_t rows, int32_t model_dim, int32_t ffn_dim) {
     if (rows < 1 || rows > 64 || !ffn_dims_ok(model_dim, ffn_dim)) return 0;
-    return align_up((size_t)rows * ffn_dim * sizeof(uint16_t), 256);
+    // the SwiGLU activation, then the down projection's split-K partials
+    return align_up((size_t)rows * ffn_dim * sizeof(uint16_t), 256) + residual_splitk_bytes(rows, ffn_dim, model_dim);
 }
 
 extern "C" pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_t ffn_dim, const float* gamma,
@@ -651,22 +605,8 @@ extern "C" pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_
         default: gemm_gateup<8><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
     }
     PA_LAUNCHED();
-    GemmOut o{};
-    o.h = static_cast<uint16_t*>(h);
-    o.x = static_cast<uint16_t*>(x);
-    o.dt = dt;
-    o.nonfinite = nonfinite;
-    const uint16_t* wd = static_cast<const uint16_t*>(w_down);
-    const dim3 grid(model_dim / 32);
-    switch (ffn_dim / 1024) {
-        case 1: gemm_down<1><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
-        case 2: gemm_down<2><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
-        case 3: gemm_down<3><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
-        case 4: gemm_down<4><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
-        case 6: gemm_down<6><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
-        default: gemm_down<8><<<grid, block, 0, s>>>(act, wd, rows, model_dim, o); break;
-    }
-    PA_LAUNCHED();
-    return PA_OK;
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           align_up((size_t)rows * ffn_dim * sizeof(uint16_t), 256));
+    return residual_splitk(act, w_down, false, h, rows, ffn_dim, model_dim, x, dt, nonfinite, part, s);
 }
 

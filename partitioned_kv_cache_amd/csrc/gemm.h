@@ -119,10 +119,23 @@ inline int qpack_blocks(int rows, int hq, int hkv) { return (rows * (hq / hkv) +
 pa_status packed_norm_gateup(const void* h, int rows, int model_dim, int ffn_dim, const float* gamma, float eps,
                              const void* w_gate_p, const void* w_up_p, void* act_p, uint32_t* nonfinite,
                              hipStream_t s);
-//   h <- bf16(h + A W^T); x <- bf16(x - dt h) when x is set   (A and W packed, K = 1024 * KC)
-//   wave_major: sum in the order of oproj_residual, else in that of ffn_swiglu's down projection
-pa_status packed_residual(const void* a_p, const void* w_p, void* h, int rows, int K, int N, void* x, float dt,
-                          uint32_t* nonfinite, bool wave_major, hipStream_t s);
+// Residual projection h <- bf16(h + A W^T); x <- bf16(x - dt h) when x is
+// set -- the stack's out-projection and the FFN's down projection -- split
+// over K: KC = K / SPLITK_CHUNK workgroups per 32 columns each sum one chunk
+// (their 8 waves one SPLITK_CHUNK / 8 slice each, merged in wave order) into
+// FP32 partials part[KC][rows][N]; a second kernel adds the chunks in order
+// and applies the residual. A and W packed (fragment order) or in row-major /
+// nn.Linear layout; both sum in the same order, so the two agree bit for bit.
+pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, int rows, int K, int N, void* x,
+                          float dt, uint32_t* nonfinite, float* part, hipStream_t s);
+constexpr int SPLITK_KS = 4;                                // MFMA k-steps per wave and chunk
+constexpr int SPLITK_CHUNK = GEMM_WAVES * SPLITK_KS * 16;   // k per workgroup
+inline bool residual_splitk_supported(int K, int N) {
+    return K % SPLITK_CHUNK == 0 && K >= SPLITK_CHUNK && K <= 8192 && N % 32 == 0;
+}
+inline size_t residual_splitk_bytes(int rows, int K, int N) {
+    return align_up((size_t)(K / SPLITK_CHUNK) * rows * N * 4, 256);
+}
 bool packed_residual_supported(int K, int N);
 bool packed_norm_supported(int model_dim);
 

@@ -198,44 +198,45 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
     }
 }
 
-// ----------------------------------------- residual projection (packed) -----
-// h <- bf16(h + A W^T) (+ Euler update of x) with A and W packed, K = KC * 1024
-// walked in chunks of 8 steps per wave, the next chunk's loads in flight.
-// WM (wave-major): wave w owns the contiguous k-range [w K / 8, (w + 1) K / 8)
-// -- the split of the unpacked out-projection; otherwise chunk c of wave w is
-// [c 1024 + w 128, c 1024 + (w + 1) 128) -- the split of the unpacked down
-// projection. Either way the products are summed in the order of the kernel
-// they stand in for, so the results are bit-identical.
-template <int KC, bool WM>
-__global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_res_packed(const uint16_t* __restrict__ ap,
-                                                                      const uint16_t* __restrict__ wp, int rows,
-                                                                      int N, GemmOut out) {
-    constexpr int KS = 8, K = KC * GEMM_WAVES * KS * 16, S = K / 16;
+// ------------------------------------------ split-K residual projection ---
+// Workgroup (column block nb, chunk c) sums k in [SPLITK_CHUNK c,
+// SPLITK_CHUNK (c + 1)): wave w the slice of KS MFMA steps from
+// SPLITK_CHUNK c + 16 KS w, the 8 waves merged in wave order, into
+// part[c][m][n] (FP32, rows m < rows).
+template <bool PACKED>
+__global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_splitk_part(const uint16_t* __restrict__ a,
+                                                                     const uint16_t* __restrict__ w, int rows, int N,
+                                                                     int K, float* __restrict__ part) {
+    constexpr int KS = SPLITK_KS;
     __shared__ float red[GEMM_WAVES][2][16][64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nb = blockIdx.x, n0 = nb * 32;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int nb = blockIdx.x, c = blockIdx.y, n0 = nb * 32;
     const bool two = rows > 32;
-    bf16x8 wf[2][KS], a0[2][KS], a1[2][KS];
-    auto load = [&](int c, int buf) {
+    bf16x8 wf[KS], a0[KS], a1[KS];
+    if (PACKED) {
+        const long long S = K / 16;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-            const int s = (WM ? wave * KC + c : c * GEMM_WAVES + wave) * KS + i;
-            wf[buf][i] = *reinterpret_cast<const bf16x8*>(wp + (((long long)nb * S + s) * 64 + lane) * 8);
-            a0[buf][i] = *reinterpret_cast<const bf16x8*>(ap + (((long long)s * 2) * 64 + lane) * 8);
-            a1[buf][i] = two ? *reinterpret_cast<const bf16x8*>(ap + (((long long)s * 2 + 1) * 64 + lane) * 8)
-                             : bf16x8{};
+            const long long st = (c * GEMM_WAVES + wave) * KS + i;
+            wf[i] = *reinterpret_cast<const bf16x8*>(w + ((nb * S + st) * 64 + lane) * 8);
+            a0[i] = *reinterpret_cast<const bf16x8*>(a + ((st * 2) * 64 + lane) * 8);
+            a1[i] = two ? *reinterpret_cast<const bf16x8*>(a + ((st * 2 + 1) * 64 + lane) * 8) : bf16x8{};
         }
-    };
+    } else {
+        const int k0 = c * SPLITK_CHUNK + wave * KS * 16 + 8 * hi;
+        const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            wf[i] = *reinterpret_cast<const bf16x8*>(w + (long long)(n0 + l32) * K + k0 + 16 * i);
+            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(a + (long long)l32 * K + k0 + 16 * i) : bf16x8{};
+            a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
+        }
+    }
     f32x16 c0 = f32x16{}, c1 = f32x16{};
-    load(0, 0);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-        if (c + 1 < KC) load(c + 1, (c + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[c & 1][i], wf[c & 1][i], c0, 0, 0, 0);
-            if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[c & 1][i], wf[c & 1][i], c1, 0, 0, 0);
-        }
+    for (int i = 0; i < KS; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wf[i], c0, 0, 0, 0);
+        if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wf[i], c1, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -243,10 +244,74 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_res_packed(const uint
         red[wave][1][r][lane] = c1[r];
     }
     __syncthreads();
-    residual_epilogue(red, n0, rows, N, out);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
+        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (m >= rows) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        part[((long long)c * rows + m) * N + n0 + l32] = v;
+    }
+}
+
+// h <- bf16(h + sum_c part[c]) in chunk order, x <- bf16(x - dt h) when x is
+// set, with the residual epilogue's arithmetic. One thread per element.
+__global__ __launch_bounds__(256) void residual_reduce(const float* __restrict__ part, int kc, int rows, int N,
+                                                       GemmOut out) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)rows * N;
+    bool bad = false;
+    if (i < total) {
+        // every load issued before the first add
+        constexpr int MAXC = 8192 / SPLITK_CHUNK;
+        float p[MAXC];
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) p[c] = c < kc ? part[c * total + i] : 0.f;
+        const float h0 = bf2f(out.h[i]);
+        const float x0 = out.x ? bf2f(out.x[i]) : 0.f;
+        float v = 0.f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c)
+            if (c < kc) v += p[c];
+        const float hn = bf2f(f2bf(h0 + v));
+        out.h[i] = f2bf(hn);
+        bad = !finite_f(hn);
+        if (out.x) {
+            const float xn = x0 - out.dt * hn;
+            bad |= !finite_f(xn);
+            out.x[i] = f2bf(xn);
+        }
+    }
+    if (out.nonfinite && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(out.nonfinite, 1u);
 }
 
 // ------------------------------------------------------------ host side -----
+pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, int rows, int K, int N, void* x,
+                           float dt, uint32_t* nonfinite, float* part, hipStream_t s) {
+    const int kc = K / SPLITK_CHUNK;
+    PA_CHECK_ARG(K % SPLITK_CHUNK == 0 && kc >= 1 && K <= 8192 && N % 32 == 0 && rows >= 1 && rows <= 64, PA_ESHAPE,
+                 "residual projection: unsupported shape rows %d, K %d, N %d", rows, K, N);
+    const uint16_t* aa = static_cast<const uint16_t*>(a);
+    const uint16_t* ww = static_cast<const uint16_t*>(w);
+    const dim3 grid(N / 32, kc), block(GEMM_WAVES * 64);
+    if (packed)
+        gemm_splitk_part<true><<<grid, block, 0, s>>>(aa, ww, rows, N, K, part);
+    else
+        gemm_splitk_part<false><<<grid, block, 0, s>>>(aa, ww, rows, N, K, part);
+    PA_LAUNCHED();
+    GemmOut o{};
+    o.h = static_cast<uint16_t*>(h);
+    o.x = static_cast<uint16_t*>(x);
+    o.dt = dt;
+    o.nonfinite = nonfinite;
+    const long long total = (long long)rows * N;
+    residual_reduce<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, kc, rows, N, o);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
 bool packed_norm_supported(int model_dim) {
     const int ks = model_dim / 128;
     return model_dim % 512 == 0 && (ks == 4 || ks == 8);
@@ -294,34 +359,6 @@ pa_status packed_norm_gateup(const void* h, int rows, int model_dim, int ffn_dim
         gemm_norm_packed<PK_GATEUP, 4><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(xx, gamma, eps, g, u, rows, ffn_dim, o, a);
     else
         gemm_norm_packed<PK_GATEUP, 8><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(xx, gamma, eps, g, u, rows, ffn_dim, o, a);
-    PA_LAUNCHED();
-    return PA_OK;
-}
-
-pa_status packed_residual(const void* a_p, const void* w_p, void* h, int rows, int K, int N, void* x, float dt,
-                          uint32_t* nonfinite, bool wave_major, hipStream_t s) {
-    GemmOut o{};
-    o.h = static_cast<uint16_t*>(h);
-    o.x = static_cast<uint16_t*>(x);
-    o.dt = dt;
-    o.nonfinite = nonfinite;
-    const uint16_t* a = static_cast<const uint16_t*>(a_p);
-    const uint16_t* w = static_cast<const uint16_t*>(w_p);
-    const dim3 grid(N / 32), block(GEMM_WAVES * 64);
-#define PA_RES(KC)                                                                                  \
-    do {                                                                                            \
-        if (wave_major) gemm_res_packed<KC, true><<<grid, block, 0, s>>>(a, w, rows, N, o);        \
-        else gemm_res_packed<KC, false><<<grid, block, 0, s>>>(a, w, rows, N, o);                  \
-    } while (0)
-    switch (K / 1024) {
-        case 1: PA_RES(1); break;
-        case 2: PA_RES(2); break;
-        case 3: PA_RES(3); break;
-        case 4: PA_RES(4); break;
-        case 6: PA_RES(6); break;
-        default: PA_RES(8); break;
-    }
-#undef PA_RES
     PA_LAUNCHED();
     return PA_OK;
 }

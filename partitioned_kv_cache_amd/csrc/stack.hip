@@ -20,8 +20,14 @@
 namespace pa {
 
 struct StackWs {
-    size_t h, q, k, v, o, attn, ffn, total;
+    size_t h, q, k, v, o, attn, part, ffn, total;
 };
+
+// the out-projection runs split over K when Hq * D allows it (always on
+// packed weights); otherwise the unpacked path falls back to oproj_residual
+static bool oproj_split(const Ring* r, const pa_stack* st) {
+    return residual_splitk_supported(st->n_q_heads * r->cfg.head_dim, st->model_dim);
+}
 
 static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes) {
     const size_t n = st->rows, m = st->model_dim, d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
@@ -41,8 +47,12 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
     // packed activations always span the 64 row slots of the operand
     w.o = take((st->packed ? 64 : n) * st->n_q_heads * d * 2);
     w.attn = take(attn_bytes);
-    if (st->packed)
-        w.ffn = take(st->ffn_dim ? (size_t)64 * st->ffn_dim * 2 : 0);
+    // FP32 partials of the split-K out-projection
+    w.part = take(oproj_split(r, st) ? residual_splitk_bytes(st->rows, st->n_q_heads * (int)d, st->model_dim) : 0);
+    if (st->packed)   // packed activation (64 row slots), then the down projection's split-K partials
+        w.ffn = take(st->ffn_dim ? align_up((size_t)64 * st->ffn_dim * 2, 256) +
+                                       residual_splitk_bytes(st->rows, st->ffn_dim, st->model_dim)
+                                 : 0);
     else
         w.ffn = take(st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0);
     w.total = off;
@@ -124,6 +134,8 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
     char* base = static_cast<char*>(ws);
     void *h = base + w.h, *q = base + w.q, *k = base + w.k, *v = base + w.v, *o = base + w.o;
     void* aws = base + w.attn;
+    float* opart = reinterpret_cast<float*>(base + w.part);
+    const bool osplit = oproj_split(r, st);
     void* fws = base + w.ffn;
     hipStream_t strm = static_cast<hipStream_t>(stream);
     const size_t xbytes = (size_t)st->rows * st->model_dim * 2;
@@ -147,16 +159,19 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
             const pattn_args a = attn_args(st, l);
             s = pattn_step_apacked(ring, &a, q, k, v, o, aws, attn, stream, true);
             if (s != PA_OK) return s;
-            s = packed_residual(o, wo, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr,
-                                st->dt, nonfinite, true, strm);
+            s = residual_splitk(o, wo, true, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr,
+                                st->dt, nonfinite, opart, strm);
             if (s != PA_OK) return s;
             if (st->ffn_dim) {
                 s = packed_norm_gateup(h, st->rows, st->model_dim, st->ffn_dim, gamma_ffn + l * gamma_layer_stride,
                                        st->eps, static_cast<const uint16_t*>(st->w_gate) + l * wf_layer,
                                        static_cast<const uint16_t*>(st->w_up) + l * wf_layer, fws, nonfinite, strm);
                 if (s != PA_OK) return s;
-                s = packed_residual(fws, static_cast<const uint16_t*>(st->w_down) + l * wf_layer, h, st->rows,
-                                    st->ffn_dim, st->model_dim, last ? x : nullptr, st->dt, nonfinite, false, strm);
+                float* part = reinterpret_cast<float*>(static_cast<char*>(fws) +
+                                                       align_up((size_t)64 * st->ffn_dim * 2, 256));
+                s = residual_splitk(fws, static_cast<const uint16_t*>(st->w_down) + l * wf_layer, true, h,
+                                    st->rows, st->ffn_dim, st->model_dim, last ? x : nullptr, st->dt, nonfinite,
+                                    part, strm);
                 if (s != PA_OK) return s;
             }
         }
@@ -172,9 +187,12 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
         const pattn_args a = attn_args(st, l);
         s = pattn_step(ring, &a, q, k, v, o, aws, attn, stream);
         if (s != PA_OK) return s;
-        // the Euler update rides on the layer's last projection
-        s = oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr, st->dt,
-                           nonfinite, stream);
+        // the Euler update rides on the layer's last projection; the split-K
+        // form sums in the packed path's order
+        void* xl = last && !st->ffn_dim ? x : nullptr;
+        s = osplit ? residual_splitk(o, wo, false, h, st->rows, in_dim, st->model_dim, xl, st->dt, nonfinite, opart,
+                                     strm)
+                   : oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, xl, st->dt, nonfinite, stream);
         if (s != PA_OK) return s;
         if (st->ffn_dim) {
             s = ffn_swiglu(h, st->rows, st->model_dim, st->ffn_dim, gamma_ffn + l * gamma_layer_stride, st->eps,
