@@ -12,6 +12,11 @@
 // written packed by their producer; and the AdaRMSNorm operand, formed from
 // user-layout rows, is normalised into LDS by the rows' own waves (coalesced
 // 1 KB loads) and read back in the operand layout.
+//
+// The two residual projections (the out-projection and the FFN's down
+// projection) split K across workgroups instead, for either weight layout:
+// a 32-column workgroup that walks all of K would stream up to 256 KB of
+// weights and re-read the whole activation through one CU.
 
 #include <math.h>
 

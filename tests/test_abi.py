@@ -216,6 +216,27 @@ def test_packed_stack_workspace_and_shape_checks_without_device():
     r.close()
 
 
+def test_split_k_workspace_sizes_without_device():
+    """The FFN workspace holds the bf16 activation and FP32 partials of the
+    down projection per 512-wide chunk of ffn_dim; the stack adds partials of
+    the out-projection when Hq * D is a multiple of 512."""
+    from partitioned_kv_cache_amd import _lib as L
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    for rows, model, ffn in [(51, 1024, 4096), (1, 256, 1024), (64, 768, 8192), (33, 512, 3072)]:
+        assert L.ffn_swiglu_workspace_bytes(rows, model, ffn) == up(rows * ffn * 2) + up(ffn // 512 * rows * model * 4)
+    r = L.Ring(L.rb_config(18, 1, 256, 48, 2, 768, L.PA_BF16), _fake(1), _fake(2))
+    w = [_fake(3), _fake(4)]
+    st = lambda hq: L.pa_stack(18, 51, 1024, hq, w[0], w[1], 1e-6, 1 / 16, 0.1)  # noqa: E731
+    attn = lambda hq: L.pattn_workspace_bytes(r, L.pattn_args(0, 1, hq, 51, 1 / 16, L.PA_BF16))  # noqa: E731
+    # h, q, k, v, o, attention, out-projection partials (Hq D = 2048: 4 chunks)
+    base = lambda hq: (up(51 * 1024 * 2) + up(51 * hq * 256 * 2) + 2 * up(51 * 256 * 2) + up(51 * hq * 256 * 2)  # noqa: E731
+                       + up(attn(hq)))
+    assert L.pa_denoise_step_workspace_bytes(r, st(8)) == base(8) + up(4 * 51 * 1024 * 4)
+    # Hq D = 768 is not a whole number of chunks: no partials, single-kernel out-projection
+    assert L.pa_denoise_step_workspace_bytes(r, st(3)) == base(3)
+    r.close()
+
+
 def test_operand_q_validation_without_device():
     from partitioned_kv_cache_amd import _lib as L
     r = L.Ring(L.rb_config(18, 1, 256, 256, 8, 768, L.PA_BF16), _fake(1), _fake(2))

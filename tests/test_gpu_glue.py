@@ -318,11 +318,14 @@ class StackRig:
         return [_oracle_gamma(self.s, l, t, state) for l in range(self.s.num_layers)]
 
 
-def test_denoise_step_matches_oracle_chain():
+# Hq * D = 2048 runs the out-projection split over K; 768 (three heads) is
+# not a multiple of the 512-wide chunk and takes the single-kernel path.
+@pytest.mark.parametrize("hq,layers", [(8, 18), (3, 4)])
+def test_denoise_step_matches_oracle_chain(hq, layers):
     L = lib()
-    _banner("denoise step 18 layers")
-    rig = StackRig(S3, 3)
-    s = S3
+    _banner(f"denoise step {layers} layers, {hq} query heads")
+    s = S3 if hq == 8 else S3.with_(name=f"stack_hq{hq}", cfg_id=81, n_q_heads=hq, num_layers=layers)
+    rig = StackRig(s, 3)
     gam = rig.oracle_gammas(2, 0)
     gam32 = np.stack(gam).astype(np.float32)
     x = synth.flow_x(s, 2)
