@@ -321,8 +321,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
 //
 // gemm_gateup: a workgroup owns 32 act columns; its 8 waves split K = model
 // (KS k-steps of 16 each) and compute both products for those columns; the
-// gate and up partial sums meet in LDS one after the other.
-template <int KS>
+// gate and up partial sums meet in LDS one after the other. Without NORM, x
+// is the already normalised operand.
+template <int KS, bool NORM = true>
 __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t* __restrict__ x,
                                                                   const float* __restrict__ gamma, float eps,
                                                                   const uint16_t* __restrict__ w_gate,
@@ -342,8 +343,17 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
         wu[i] = *reinterpret_cast<const bf16x8*>(w_up + wrow + 16 * i);
     }
     bf16x8 a0[KS], a1[KS];
-    norm_fragments<KS>(x, gamma, eps, rows, rinv_s, a0, a1);
-    if (blockIdx.x == 0 && nonfinite) report_nonfinite<KS>(a0, a1, nonfinite);
+    if (NORM) {
+        norm_fragments<KS>(x, gamma, eps, rows, rinv_s, a0, a1);
+        if (blockIdx.x == 0 && nonfinite) report_nonfinite<KS>(a0, a1, nonfinite);
+    } else {
+        const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(x + (long long)l32 * K + k0 + 16 * i) : bf16x8{};
+            a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(x + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
+        }
+    }
     const bool two = rows > 32;
     f32x16 g0 = f32x16{}, g1 = f32x16{}, u0 = f32x16{}, u1 = f32x16{};
 #pragma unroll
@@ -439,6 +449,42 @@ static pa_status launch_gamma(const ada_mlp* m, const uint16_t* w1, const uint16
     PA_LAUNCHED();
     gamma_out<<<dim3((m->model_dim + 15) / 16, n_layers), 256, n_t * m->hidden_dim * sizeof(uint16_t), s>>>(
         w2, b2, a_ws, n_t, m->hidden_dim, m->model_dim, gamma);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
+// Stack-internal projections on an operand the residual kernel has already
+// normalised (nn.Linear layouts; the packed forms are in packed.hip).
+pa_status qkv_proj(const void* y, int rows, int model_dim, const void* w_qkv, int hq, int hkv, int d, void* q,
+                   void* k, void* v, hipStream_t s) {
+    PA_CHECK_ARG(gemm_k_supported(model_dim) && rows >= 1 && rows <= 64, PA_ESHAPE,
+                 "qkv projection: model_dim must be 128 x {2, 4, 6, 8, 12, 16} (got %d)", model_dim);
+    GemmOut o{};
+    o.q = static_cast<uint16_t*>(q);
+    o.k = static_cast<uint16_t*>(k);
+    o.v = static_cast<uint16_t*>(v);
+    o.nq = hq * d;
+    o.nk = hkv * d;
+    const hipError_t e = launch_gemm<GEMM_QKV, false>(static_cast<const uint16_t*>(y), nullptr, 0.f,
+                                                      static_cast<const uint16_t*>(w_qkv), rows, model_dim,
+                                                      (hq + 2 * hkv) * d, o, s);
+    PA_CHECK_ARG(e == hipSuccess, PA_EDEVICE, "qkv projection: launch failed (%s)", hipGetErrorString(e));
+    return PA_OK;
+}
+
+pa_status gateup_proj(const void* y, int rows, int model_dim, int ffn_dim, const void* w_gate, const void* w_up,
+                      void* act, hipStream_t s) {
+    const uint16_t* yy = static_cast<const uint16_t*>(y);
+    const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
+    const uint16_t* wu = static_cast<const uint16_t*>(w_up);
+    uint16_t* a = static_cast<uint16_t*>(act);
+    const dim3 block(GEMM_WAVES * 64);
+    switch (model_dim / 128) {
+        case 2: gemm_gateup<2, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        case 4: gemm_gateup<4, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        case 6: gemm_gateup<6, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        default: gemm_gateup<8, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+    }
     PA_LAUNCHED();
     return PA_OK;
 }

@@ -108,17 +108,35 @@ __host__ __device__ inline long long apack_index(int m, int k) {
     return (((long long)(k >> 4) * 2 + (m >> 5)) * 64 + ((k >> 3) & 1) * 32 + (m & 31)) * 8 + (k & 7);
 }
 
-// Stack-internal GEMMs on packed operands (rows <= 64).
-//   q|k|v = bf16(AdaRMSNorm(x, gamma)) W_qkv^T           (W_qkv packed; q in operand order when q_packed)
-pa_status packed_norm_qkv(const void* x, int rows, int model_dim, const float* gamma, float eps, const void* w_qkv_p,
-                          int hq, int hkv, int d, void* q, void* k, void* v, uint32_t* nonfinite, bool q_packed,
-                          hipStream_t s);
+// Stack-internal GEMMs (rows <= 64) on an operand y = bf16(AdaRMSNorm(h))
+// that the residual kernel before them has already formed (NormNext):
+//   q|k|v = y W_qkv^T
+//   act   = bf16(SiLU(y W_gate^T) * (y W_up^T))
+// packed_*: y and the weights in fragment order (y over 64 row slots, the
+// padding rows zero), q in operand order when q_packed, act written packed;
+// *_proj (adanorm.hip): y [rows][model_dim], nn.Linear weights. Both sum in
+// the same order.
+pa_status packed_qkv(const void* y_p, int rows, int model_dim, const void* w_qkv_p, int hq, int hkv, int d, void* q,
+                     void* k, void* v, bool q_packed, hipStream_t s);
+pa_status packed_gateup(const void* y_p, int rows, int model_dim, int ffn_dim, const void* w_gate_p,
+                        const void* w_up_p, void* act_p, hipStream_t s);
+pa_status qkv_proj(const void* y, int rows, int model_dim, const void* w_qkv, int hq, int hkv, int d, void* q,
+                   void* k, void* v, hipStream_t s);
+pa_status gateup_proj(const void* y, int rows, int model_dim, int ffn_dim, const void* w_gate, const void* w_up,
+                      void* act, hipStream_t s);
 // 32-row blocks per KV head of the packed Q of `rows` tokens
 inline int qpack_blocks(int rows, int hq, int hkv) { return (rows * (hq / hkv) + 31) / 32; }
-//   act_p = packed bf16(SiLU(y W_gate^T) * (y W_up^T)), y = bf16(AdaRMSNorm(h, gamma))
-pa_status packed_norm_gateup(const void* h, int rows, int model_dim, int ffn_dim, const float* gamma, float eps,
-                             const void* w_gate_p, const void* w_up_p, void* act_p, uint32_t* nonfinite,
-                             hipStream_t s);
+
+// The AdaRMSNorm of the next GEMM's operand, fused into the kernel that
+// finishes h: y = bf16(h / sqrt(mean(h^2) + eps) * gamma), FP32 arithmetic,
+// written in fragment order over 64 row slots (packed; padding rows zero) or
+// as [rows][N].
+struct NormNext {
+    const float* gamma;
+    float eps;
+    void* y;
+    bool packed;
+};
 // Residual projection h <- bf16(h + A W^T); x <- bf16(x - dt h) when x is
 // set -- the stack's out-projection and the FFN's down projection -- split
 // over K: KC = K / SPLITK_CHUNK workgroups per 32 columns each sum one chunk
@@ -126,8 +144,14 @@ pa_status packed_norm_gateup(const void* h, int rows, int model_dim, int ffn_dim
 // FP32 partials part[KC][rows][N]; a second kernel adds the chunks in order
 // and applies the residual. A and W packed (fragment order) or in row-major /
 // nn.Linear layout; both sum in the same order, so the two agree bit for bit.
+// With nn, the reduction runs one workgroup per row and also forms the next
+// operand y (the h it writes is the same).
 pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, int rows, int K, int N, void* x,
-                          float dt, uint32_t* nonfinite, float* part, hipStream_t s);
+                          float dt, uint32_t* nonfinite, float* part, hipStream_t s, const NormNext* nn = nullptr);
+// h_out <- h_in and y <- AdaRMSNorm(h_in) (the first layer's operand; h_out
+// may be h_in).
+pa_status norm_rows(const void* h_in, void* h_out, int rows, int N, const NormNext& nn, uint32_t* nonfinite,
+                    hipStream_t s);
 constexpr int SPLITK_KS = 4;                                // MFMA k-steps per wave and chunk
 constexpr int SPLITK_CHUNK = GEMM_WAVES * SPLITK_KS * 16;   // k per workgroup
 inline bool residual_splitk_supported(int K, int N) {

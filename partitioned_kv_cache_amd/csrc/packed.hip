@@ -37,106 +37,37 @@ __global__ __launch_bounds__(256) void pack_weight(const uint4* __restrict__ w, 
     wp[c] = w[((long long)n * K + k) >> 3];
 }
 
-// -------------------------------------------- norm + projection (packed) ----
-// A workgroup owns 32 output columns (W block nb) and all 64 row slots; its
-// 8 waves split K into KS 16-k steps each. Wave w normalises rows w, w + 8,
-// ... into LDS (its own rows, so no barrier between the mean of squares and
-// the scaling); after one barrier every wave reads its operand fragments
-// from LDS. The LDS is then reused for the split-K reduction.
+// ------------------------------------------------ projection (packed) ----
+// A workgroup owns 32 output columns (W block nb) and all 64 row slots of the
+// packed operand y; its 8 waves split K into KS 16-k steps each, load their
+// operand fragments straight from y (1 KB contiguous per wave load) and meet
+// in LDS for the reduction over waves.
 enum PackedMode { PK_QKV = 0, PK_GATEUP = 1 };
 
 template <int MODE, int KS>
-__global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_norm_packed(
-    const uint16_t* __restrict__ x, const float* __restrict__ gamma, float eps, const uint16_t* __restrict__ wp1,
-    const uint16_t* __restrict__ wp2, int rows, int N, GemmOut out, uint16_t* __restrict__ act_p) {
+__global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t* __restrict__ y,
+                                                                  const uint16_t* __restrict__ wp1,
+                                                                  const uint16_t* __restrict__ wp2, int rows, int N,
+                                                                  GemmOut out, uint16_t* __restrict__ act_p) {
     constexpr int K = GEMM_WAVES * KS * 16, S = K / 16;
-    constexpr int XS = K + 8;                         // staged row stride in bf16 elements (16 B of padding)
-    constexpr int LPR = K / 512;                      // 1 KB row pieces per wave load
-    constexpr int RED = GEMM_WAVES * 2 * 16 * 64 * 4;
-    constexpr int SMEM = 64 * XS * 2 > RED ? 64 * XS * 2 : RED;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: row choices are scalar branches
+    __shared__ float red[GEMM_WAVES][2][16][64];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int nb = blockIdx.x, n0 = nb * 32;
-
-    // normalise rows w, w + 8, ... into LDS (rows >= `rows` are zeros)
-    static_assert(K % 512 == 0, "rows are staged in 1 KB pieces");
-    float4 g[LPR][2];
+    const bool two = rows > 32;
+    bf16x8 a0[KS], a1[KS], w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
 #pragma unroll
-    for (int c = 0; c < LPR; ++c) {
-        g[c][0] = *reinterpret_cast<const float4*>(gamma + c * 512 + lane * 8);
-        g[c][1] = *reinterpret_cast<const float4*>(gamma + c * 512 + lane * 8 + 4);
+    for (int i = 0; i < KS; ++i) {
+        const long long st = wave * KS + i;
+        a0[i] = *reinterpret_cast<const bf16x8*>(y + ((st * 2) * 64 + lane) * 8);
+        a1[i] = two ? *reinterpret_cast<const bf16x8*>(y + ((st * 2 + 1) * 64 + lane) * 8) : bf16x8{};
     }
-    constexpr int RPW = 64 / GEMM_WAVES;
-    uint4 raw[RPW][LPR];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-        const int r = wave + rr * GEMM_WAVES;
-#pragma unroll
-        for (int c = 0; c < LPR; ++c)
-            raw[rr][c] = r < rows ? *reinterpret_cast<const uint4*>(x + (long long)r * K + c * 512 + lane * 8)
-                                  : make_uint4(0, 0, 0, 0);
-    }
-    // Then this wave's weight blocks (KS consecutive 1 KB blocks): issued after
-    // x, so the normalisation waits only for x (loads return in issue order)
-    // while the weights stream in.
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
     const long long wb = ((long long)nb * S + wave * KS) * 512 + lane * 8;
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
         w1[i] = *reinterpret_cast<const bf16x8*>(wp1 + wb + i * 512);
         if (MODE == PK_GATEUP) w2[i] = *reinterpret_cast<const bf16x8*>(wp2 + wb + i * 512);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t bad = 0;                  // nonfinite_bits of every rounded operand, as the MFMA sees it
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-        const int r = wave + rr * GEMM_WAVES;          // wave-uniform
-        if (r >= rows) {                               // padding rows are zeros
-#pragma unroll
-            for (int c = 0; c < LPR; ++c)
-                *reinterpret_cast<uint4*>(xs + r * XS + c * 512 + lane * 8) = make_uint4(0, 0, 0, 0);
-            continue;
-        }
-        float ss = 0.f;
-#pragma unroll
-        for (int c = 0; c < LPR; ++c) {
-            const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][c]);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float v = bf2f(e[u]);
-                ss += v * v;
-            }
-        }
-        ss = wsum(ss);
-        const float rinv = 1.f / sqrtf(ss / (float)K + eps);
-#pragma unroll
-        for (int c = 0; c < LPR; ++c) {
-            const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][c]);
-            const float gg[8] = {g[c][0].x, g[c][0].y, g[c][0].z, g[c][0].w, g[c][1].x, g[c][1].y, g[c][1].z, g[c][1].w};
-            uint32_t pk[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                pk[u] = pack2_bf16(bf2f(e[2 * u]) * rinv * gg[2 * u], bf2f(e[2 * u + 1]) * rinv * gg[2 * u + 1]);
-                bad |= nonfinite_bits(pk[u]);
-            }
-            *reinterpret_cast<uint4*>(xs + r * XS + c * 512 + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        }
-    }
-    if (blockIdx.x == 0 && out.nonfinite && __any(nonfinite_seen(bad)) && lane == 0) atomicOr(out.nonfinite, 1u);
-    __syncthreads();
-    const int k0 = wave * KS * 16 + 8 * hi;
-    bf16x8 a0[KS], a1[KS];
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-        a0[i] = *reinterpret_cast<const bf16x8*>(xs + l32 * XS + k0 + 16 * i);
-        a1[i] = *reinterpret_cast<const bf16x8*>(xs + (32 + l32) * XS + k0 + 16 * i);
-    }
-    __syncthreads();                                   // the staging area becomes the reduction buffer
-    auto& red = *reinterpret_cast<float (*)[GEMM_WAVES][2][16][64]>(smem);
-    const bool two = rows > 32;
     f32x16 c0 = f32x16{}, c1 = f32x16{}, u0 = f32x16{}, u1 = f32x16{};
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
@@ -292,12 +223,107 @@ __global__ __launch_bounds__(256) void residual_reduce(const float* __restrict__
     if (out.nonfinite && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(out.nonfinite, 1u);
 }
 
+// The same residual with the next AdaRMSNorm: one workgroup per row, 4
+// consecutive elements per thread (threads past N / 4 only join the row
+// sum). h_out <- bf16(h_in + sum_c part[c]) (chunk order, as residual_reduce;
+// kc may be 0), x <- bf16(x - dt h) when x is set, and with nn.gamma set
+// y <- bf16(h * rsqrt(mean(h^2) + eps) * gamma): the row's sum of squares in
+// FP32, each thread's four in order, then the wave sum, then the waves in
+// order. With a packed y, workgroups past `rows` write the padding rows of
+// its 64 row slots as zeros. Reports a non-finite h, x or y element.
+__global__ __launch_bounds__(512) void residual_norm_rows(const float* __restrict__ part, int kc,
+                                                          const uint16_t* h_in, uint16_t* h_out, int rows, int N,
+                                                          uint16_t* __restrict__ x, float dt, NormNext nn,
+                                                          uint32_t* nonfinite) {
+    __shared__ float wsums[8];
+    const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+    const int k0 = 4 * t;
+    const bool own = k0 < N;
+    uint16_t* y = static_cast<uint16_t*>(nn.y);
+    if (m >= rows) {                     // packed padding rows (whole workgroup)
+        if (own) *reinterpret_cast<uint2*>(y + apack_index(m, k0)) = make_uint2(0, 0);
+        return;
+    }
+    const long long off = (long long)m * N + k0, total = (long long)rows * N;
+    constexpr int MAXC = 8192 / SPLITK_CHUNK;
+    float4 p[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+        p[c] = own && c < kc ? *reinterpret_cast<const float4*>(part + c * total + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint2 hr = own ? *reinterpret_cast<const uint2*>(h_in + off) : make_uint2(0, 0);
+    const uint2 xr = own && x ? *reinterpret_cast<const uint2*>(x + off) : make_uint2(0, 0);
+    const float h0[4] = {__uint_as_float(hr.x << 16), __uint_as_float(hr.x & 0xffff0000u),
+                         __uint_as_float(hr.y << 16), __uint_as_float(hr.y & 0xffff0000u)};
+    const float x0[4] = {__uint_as_float(xr.x << 16), __uint_as_float(xr.x & 0xffff0000u),
+                         __uint_as_float(xr.y << 16), __uint_as_float(xr.y & 0xffff0000u)};
+    float hn[4];
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float v = 0.f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c)
+            if (c < kc) v += (e == 0 ? p[c].x : e == 1 ? p[c].y : e == 2 ? p[c].z : p[c].w);
+        hn[e] = bf2f(f2bf(h0[e] + v));
+        bad |= !finite_f(hn[e]);
+    }
+    if (own) *reinterpret_cast<uint2*>(h_out + off) = make_uint2(pack2_bf16(hn[0], hn[1]), pack2_bf16(hn[2], hn[3]));
+    if (own && x) {
+        float xn[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xn[e] = x0[e] - dt * hn[e];
+            bad |= !finite_f(xn[e]);
+        }
+        *reinterpret_cast<uint2*>(x + off) = make_uint2(pack2_bf16(xn[0], xn[1]), pack2_bf16(xn[2], xn[3]));
+    }
+    if (nn.gamma) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += hn[e] * hn[e];
+        ss = wsum(ss);
+        if (lane == 0) wsums[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int w = 0; w < nw; ++w) tot += wsums[w];
+        const float rinv = 1.f / sqrtf(tot / (float)N + nn.eps);
+        if (own) {
+            const float4 g = *reinterpret_cast<const float4*>(nn.gamma + k0);
+            const uint32_t y01 = pack2_bf16(hn[0] * rinv * g.x, hn[1] * rinv * g.y);
+            const uint32_t y23 = pack2_bf16(hn[2] * rinv * g.z, hn[3] * rinv * g.w);
+            bad |= nonfinite_seen(nonfinite_bits(y01) | nonfinite_bits(y23)) != 0;
+            *reinterpret_cast<uint2*>(y + (nn.packed ? apack_index(m, k0) : off)) = make_uint2(y01, y23);
+        }
+    }
+    if (nonfinite && __any(bad) && lane == 0) atomicOr(nonfinite, 1u);
+}
+
 // ------------------------------------------------------------ host side -----
+static void launch_norm_rows(const float* part, int kc, const void* h_in, void* h_out, int rows, int N, void* x,
+                             float dt, const NormNext& nn, uint32_t* nonfinite, hipStream_t s) {
+    const int threads = ((N / 4 + 63) / 64) * 64;
+    const int grid = nn.gamma && nn.packed ? 64 : rows;
+    residual_norm_rows<<<grid, threads, 0, s>>>(part, kc, static_cast<const uint16_t*>(h_in),
+                                                static_cast<uint16_t*>(h_out), rows, N, static_cast<uint16_t*>(x),
+                                                dt, nn, nonfinite);
+}
+
+pa_status norm_rows(const void* h_in, void* h_out, int rows, int N, const NormNext& nn, uint32_t* nonfinite,
+                    hipStream_t s) {
+    PA_CHECK_ARG(nn.gamma && nn.y && N % 128 == 0 && N <= 2048 && rows >= 1 && rows <= 64, PA_ESHAPE,
+                 "norm: unsupported shape rows %d, N %d", rows, N);
+    launch_norm_rows(nullptr, 0, h_in, h_out, rows, N, nullptr, 0.f, nn, nonfinite, s);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
 pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, int rows, int K, int N, void* x,
-                           float dt, uint32_t* nonfinite, float* part, hipStream_t s) {
+                          float dt, uint32_t* nonfinite, float* part, hipStream_t s, const NormNext* nn) {
     const int kc = K / SPLITK_CHUNK;
     PA_CHECK_ARG(K % SPLITK_CHUNK == 0 && kc >= 1 && K <= 8192 && N % 32 == 0 && rows >= 1 && rows <= 64, PA_ESHAPE,
                  "residual projection: unsupported shape rows %d, K %d, N %d", rows, K, N);
+    PA_CHECK_ARG(!nn || (nn->gamma && nn->y && N % 128 == 0 && N <= 2048), PA_ESHAPE,
+                 "residual projection: the fused norm needs N a multiple of 128, at most 2048 (got %d)", N);
     const uint16_t* aa = static_cast<const uint16_t*>(a);
     const uint16_t* ww = static_cast<const uint16_t*>(w);
     const dim3 grid(N / 32, kc), block(GEMM_WAVES * 64);
@@ -306,6 +332,11 @@ pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, in
     else
         gemm_splitk_part<false><<<grid, block, 0, s>>>(aa, ww, rows, N, K, part);
     PA_LAUNCHED();
+    if (nn) {
+        launch_norm_rows(part, kc, h, h, rows, N, x, dt, *nn, nonfinite, s);
+        PA_LAUNCHED();
+        return PA_OK;
+    }
     GemmOut o{};
     o.h = static_cast<uint16_t*>(h);
     o.x = static_cast<uint16_t*>(x);
@@ -326,9 +357,8 @@ bool packed_residual_supported(int K, int N) {
     return K % 1024 == 0 && (kc == 1 || kc == 2 || kc == 3 || kc == 4 || kc == 6 || kc == 8) && N % 32 == 0;
 }
 
-pa_status packed_norm_qkv(const void* x, int rows, int model_dim, const float* gamma, float eps, const void* w_p,
-                          int hq, int hkv, int d, void* q, void* k, void* v, uint32_t* nonfinite, bool q_packed,
-                          hipStream_t s) {
+pa_status packed_qkv(const void* y_p, int rows, int model_dim, const void* w_p, int hq, int hkv, int d, void* q,
+                     void* k, void* v, bool q_packed, hipStream_t s) {
     GemmOut o{};
     if (q_packed) {
         o.q_nrb = qpack_blocks(rows, hq, hkv);
@@ -340,30 +370,28 @@ pa_status packed_norm_qkv(const void* x, int rows, int model_dim, const float* g
     o.v = static_cast<uint16_t*>(v);
     o.nq = hq * d;
     o.nk = hkv * d;
-    o.nonfinite = nonfinite;
     const int n = (hq + 2 * hkv) * d;
-    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    const uint16_t* yy = static_cast<const uint16_t*>(y_p);
     const uint16_t* ww = static_cast<const uint16_t*>(w_p);
     if (model_dim == 512)
-        gemm_norm_packed<PK_QKV, 4><<<n / 32, GEMM_WAVES * 64, 0, s>>>(xx, gamma, eps, ww, nullptr, rows, n, o, nullptr);
+        gemm_packed<PK_QKV, 4><<<n / 32, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
     else
-        gemm_norm_packed<PK_QKV, 8><<<n / 32, GEMM_WAVES * 64, 0, s>>>(xx, gamma, eps, ww, nullptr, rows, n, o, nullptr);
+        gemm_packed<PK_QKV, 8><<<n / 32, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
     PA_LAUNCHED();
     return PA_OK;
 }
 
-pa_status packed_norm_gateup(const void* h, int rows, int model_dim, int ffn_dim, const float* gamma, float eps,
-                             const void* wg_p, const void* wu_p, void* act_p, uint32_t* nonfinite, hipStream_t s) {
+pa_status packed_gateup(const void* y_p, int rows, int model_dim, int ffn_dim, const void* wg_p, const void* wu_p,
+                        void* act_p, hipStream_t s) {
     GemmOut o{};
-    o.nonfinite = nonfinite;
-    const uint16_t* xx = static_cast<const uint16_t*>(h);
+    const uint16_t* yy = static_cast<const uint16_t*>(y_p);
     const uint16_t* g = static_cast<const uint16_t*>(wg_p);
     const uint16_t* u = static_cast<const uint16_t*>(wu_p);
     uint16_t* a = static_cast<uint16_t*>(act_p);
     if (model_dim == 512)
-        gemm_norm_packed<PK_GATEUP, 4><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(xx, gamma, eps, g, u, rows, ffn_dim, o, a);
+        gemm_packed<PK_GATEUP, 4><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
     else
-        gemm_norm_packed<PK_GATEUP, 8><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(xx, gamma, eps, g, u, rows, ffn_dim, o, a);
+        gemm_packed<PK_GATEUP, 8><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
     PA_LAUNCHED();
     return PA_OK;
 }

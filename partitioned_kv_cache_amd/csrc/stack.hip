@@ -20,7 +20,7 @@
 namespace pa {
 
 struct StackWs {
-    size_t h, q, k, v, o, attn, part, ffn, total;
+    size_t h, y, q, k, v, o, attn, part, ffn, total;
 };
 
 // the out-projection runs split over K when Hq * D allows it (always on
@@ -39,6 +39,8 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
         return at;
     };
     w.h = take(n * m * 2);
+    // the normalised operand of the next QKV or gate/up GEMM (packed: 64 row slots)
+    w.y = take((st->packed ? 64 : n) * m * 2);
     // packed Q (operand order) pads each KV head's rows to whole 32-row blocks
     const size_t qpk = st->packed ? (size_t)qpack_blocks(st->rows, st->n_q_heads, (int)hkv) * 32 * hkv * d : 0;
     w.q = take((qpk > n * st->n_q_heads * d ? qpk : n * st->n_q_heads * d) * 2);
@@ -49,12 +51,10 @@ static StackWs stack_layout(const Ring* r, const pa_stack* st, size_t attn_bytes
     w.attn = take(attn_bytes);
     // FP32 partials of the split-K out-projection
     w.part = take(oproj_split(r, st) ? residual_splitk_bytes(st->rows, st->n_q_heads * (int)d, st->model_dim) : 0);
-    if (st->packed)   // packed activation (64 row slots), then the down projection's split-K partials
-        w.ffn = take(st->ffn_dim ? align_up((size_t)64 * st->ffn_dim * 2, 256) +
-                                       residual_splitk_bytes(st->rows, st->ffn_dim, st->model_dim)
-                                 : 0);
-    else
-        w.ffn = take(st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0);
+    // SwiGLU activation (packed: 64 row slots), then the down projection's split-K partials
+    w.ffn = take(st->ffn_dim ? align_up((size_t)(st->packed ? 64 : n) * st->ffn_dim * 2, 256) +
+                                   residual_splitk_bytes(st->rows, st->ffn_dim, st->model_dim)
+                             : 0);
     w.total = off;
     return w;
 }
@@ -132,74 +132,66 @@ extern "C" pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* st, vo
     const StackWs w = stack_layout(r, st, attn);
     PA_CHECK_ARG(ws_bytes >= w.total, PA_ERANGE, "pa_denoise_step: workspace %zu < %zu bytes", ws_bytes, w.total);
     char* base = static_cast<char*>(ws);
-    void *h = base + w.h, *q = base + w.q, *k = base + w.k, *v = base + w.v, *o = base + w.o;
+    void *h = base + w.h, *y = base + w.y, *q = base + w.q, *k = base + w.k, *v = base + w.v, *o = base + w.o;
     void* aws = base + w.attn;
     float* opart = reinterpret_cast<float*>(base + w.part);
     const bool osplit = oproj_split(r, st);
     void* fws = base + w.ffn;
     hipStream_t strm = static_cast<hipStream_t>(stream);
-    const size_t xbytes = (size_t)st->rows * st->model_dim * 2;
-    PA_HIP(hipMemcpyAsync(h, x, xbytes, hipMemcpyDeviceToDevice, strm));
     const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
     const int in_dim = st->n_q_heads * d;
     const size_t wqkv_layer = (size_t)(st->n_q_heads + 2 * hkv) * d * st->model_dim;
     const size_t wo_layer = (size_t)st->model_dim * in_dim;
     const size_t wf_layer = (size_t)st->ffn_dim * st->model_dim;
-    const size_t fws_bytes = st->ffn_dim ? ffn_swiglu_workspace_bytes(st->rows, st->model_dim, st->ffn_dim) : 0;
-    if (st->packed) {
-        // Same chain on fragment-packed weights; the attention output and the
-        // SwiGLU activation are written packed by their producers.
-        for (int l = 0; l < st->num_layers; ++l) {
-            const bool last = l + 1 == st->num_layers;
-            const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
-            const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
-            s = packed_norm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq,
-                                st->n_q_heads, hkv, d, q, k, v, nonfinite, true, strm);
-            if (s != PA_OK) return s;
-            const pattn_args a = attn_args(st, l);
-            s = pattn_step_apacked(ring, &a, q, k, v, o, aws, attn, stream, true);
-            if (s != PA_OK) return s;
-            s = residual_splitk(o, wo, true, h, st->rows, in_dim, st->model_dim, last && !st->ffn_dim ? x : nullptr,
-                                st->dt, nonfinite, opart, strm);
-            if (s != PA_OK) return s;
-            if (st->ffn_dim) {
-                s = packed_norm_gateup(h, st->rows, st->model_dim, st->ffn_dim, gamma_ffn + l * gamma_layer_stride,
-                                       st->eps, static_cast<const uint16_t*>(st->w_gate) + l * wf_layer,
-                                       static_cast<const uint16_t*>(st->w_up) + l * wf_layer, fws, nonfinite, strm);
-                if (s != PA_OK) return s;
-                float* part = reinterpret_cast<float*>(static_cast<char*>(fws) +
-                                                       align_up((size_t)64 * st->ffn_dim * 2, 256));
-                s = residual_splitk(fws, static_cast<const uint16_t*>(st->w_down) + l * wf_layer, true, h,
-                                    st->rows, st->ffn_dim, st->model_dim, last ? x : nullptr, st->dt, nonfinite,
-                                    part, strm);
-                if (s != PA_OK) return s;
-            }
-        }
-        return PA_OK;
-    }
+    void* act = fws;
+    float* fpart = reinterpret_cast<float*>(static_cast<char*>(fws) +
+                                            align_up((size_t)(st->packed ? 64 : st->rows) * st->ffn_dim * 2, 256));
+    const bool pk = st->packed != 0;
+    // Every GEMM that starts from h reads y = bf16(AdaRMSNorm(h)), formed by
+    // the kernel that finished h (the first layer's by a norm pass that also
+    // copies x into h), in the GEMM's own operand layout. Packed and unpacked
+    // weights run the same normalisation and the same summation orders, so
+    // their x agree bit for bit.
+    auto norm_of = [&](const float* g) { return NormNext{g, st->eps, y, pk}; };
+    NormNext nn = norm_of(gamma);
+    s = norm_rows(x, h, st->rows, st->model_dim, nn, nonfinite, strm);
+    if (s != PA_OK) return s;
     for (int l = 0; l < st->num_layers; ++l) {
         const bool last = l + 1 == st->num_layers;
         const uint16_t* wq = static_cast<const uint16_t*>(st->w_qkv) + l * wqkv_layer;
         const uint16_t* wo = static_cast<const uint16_t*>(st->w_o) + l * wo_layer;
-        s = ada_rmsnorm_qkv(h, st->rows, st->model_dim, gamma + l * gamma_layer_stride, st->eps, wq, st->n_q_heads,
-                            hkv, d, q, k, v, nonfinite, nullptr, 0, stream);
+        s = pk ? packed_qkv(y, st->rows, st->model_dim, wq, st->n_q_heads, hkv, d, q, k, v, true, strm)
+               : qkv_proj(y, st->rows, st->model_dim, wq, st->n_q_heads, hkv, d, q, k, v, strm);
         if (s != PA_OK) return s;
         const pattn_args a = attn_args(st, l);
-        s = pattn_step(ring, &a, q, k, v, o, aws, attn, stream);
+        s = pk ? pattn_step_apacked(ring, &a, q, k, v, o, aws, attn, stream, true)
+               : pattn_step(ring, &a, q, k, v, o, aws, attn, stream);
         if (s != PA_OK) return s;
-        // the Euler update rides on the layer's last projection; the split-K
-        // form sums in the packed path's order
+        // the out-projection's residual forms the FFN's operand, or the next
+        // layer's, and applies the Euler update after the last projection
+        const float* g_next = st->ffn_dim ? gamma_ffn + l * gamma_layer_stride
+                                          : (last ? nullptr : gamma + (l + 1) * gamma_layer_stride);
+        nn = norm_of(g_next);
         void* xl = last && !st->ffn_dim ? x : nullptr;
-        s = osplit ? residual_splitk(o, wo, false, h, st->rows, in_dim, st->model_dim, xl, st->dt, nonfinite, opart,
-                                     strm)
-                   : oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, xl, st->dt, nonfinite, stream);
+        if (osplit) {
+            s = residual_splitk(o, wo, pk, h, st->rows, in_dim, st->model_dim, xl, st->dt, nonfinite, opart, strm,
+                                g_next ? &nn : nullptr);
+        } else {   // unpacked weights only: single-kernel out-projection, then the norm in place
+            s = oproj_residual(o, wo, h, st->rows, in_dim, st->model_dim, xl, st->dt, nonfinite, stream);
+            if (s == PA_OK && g_next) s = norm_rows(h, h, st->rows, st->model_dim, nn, nonfinite, strm);
+        }
         if (s != PA_OK) return s;
         if (st->ffn_dim) {
-            s = ffn_swiglu(h, st->rows, st->model_dim, st->ffn_dim, gamma_ffn + l * gamma_layer_stride, st->eps,
-                           static_cast<const uint16_t*>(st->w_gate) + l * wf_layer,
-                           static_cast<const uint16_t*>(st->w_up) + l * wf_layer,
-                           static_cast<const uint16_t*>(st->w_down) + l * wf_layer, last ? x : nullptr, st->dt,
-                           nonfinite, fws, fws_bytes, stream);
+            const uint16_t* wg = static_cast<const uint16_t*>(st->w_gate) + l * wf_layer;
+            const uint16_t* wu = static_cast<const uint16_t*>(st->w_up) + l * wf_layer;
+            const uint16_t* wd = static_cast<const uint16_t*>(st->w_down) + l * wf_layer;
+            s = pk ? packed_gateup(y, st->rows, st->model_dim, st->ffn_dim, wg, wu, act, strm)
+                   : gateup_proj(y, st->rows, st->model_dim, st->ffn_dim, wg, wu, act, strm);
+            if (s != PA_OK) return s;
+            const float* g2 = last ? nullptr : gamma + (l + 1) * gamma_layer_stride;
+            nn = norm_of(g2);
+            s = residual_splitk(act, wd, pk, h, st->rows, st->ffn_dim, st->model_dim, last ? x : nullptr, st->dt,
+                                nonfinite, fpart, strm, g2 ? &nn : nullptr);
             if (s != PA_OK) return s;
         }
     }

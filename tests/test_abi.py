@@ -197,12 +197,13 @@ def test_packed_stack_workspace_and_shape_checks_without_device():
     plain = L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 8, w[0], w[1], 1e-6, 1 / 16, 0.1, **full))
     packed = L.pa_denoise_step_workspace_bytes(r, L.pa_stack(18, 51, 1024, 8, w[0], w[1], 1e-6, 1 / 16, 0.1,
                                                              packed=1, **full))
-    # packed operands span all 64 row slots: the attention output (Hq D = 2048)
-    # and the SwiGLU activation (4096) each take 13 more rows of bf16; packed Q
-    # pads 51 x 8 = 408 query rows to 13 blocks of 32 (416 rows of D = 256)
+    # packed operands span all 64 row slots: the normalised GEMM operand
+    # (model 1024), the attention output (Hq D = 2048) and the SwiGLU
+    # activation (4096) each take 13 more rows of bf16; packed Q pads
+    # 51 x 8 = 408 query rows to 13 blocks of 32 (416 rows of D = 256)
     up = lambda b: (b + 255) // 256 * 256
-    assert packed - plain == (up(64 * 2048 * 2) - up(51 * 2048 * 2) + up(64 * 4096 * 2) - up(51 * 4096 * 2)
-                              + up(416 * 256 * 2) - up(408 * 256 * 2))
+    assert packed - plain == (up(64 * 1024 * 2) - up(51 * 1024 * 2) + up(64 * 2048 * 2) - up(51 * 2048 * 2)
+                              + up(64 * 4096 * 2) - up(51 * 4096 * 2) + up(416 * 256 * 2) - up(408 * 256 * 2))
     for kw in (dict(packed=2), dict(packed=1, model_dim=768), dict(packed=1, ffn_dim=5120)):
         md = kw.pop("model_dim", 1024)
         f = dict(full, ffn_dim=kw.pop("ffn_dim", 4096))
@@ -228,9 +229,9 @@ def test_split_k_workspace_sizes_without_device():
     w = [_fake(3), _fake(4)]
     st = lambda hq: L.pa_stack(18, 51, 1024, hq, w[0], w[1], 1e-6, 1 / 16, 0.1)  # noqa: E731
     attn = lambda hq: L.pattn_workspace_bytes(r, L.pattn_args(0, 1, hq, 51, 1 / 16, L.PA_BF16))  # noqa: E731
-    # h, q, k, v, o, attention, out-projection partials (Hq D = 2048: 4 chunks)
-    base = lambda hq: (up(51 * 1024 * 2) + up(51 * hq * 256 * 2) + 2 * up(51 * 256 * 2) + up(51 * hq * 256 * 2)  # noqa: E731
-                       + up(attn(hq)))
+    # h, normalised operand y, q, k, v, o, attention, out-projection partials (Hq D = 2048: 4 chunks)
+    base = lambda hq: (2 * up(51 * 1024 * 2) + up(51 * hq * 256 * 2) + 2 * up(51 * 256 * 2)  # noqa: E731
+                       + up(51 * hq * 256 * 2) + up(attn(hq)))
     assert L.pa_denoise_step_workspace_bytes(r, st(8)) == base(8) + up(4 * 51 * 1024 * 4)
     # Hq D = 768 is not a whole number of chunks: no partials, single-kernel out-projection
     assert L.pa_denoise_step_workspace_bytes(r, st(3)) == base(3)
