@@ -4,12 +4,14 @@
 // action chunk ("Reflex: Real-Time VLA Control through Streaming Inference"
 // paper review, §6 Table 7) -- and describe each step's suffix as recomputed
 // while the cached regions are only read (§3 Eq. 1 text). Per layer the
-// chain is AdaRMSNorm fused into the packed QKV projection (§3 Eq. 2; §2/§4
-// fused operators), partitioned attention (Eq. 1), and a residual
-// out-projection, optionally followed by the SwiGLU FFN; the Euler update of
-// the flow state is fused into the last projection of the last layer. The
-// out-projection, the FFN, the velocity (last layer's stream) and the Euler
-// step are readings: the pages give no layer glue.
+// chain is AdaRMSNorm (§3 Eq. 2) and the packed QKV projection, partitioned
+// attention (Eq. 1), and a residual out-projection, optionally followed by
+// the SwiGLU FFN; the Euler update of the flow state is fused into the last
+// projection of the last layer. The norm is fused (§2/§4 fused operators)
+// into the kernel that finishes h, which writes the normalised operand of the
+// next GEMM, so no GEMM workgroup renormalises the rows. The out-projection,
+// the FFN, the velocity (last layer's stream) and the Euler step are
+// readings: the pages give no layer glue.
 //
 // Everything is enqueued on one stream with no host synchronisation and no
 // allocation, so a caller can capture the whole step in a graph and replay
