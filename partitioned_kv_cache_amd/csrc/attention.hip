@@ -349,8 +349,11 @@ __device__ __forceinline__ void wait_vmem() {
 // [call layer x KV head][32-row block][D / 16][64 lanes][8] (rows padded to
 // whole blocks), so each Q load is 1 KB contiguous across the wave instead of
 // 32 B from each of 32 rows. The stack's QKV projection writes it that way.
-template <int D, bool FUSED = false, bool QPK = false>
-__global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
+// WAVES: 8 (two per SIMD, the throughput form) or 4 (one per SIMD, for
+// launches too small to fill the chip: each wave's key loop then runs at the
+// single-wave rate).
+template <int D, bool FUSED = false, bool QPK = false, int WAVES = MFMA_WAVES>
+__global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
                                                                           long long q_layer, int hq, int group,
                                                                           int m_rows, KvSource src, int chunk,
                                                                           float scale_log2, Partials part, int parts,
@@ -362,8 +365,9 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     constexpr int PLANE = KT * 64;           // bytes per plane (KT keys x 32 dims x 2 B)
     constexpr int TILE = DB * PLANE;         // bytes per K or V tile
     constexpr int NBLK = TILE / 1024;        // 1 KB direct-to-LDS loads per tile and tensor
-    constexpr int DPW = (NBLK + MFMA_WAVES - 1) / MFMA_WAVES;   // loads per wave, per tile and tensor
-    static_assert(NBLK % 2 == 0 && (NBLK <= MFMA_WAVES || NBLK % MFMA_WAVES == 0), "tile / wave split");
+    constexpr int DPW = (NBLK + WAVES - 1) / WAVES;   // loads per wave, per tile and tensor
+    constexpr int RPW = WAVES * 32;                   // query rows per workgroup
+    static_assert(NBLK % 2 == 0 && (NBLK <= WAVES || NBLK % WAVES == 0) && WAVES % 2 == 0, "tile / wave split");
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     // XCD-aware placement. Workgroups go to the 8 XCDs round-robin by id, and
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     if (unit >= parts * part.lg_count) return;                 // id padding, whole workgroup
     const int split = unit % parts, lg = unit / parts, rblk = slot % row_blocks;
     const int lb = lg / src.hkv, g = lg % src.hkv;
-    const int row0 = rblk * ROWS_PER_WG + wave * 32;
+    const int row0 = rblk * RPW + wave * 32;
     const int row = row0 + l32;
     const bool active = row0 < m_rows;       // wave-uniform
 
@@ -421,15 +425,16 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
     const int skip_at = pinned + src.skip_at, skip_len = src.skip_len;   // in context-key units
 
     // Direct-to-LDS loads: one 1 KB load = 16 keys x 64 B of one plane, lane
-    // -> (key, 16-byte chunk). Wave w loads blocks w, w + 8, ... of a tile;
-    // block b is plane b / 2, keys 16 (b % 2) .. + 15. With 8 waves every
-    // block a wave loads has the same keys, so one address per tile serves.
+    // -> (key, 16-byte chunk). Wave w loads blocks w, w + WAVES, ... of a
+    // tile; block b is plane b / 2, keys 16 (b % 2) .. + 15. With an even wave
+    // count every block a wave loads has the same keys, so one address per
+    // tile serves.
     const int dma_key = lane >> 2, dma_pos = lane & 3;
     const int kq = wave & 1;
     const int key_in_tile = kq * 16 + dma_key;
     const int kchunk = (dma_pos ^ ((key_in_tile >> 2) & 3)) << 3;   // K plane rotation
     auto issue_tile = [&](int t, char* kbuf, char* vbuf) {
-        if (DPW * MFMA_WAVES > NBLK && wave >= NBLK) return;         // fewer blocks than waves
+        if (DPW * WAVES > NBLK && wave >= NBLK) return;               // fewer blocks than waves
         const int j = min(k_begin + t * KT + key_in_tile, k_end - 1);  // ragged tail: a valid key, masked later
         const bool dyn = j >= n_cached;
         const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap + (j >= skip_at ? skip_len : 0));
@@ -438,10 +443,10 @@ __global__ __launch_bounds__(MFMA_WAVES * 64, MFMA_OCC) void partial_mfma(const 
         const uint16_t* vp = (dyn ? dv : rv) + off + (dma_pos << 3);
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
-            const int blk = __builtin_amdgcn_readfirstlane(wave + i * MFMA_WAVES);
-            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(kp + i * (MFMA_WAVES / 2) * 32),
+            const int blk = __builtin_amdgcn_readfirstlane(wave + i * WAVES);
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(kp + i * (WAVES / 2) * 32),
                                              (LDS_AS void*)(kbuf + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(vp + i * (MFMA_WAVES / 2) * 32),
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(vp + i * (WAVES / 2) * 32),
                                              (LDS_AS void*)(vbuf + blk * 1024), 16, 0, 0);
         }
     };
@@ -898,16 +903,24 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
     const float scale_log2 = scale * 1.4426950408889634f;
     const int d = r->cfg.head_dim;
     if (p.mfma) {
-        const int row_blocks = (p.m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG;
+        // A launch that leaves most CUs idle with 8-wave workgroups (the
+        // single-layer calls of the stack) runs 4-wave ones: one wave per
+        // SIMD, twice the workgroups, each key loop at the single-wave rate.
         const int units = p.parts * p.lg_count;
+        const bool narrow = d == 256 && !q2 && units * ((p.m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG) <= 64;
+        const int rpw = narrow ? ROWS_PER_WG / 2 : ROWS_PER_WG;
+        const int row_blocks = (p.m_rows + rpw - 1) / rpw;
         const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         const uint16_t* qq2 = static_cast<const uint16_t*>(q2);
-#define PA_MFMA(DD, FU, QP)                                                                                      \
-    partial_mfma<DD, FU, QP><<<grid, MFMA_WAVES * 64, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
+#define PA_MFMA(DD, FU, QP, ...)                                                                                 \
+    partial_mfma<DD, FU, QP, ##__VA_ARGS__><<<grid, rpw * 2, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
                                                                    scale_log2, part, p.parts, row_blocks, qq2,       \
                                                                    q2_layer, m1)
-        if (q_packed) {
+        if (narrow) {
+            if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES / 2);
+            else PA_MFMA(256, false, false, MFMA_WAVES / 2);
+        } else if (q_packed) {
             if (d == 256) PA_MFMA(256, false, true);
             else if (d == 128) PA_MFMA(128, false, true);
             else PA_MFMA(64, false, true);
