@@ -570,14 +570,17 @@ template <> struct CombineRaw<uint16_t> {
 // Merges partial rows [row_lo, row_hi); output row index row - row_lo.
 // APK: the output (bf16, one layer) goes to the fragment-packed activation
 // layout of the out-projection's operand (token m < 64, column head * D + d).
-template <typename TO, int D, typename PO, bool APK = false>
+// A wave takes JW of the four 8-dim slices of a (32-row, 32-dim) block: 4
+// (256 B contiguous per slice and split) when the launch is large, 1 when it
+// would leave most CUs idle, so that the per-wave merge is a quarter as long.
+template <typename TO, int D, typename PO, bool APK = false, int JW = 4>
 __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int row_lo, int row_hi, int group, int hq,
                                                int hkv, long long out_layer, TO* out) {
-    constexpr int DB = D / 32;
-    // one wave per (32-row block, 32-dim block): 1 KB contiguous per split
+    constexpr int DB = D / 32, NJ = 4 / JW;
+    static_assert(JW == 1 || JW == 2 || JW == 4, "slices per wave");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int unit = blockIdx.x * 4 + wave, lg = blockIdx.y;
-    const int row0 = (row_lo & ~31) + (unit / DB) * 32, b = unit % DB;
+    const int row0 = (row_lo & ~31) + (unit / (DB * NJ)) * 32, b = (unit / NJ) % DB, j0 = (unit % NJ) * JW;
     if (row0 >= row_hi) return;
     const int row = row0 + l32;
     const bool ok = row >= row_lo && row < row_hi;
@@ -585,22 +588,22 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     // Online merge over batches of splits: (mx, lsum, acc) is the merge of
     // the splits seen so far, referenced to mx.
     float mx = -INFINITY, lsum = 0.f;
-    float4 acc[4];
+    float4 acc[JW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < JW; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     using R = CombineRaw<PO>;
     constexpr int BATCH = R::BATCH;
     for (int s0 = 0; s0 < n_parts; s0 += BATCH) {
         float2 ml[BATCH];
-        typename R::T v[BATCH][4];
+        typename R::T v[BATCH][JW];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             const bool has = s0 + i < n_parts;         // uniform: slots past the end load nothing, weigh 0
             const int s = has ? s0 + i : 0;
             ml[i] = ok && has ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
-            const PO* op = part.optr<PO>() + part.oblock(s, lg, row0) + (b * 4) * 256 + lane * 4;
+            const PO* op = part.optr<PO>() + part.oblock(s, lg, row0) + (b * 4 + j0) * 256 + lane * 4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[i][j] = has ? R::load(op + j * 256) : typename R::T{};
+            for (int j = 0; j < JW; ++j) v[i][j] = has ? R::load(op + j * 256) : typename R::T{};
         }
         float bm = mx;
 #pragma unroll
@@ -609,13 +612,13 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
         const float sc = exp2f(mx - bm);                // 0 while mx is -inf
         lsum *= sc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { acc[j].x *= sc; acc[j].y *= sc; acc[j].z *= sc; acc[j].w *= sc; }
+        for (int j = 0; j < JW; ++j) { acc[j].x *= sc; acc[j].y *= sc; acc[j].z *= sc; acc[j].w *= sc; }
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             const float w = ml[i].x == -INFINITY ? 0.f : exp2f(ml[i].x - bm);   // an empty partial weighs 0
             lsum += w * ml[i].y;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 const float4 vv = R::widen(v[i][j]);
                 acc[j].x += w * vv.x; acc[j].y += w * vv.y;
                 acc[j].z += w * vv.z; acc[j].w += w * vv.w;
@@ -629,15 +632,15 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     if (APK) {
         const int col = (g * group + r % group) * D + 32 * b + 4 * hi;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            st4(out + apack_index(r / group, col + 8 * j),
+        for (int j = 0; j < JW; ++j)
+            st4(out + apack_index(r / group, col + 8 * (j0 + j)),
                 make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv));
         return;
     }
     TO* orow = out + lb * out_layer + ((long long)(r / group) * hq + g * group + r % group) * D + 32 * b + 4 * hi;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        st4(orow + 8 * j, make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv));
+    for (int j = 0; j < JW; ++j)
+        st4(orow + 8 * (j0 + j), make_float4(acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv));
 }
 
 // ---------------------------------------------------------------------------
@@ -957,25 +960,30 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
                                 int row_hi = -1) {
     const int d = r->cfg.head_dim, hkv = r->cfg.num_kv_heads;
     if (row_hi < 0) row_hi = p.m_rows;
-    const int units = (row_hi - (row_lo & ~31) + 31) / 32 * (d / 32);   // (32-row, 32-dim) blocks, one wave each
-    const dim3 grid((units + 3) / 4, p.lg_count);
+    const int units = (row_hi - (row_lo & ~31) + 31) / 32 * (d / 32);   // (32-row, 32-dim) blocks
+    // at most 64 workgroups of whole blocks (a single-layer call): one slice
+    // per wave instead (larger launches, the 18-layer decode pass included,
+    // measured no gain)
+    const bool thin = units * p.lg_count <= 256;
+    const dim3 grid((units * (thin ? 4 : 1) + 3) / 4, p.lg_count);
+#define PA_COMBINE_JW(TO, DD, PO, APK)                                                                         \
+    do {                                                                                                       \
+        if (thin)                                                                                              \
+            combine<TO, DD, PO, APK, 1><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,  \
+                                                                  hkv, out_layer, static_cast<TO*>(out));      \
+        else                                                                                                   \
+            combine<TO, DD, PO, APK, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,  \
+                                                                  hkv, out_layer, static_cast<TO*>(out));      \
+    } while (0)
 #define PA_COMBINE(TO, DD)                                                                                  \
     do {                                                                                                    \
-        if (p.o_bytes == 2)                                                                                 \
-            combine<TO, DD, uint16_t><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
-                                                                hkv, out_layer, static_cast<TO*>(out));     \
-        else                                                                                                \
-            combine<TO, DD, float><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,    \
-                                                             hkv, out_layer, static_cast<TO*>(out));        \
+        if (p.o_bytes == 2) PA_COMBINE_JW(TO, DD, uint16_t, false);                                          \
+        else PA_COMBINE_JW(TO, DD, float, false);                                                            \
     } while (0)
 #define PA_COMBINE_APK(DD)                                                                                   \
     do {                                                                                                     \
-        if (p.o_bytes == 2)                                                                                  \
-            combine<uint16_t, DD, uint16_t, true><<<grid, 256, 0, stream>>>(                                 \
-                part, n_parts, row_lo, row_hi, p.group, hq, hkv, out_layer, static_cast<uint16_t*>(out));    \
-        else                                                                                                 \
-            combine<uint16_t, DD, float, true><<<grid, 256, 0, stream>>>(                                    \
-                part, n_parts, row_lo, row_hi, p.group, hq, hkv, out_layer, static_cast<uint16_t*>(out));    \
+        if (p.o_bytes == 2) PA_COMBINE_JW(uint16_t, DD, uint16_t, true);                                      \
+        else PA_COMBINE_JW(uint16_t, DD, float, true);                                                        \
     } while (0)
     if (out_dtype == PA_BF16_APACKED) {
         if (d == 256) PA_COMBINE_APK(256);
@@ -998,6 +1006,7 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
     }
 #undef PA_COMBINE
 #undef PA_COMBINE_APK
+#undef PA_COMBINE_JW
     PA_LAUNCHED();
     return PA_OK;
 }
