@@ -30,7 +30,7 @@ namespace pa {
 constexpr int KT = 32;           // key granularity of splits, keys per LDS tile
 constexpr int MFMA_WAVES = 8;    // waves per workgroup: two per SIMD, 32 query rows each
 constexpr int MFMA_OCC = 1;      // workgroups per CU
-constexpr int NBUF = 4;          // K/V tile buffers in the LDS ring: NBUF - 1 tiles in flight
+constexpr int NBUF = 2;          // K/V tile buffers in the LDS ring: NBUF - 1 tiles in flight
 constexpr int N_XCD = 8;         // accelerator complex dies, one L2 each
 constexpr int ROWS_PER_WG = MFMA_WAVES * 32;
 constexpr float RESCALE_SLACK = 8.f;   // log2 units the running max may lag the true max
@@ -487,15 +487,14 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
             pv_tile<D>(lds_buffer<NBUF + J, TILE>(), voff, pf, acc);
         }
     };
-    static_assert(NBUF == 4, "the prologue and the unrolled loop below assume four buffers");
+    // One tile in flight while one is consumed: two buffers measured faster
+    // than three or four (fewer loads outstanding per CU) on every launch
+    // shape here.
+    static_assert(NBUF == 2, "the prologue and the unrolled loop below assume two buffers");
     issue_tile(0, lds_buffer<0, TILE>(), lds_buffer<NBUF + 0, TILE>());
-    if (1 < n_tiles) issue_tile(1, lds_buffer<1, TILE>(), lds_buffer<NBUF + 1, TILE>());
-    if (2 < n_tiles) issue_tile(2, lds_buffer<2, TILE>(), lds_buffer<NBUF + 2, TILE>());
     for (int t = 0; t < n_tiles; t += NBUF) {
         step(std::integral_constant<int, 0>{}, t);
         step(std::integral_constant<int, 1>{}, t + 1);
-        step(std::integral_constant<int, 2>{}, t + 2);
-        step(std::integral_constant<int, 3>{}, t + 3);
     }
 
     l_run += __shfl_xor(l_run, 32);
