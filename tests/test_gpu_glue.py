@@ -319,12 +319,14 @@ class StackRig:
 
 
 # Hq * D = 2048 runs the out-projection split over K; 768 (three heads) is
-# not a multiple of the 512-wide chunk and takes the single-kernel path.
-@pytest.mark.parametrize("hq,layers", [(8, 18), (3, 4)])
-def test_denoise_step_matches_oracle_chain(hq, layers):
+# not a multiple of the 512-wide chunk and takes the single-kernel path. A
+# 768-wide stream runs the residual-and-norm kernel with 3 waves per row.
+@pytest.mark.parametrize("hq,layers,model", [(8, 18, 1024), (3, 4, 1024), (8, 3, 768)])
+def test_denoise_step_matches_oracle_chain(hq, layers, model):
     L = lib()
-    _banner(f"denoise step {layers} layers, {hq} query heads")
-    s = S3 if hq == 8 else S3.with_(name=f"stack_hq{hq}", cfg_id=81, n_q_heads=hq, num_layers=layers)
+    _banner(f"denoise step {layers} layers, {hq} query heads, model {model}")
+    s = S3 if (hq, layers, model) == (8, 18, 1024) else S3.with_(
+        name=f"stack_hq{hq}_m{model}", cfg_id=81 + model // 256, n_q_heads=hq, num_layers=layers, model_dim=model)
     rig = StackRig(s, 3)
     gam = rig.oracle_gammas(2, 0)
     gam32 = np.stack(gam).astype(np.float32)
