@@ -792,11 +792,15 @@ struct Plan {
 static int valu_row_blocks(int m) { return (m + VALU_ROWS - 1) / VALU_ROWS; }
 
 // Choose the split count: as many workgroups as fit at once (one per CU on
-// 256 CUs) without a partial second wave, and no split shorter than 128 keys.
-static int default_splits(int lg_count, int row_blocks, int max_keys) {
+// 256 CUs) without a partial second wave, and no split shorter than
+// min_keys: three 32-key tiles for the matrix-core kernel; half a tile for
+// the vector kernel, whose waves walk their keys one at a time (splits are
+// still whole 32-key chunks: the 88-key fp32 call went from 1 to 3 splits,
+// 24.6 to 12.7 us).
+static int default_splits(int lg_count, int row_blocks, int max_keys, int min_keys) {
     const int base = lg_count * row_blocks;
     int s = 256 * MFMA_OCC / base;
-    int by_len = max_keys / 96;    // at least three 32-key tiles per split
+    int by_len = max_keys / min_keys;
     if (by_len < 1) by_len = 1;
     if (s > by_len) s = by_len;
     if (s > 64) s = 64;
@@ -841,7 +845,7 @@ static pa_status plan_for(const Ring* r, int layer_begin, int num_layers, int hq
     const int row_blocks = p->mfma ? (p->m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG : valu_row_blocks(p->m_rows);
     p->mpad = (p->m_rows + 31) / 32 * 32;
     const int max_keys = (int)(r->seq_len() + n_dyn);
-    const int s_max = req_splits ? req_splits : default_splits(p->lg_count, row_blocks, max_keys);
+    const int s_max = req_splits ? req_splits : default_splits(p->lg_count, row_blocks, max_keys, p->mfma ? 96 : KT / 2);
     p->max_parts = s_max + extra;
     p->total = r->cached_tokens() + n_dyn;
     if (p->total > 0) {
