@@ -19,7 +19,7 @@ from partitioned_kv_cache_amd import configs, synth
 
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_helpers import Scenario, dev, host, lib, rel_err  # noqa: E402
+from tests.gpu_helpers import Scenario, dev, host, lib, rel_err, tdtype  # noqa: E402
 
 BAR = 2e-2
 
@@ -28,13 +28,17 @@ def _banner(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("layers,G,n_act,cap,frames,splits", [(3, 16, 51, 30, 9, 0), (2, 1, 1, 4, 2, 0),
-                                                                 (2, 5, 17, 8, 3, 3), (18, 16, 51, 30, 9, 0)])
-def test_fused_pass_matches_oracle_and_separate_passes(layers, G, n_act, cap, frames, splits):
+# The last case is the benchmark's launch: 18 layers, 16 streams, bf16 outputs.
+@pytest.mark.parametrize("layers,G,n_act,cap,frames,splits,odt", [(3, 16, 51, 30, 9, 0, "f32"),
+                                                                     (2, 1, 1, 4, 2, 0, "f32"),
+                                                                     (2, 5, 17, 8, 3, 3, "f32"),
+                                                                     (18, 16, 51, 30, 9, 0, "f32"),
+                                                                     (18, 16, 51, 30, 9, 0, "bf16")])
+def test_fused_pass_matches_oracle_and_separate_passes(layers, G, n_act, cap, frames, splits, odt):
     L = lib()
     s = configs.SHARED_KV.with_(name=f"fused_{layers}_{G}_{n_act}", cfg_id=300 + layers + G, num_layers=layers,
                                 n_streams=G, tail_capacity=cap, n_dyn=n_act)
-    _banner(f"fused pass layers={layers} streams={G} action tokens={n_act} cap={cap} splits={splits}")
+    _banner(f"fused pass layers={layers} streams={G} action tokens={n_act} cap={cap} splits={splits} out={odt}")
     sc = Scenario(s)
     for f in range(frames):
         sc.push(f)
@@ -44,23 +48,24 @@ def test_fused_pass_matches_oracle_and_separate_passes(layers, G, n_act, cap, fr
     tv = synth.normal((layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILV, 5)
     q, kd, vd = synth.suffix_qkv(s, 0, 3)
     qd = synth.decode_q(s, frames, 0)
-    a = L.pattn_args(0, layers, s.n_q_heads, n_act, s.scale, L.PA_F32, splits)
-    d = L.decode_args(0, layers, s.n_q_heads, G, cap, s.scale, L.PA_F32, splits)
+    od = L.PA_F32 if odt == "f32" else L.PA_BF16
+    a = L.pattn_args(0, layers, s.n_q_heads, n_act, s.scale, od, splits)
+    d = L.decode_args(0, layers, s.n_q_heads, G, cap, s.scale, od, splits)
     wsb = L.pattn_fused_workspace_bytes(sc.ring, a, d)
     assert wsb > 0
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    out = torch.empty((layers, n_act, s.n_q_heads, D), dtype=torch.float32, device="cuda")
-    out_d = torch.empty((layers, G, s.n_q_heads, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((layers, n_act, s.n_q_heads, D), dtype=tdtype(odt), device="cuda")
+    out_d = torch.empty((layers, G, s.n_q_heads, D), dtype=tdtype(odt), device="cuda")
     tk_d, tv_d, len_d = dev(tk), dev(tv), dev(lens)
     L.pattn_fused_step(sc.ring, a, dev(q), dev(kd), dev(vd), out, d, dev(qd), tk_d, tv_d, len_d, out_d, ws, wsb)
     # the two separate passes on the same inputs
-    sep = sc.run_step(q, kd, vd, num_splits=splits)
+    sep = sc.run_step(q, kd, vd, out_dtype=od, num_splits=splits)
     dwsb = L.pattn_decode_workspace_bytes(sc.ring, d)
     dws = torch.empty(dwsb, dtype=torch.uint8, device="cuda")
     out_d2 = torch.empty_like(out_d)
     L.pattn_decode(sc.ring, d, dev(qd), tk_d, tv_d, len_d, out_d2, dws, dwsb)
     torch.cuda.synchronize()
-    got_a, got_d, sep_d = host(out).astype(np.float64), host(out_d).astype(np.float64), host(out_d2).astype(np.float64)
+    got_a, got_d, sep_d = (synth.widen(host(t)) for t in (out, out_d, out_d2))
     worst = 0.0
     for l in sorted({0, layers // 2, layers - 1}):
         ref_a = sc.oracle_step(q, kd, vd, l)

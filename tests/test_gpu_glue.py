@@ -21,7 +21,7 @@ from partitioned_kv_cache_amd import configs, synth
 
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_helpers import Scenario, dev, host, lib, rel_err  # noqa: E402
+from tests.gpu_helpers import Scenario, dev, host, lib, rel_err, tdtype  # noqa: E402
 
 BAR = 2e-2
 S3 = configs.PI05_18L
@@ -145,11 +145,13 @@ def test_nonfinite_flag_trips_on_injected_inf_and_nan():
 
 # ----------------------------------------------------------- decode readers --
 
-def test_decode_readers_private_tails():
-    """16 streams x 1 query token over the long-history cache plus private tails."""
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_decode_readers_private_tails(odt):
+    """16 streams x 1 query token over the long-history cache plus private tails
+    (bf16 outputs: the benchmark's launch)."""
     L = lib()
     s = configs.SHARED_KV
-    _banner("decode readers")
+    _banner(f"decode readers out={odt}")
     sc = Scenario(s)
     for f in range(9):
         sc.push(f)
@@ -160,20 +162,20 @@ def test_decode_readers_private_tails():
     tv = synth.normal((s.num_layers, G, cap, hkv, D), "bf16", s.cfg_id, synth.T_TAILV, 99)
     tk_d, tv_d, len_d = dev(tk), dev(tv), dev(lens0)
     ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
-    a = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_F32)
+    a = L.decode_args(0, s.num_layers, s.n_q_heads, G, cap, s.scale, L.PA_F32 if odt == "f32" else L.PA_BF16)
     kn, vn = synth.decode_kv(s, 9, 0)
     L.pattn_append_private(sc.ring, a, tk_d, tv_d, len_d, dev(kn), dev(vn), ovf)
     q = synth.decode_q(s, 9, 0)
     wsb = L.pattn_decode_workspace_bytes(sc.ring, a)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    out = torch.empty((s.num_layers, G, s.n_q_heads, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((s.num_layers, G, s.n_q_heads, D), dtype=tdtype(odt), device="cuda")
     L.pattn_decode(sc.ring, a, dev(q), tk_d, tv_d, len_d, out, ws, wsb)
     torch.cuda.synchronize()
     lens1 = host(len_d)
     want_lens = np.minimum(lens0 + 1, cap)
     assert np.array_equal(lens1, want_lens)
     assert int(host(ovf)[0]) == 1 << 3
-    got = host(out).astype(np.float64)
+    got = synth.widen(host(out))
     worst = 0.0
     for l in (0, 9, 17):
         tails = decode.PrivateTails(G, cap, hkv, D)
