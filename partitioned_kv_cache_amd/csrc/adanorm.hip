@@ -29,96 +29,141 @@ constexpr int MAX_T = 16;            // timesteps per ada_gamma call
 struct TArr { float t[MAX_T]; };
 
 
-__device__ __forceinline__ float bf_round(float v) { return bf2f(f2bf(v)); }
 
 // ------------------------------------------------------------- gamma MLP ----
+// Both layers are n_t dot products per output row over an operand held in LDS
+// as [n_t][K] bf16. KL adjacent lanes share one output row: lane q of the
+// group takes the 8-wide k chunks q, q + KL, q + 2 KL, ... (weight loads of a
+// group are KL x 16 B contiguous), NF chunk loads per lane in flight at once
+// (16-lane groups and 8 loads measured fastest for the 1024-wide output layer),
+// products by v_dot2c_f32_bf16 (two bf16 pairs into an FP32 accumulator); a
+// few row-local lane exchanges then finish each sum.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int KL, int NF>
+struct RowDots {
+    const uint16_t* w;    // this lane group's weight row
+    int nc;               // chunks of 8 k in the row
+    int q;                // lane within the group
+    uint4 wv[NF];
+
+    __device__ __forceinline__ void load(int c0) {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            const int c = c0 + u * KL;
+            wv[u] = c < nc ? *reinterpret_cast<const uint4*>(w + c * 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    // acc[i] += the row's dot product with x_i over every chunk of this lane;
+    // the first group's loads must already be issued by load(q).
+    __device__ __forceinline__ void run(const uint16_t* xs, int n_t, float (&acc)[MAX_T]) {
+        const int K = nc * 8;
+        for (int c0 = q; c0 < nc; c0 += KL * NF) {
+            if (c0 != q) load(c0);
+#pragma unroll
+            for (int u = 0; u < NF; ++u) {
+                const int c = c0 + u * KL;
+                if (c >= nc) break;
+#pragma unroll
+                for (int i = 0; i < MAX_T; ++i) {
+                    if (i < n_t) {
+                        const uint4 xv = *reinterpret_cast<const uint4*>(xs + i * K + c * 8);
+                        float a = acc[i];
+                        a = dot2_bf16(wv[u].x, xv.x, a);
+                        a = dot2_bf16(wv[u].y, xv.y, a);
+                        a = dot2_bf16(wv[u].z, xv.z, a);
+                        acc[i] = dot2_bf16(wv[u].w, xv.w, a);
+                    }
+                }
+            }
+        }
+    }
+};
+
+// Sum over the KL (4, 8 or 16) adjacent lanes of a group, the same value in each.
+template <int KL>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(KL == 4 || KL == 8 || KL == 16, "lane group of 4, 8 or 16");
+#define PA_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false))
+    v += PA_DPP(v, 0xB1);                     // quad_perm [1, 0, 3, 2]
+    v += PA_DPP(v, 0x4E);                     // quad_perm [2, 3, 0, 1]
+    if (KL >= 8) v += PA_DPP(v, 0x141);       // row_half_mirror: the other quad of the 8
+    if (KL == 16) v += PA_DPP(v, 0x140);      // row_mirror: the other half of the 16
+#undef PA_DPP
+    return v;
+}
+
+constexpr int GH_KL = 4, GH_NF = 8;    // hidden layer: K = cond <= 512
+constexpr int GO_KL = 16, GO_NF = 8;   // output layer: K = hidden <= 4096
+constexpr int GH_ROWS = 256 / 64 * (64 / GH_KL);   // hidden units per workgroup (64)
+constexpr int GO_ROWS = 256 / 64 * (64 / GO_KL);   // outputs per workgroup (16)
+
 // Hidden layer: a[l][i][j] = bf16(SiLU(W1[l][j] . c_i + b1[l][j])), with
-// c_i = bf16([emb(t_i); state]).
-// grid (ceil(hidden / 256), L), block 256, dynamic LDS n_t * cond floats.
+// c_i = bf16([emb(t_i); state]) built in LDS by each workgroup (one sincos
+// per timestep and frequency).
+// grid (hidden / GH_ROWS, L), block 256, dynamic LDS n_t * cond bf16.
 __global__ __launch_bounds__(256) void gamma_hidden(const uint16_t* w1, const uint16_t* b1, const uint16_t* state,
                                                     TArr ts, int n_t, int cond_emb, int state_dim, int hidden,
                                                     uint16_t* a_out) {
-    extern __shared__ float cs[];
+    extern __shared__ uint16_t cs[];
     const int cond = cond_emb + state_dim, half = cond_emb / 2;
-    const int l = blockIdx.y;
+    const int l = blockIdx.y, lane = threadIdx.x & 63;
+    const int j = blockIdx.x * GH_ROWS + (threadIdx.x >> 6) * (64 / GH_KL) + lane / GH_KL;
+    RowDots<GH_KL, GH_NF> rd{w1 + ((long long)l * hidden + j) * cond, cond / 8, lane % GH_KL, {}};
+    rd.load(rd.q);
     const float log2_base = 13.287712379549449f;   // log2(10000)
-    for (int idx = threadIdx.x; idx < n_t * cond; idx += blockDim.x) {
-        const int i = idx / cond, k = idx % cond;
-        float v;
-        if (k < cond_emb) {
-            const int f = k < half ? k : k - half;
-            const float w = exp2f(-(float)f / (float)half * log2_base);
-            v = k < half ? sinf(ts.t[i] * w) : cosf(ts.t[i] * w);
-        } else {
-            v = bf2f(state[k - cond_emb]);
-        }
-        cs[idx] = bf_round(v);
+    for (int idx = threadIdx.x; idx < n_t * half; idx += blockDim.x) {
+        const int i = idx / half, f = idx - i * half;
+        float sn, cn;
+        sincosf(ts.t[i] * exp2f(-(float)f / (float)half * log2_base), &sn, &cn);
+        cs[i * cond + f] = f2bf(sn);
+        cs[i * cond + half + f] = f2bf(cn);
+    }
+    for (int idx = threadIdx.x; idx < n_t * state_dim; idx += blockDim.x) {
+        const int i = idx / state_dim, k = idx - i * state_dim;
+        cs[i * cond + cond_emb + k] = state[k];
     }
     __syncthreads();
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= hidden) return;
     float acc[MAX_T];
 #pragma unroll
     for (int i = 0; i < MAX_T; ++i) acc[i] = 0.f;
-    const uint16_t* wr = w1 + ((long long)l * hidden + j) * cond;
-    for (int k = 0; k < cond; k += 8) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(wr + k);
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float w = bf2f(e[u]);
-#pragma unroll
-            for (int i = 0; i < MAX_T; ++i)
-                if (i < n_t) acc[i] += w * cs[i * cond + k + u];
-        }
-    }
+    rd.run(cs, n_t, acc);
     const float bias = bf2f(b1[(long long)l * hidden + j]);
 #pragma unroll
     for (int i = 0; i < MAX_T; ++i) {
         if (i < n_t) {
-            const float h = acc[i] + bias;
-            const float s = h / (1.f + expf(-h));
-            a_out[((long long)l * n_t + i) * hidden + j] = f2bf(s);
+            const float h = group_sum<GH_KL>(acc[i]) + bias;
+            if (rd.q == 0) a_out[((long long)l * n_t + i) * hidden + j] = f2bf(h / (1.f + expf(-h)));
         }
     }
 }
 
 // Output layer: gamma[l][i][m] = 1 + b2[l][m] + W2[l][m] . a[l][i].
-// One wave per 4 outputs; grid (model / 16, L), block 256, dynamic LDS n_t * hidden bf16.
+// grid (model / GO_ROWS, L), block 256, dynamic LDS n_t * hidden bf16.
 __global__ __launch_bounds__(256) void gamma_out(const uint16_t* w2, const uint16_t* b2, const uint16_t* a_in, int n_t,
                                                  int hidden, int model, float* gamma) {
     extern __shared__ uint16_t as[];
-    const int l = blockIdx.y;
+    const int l = blockIdx.y, lane = threadIdx.x & 63;
+    const int m = blockIdx.x * GO_ROWS + (threadIdx.x >> 6) * (64 / GO_KL) + lane / GO_KL;
+    RowDots<GO_KL, GO_NF> rd{w2 + ((long long)l * model + m) * hidden, hidden / 8, lane % GO_KL, {}};
+    rd.load(rd.q);       // in flight across the barrier that publishes the staged activations
     const uint16_t* a_l = a_in + (long long)l * n_t * hidden;
     for (int idx = threadIdx.x * 8; idx < n_t * hidden; idx += blockDim.x * 8)
         *reinterpret_cast<uint4*>(&as[idx]) = *reinterpret_cast<const uint4*>(a_l + idx);
     __syncthreads();
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int o = 0; o < 4; ++o) {
-        const int m = blockIdx.x * 16 + wave * 4 + o;
-        if (m >= model) break;
-        float acc[MAX_T];
+    float acc[MAX_T];
 #pragma unroll
-        for (int i = 0; i < MAX_T; ++i) acc[i] = 0.f;
-        const uint16_t* wr = w2 + ((long long)l * model + m) * hidden;
-        for (int k = lane * 8; k < hidden; k += 512) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(wr + k);
-            const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+    for (int i = 0; i < MAX_T; ++i) acc[i] = 0.f;
+    rd.run(as, n_t, acc);
+    const float bias = bf2f(b2[(long long)l * model + m]);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float w = bf2f(e[u]);
-#pragma unroll
-                for (int i = 0; i < MAX_T; ++i)
-                    if (i < n_t) acc[i] += w * bf2f(as[i * hidden + k + u]);
-            }
-        }
-        const float bias = bf2f(b2[(long long)l * model + m]);
-#pragma unroll
-        for (int i = 0; i < MAX_T; ++i) {
-            if (i < n_t) {
-                const float s = wsum(acc[i]);
-                if (lane == 0) gamma[((long long)l * n_t + i) * model + m] = 1.f + bias + s;
-            }
+    for (int i = 0; i < MAX_T; ++i) {
+        if (i < n_t) {
+            const float sum = group_sum<GO_KL>(acc[i]);
+            if (rd.q == 0) gamma[((long long)l * n_t + i) * model + m] = 1.f + bias + sum;
         }
     }
 }
@@ -444,10 +489,10 @@ static pa_status launch_gamma(const ada_mlp* m, const uint16_t* w1, const uint16
     TArr ts{};
     for (int i = 0; i < n_t; ++i) ts.t[i] = t[i];
     const int cond = m->cond_emb + m->state_dim;
-    gamma_hidden<<<dim3((m->hidden_dim + 255) / 256, n_layers), 256, n_t * cond * sizeof(float), s>>>(
+    gamma_hidden<<<dim3(m->hidden_dim / GH_ROWS, n_layers), 256, n_t * cond * sizeof(uint16_t), s>>>(
         w1, b1, state, ts, n_t, m->cond_emb, m->state_dim, m->hidden_dim, a_ws);
     PA_LAUNCHED();
-    gamma_out<<<dim3((m->model_dim + 15) / 16, n_layers), 256, n_t * m->hidden_dim * sizeof(uint16_t), s>>>(
+    gamma_out<<<dim3(m->model_dim / GO_ROWS, n_layers), 256, n_t * m->hidden_dim * sizeof(uint16_t), s>>>(
         w2, b2, a_ws, n_t, m->hidden_dim, m->model_dim, gamma);
     PA_LAUNCHED();
     return PA_OK;

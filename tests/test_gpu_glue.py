@@ -47,22 +47,35 @@ def _oracle_gamma(s, layer, t, state_bits):
     return adanorm.gamma(w1, b1, w2, b2, t, synth.widen(state_bits))
 
 
-def test_ada_gamma_batched_over_layers_and_steps():
+# The Pi0.5-like MLP (160 -> 1024 -> 1024, 18 layers, 10 steps); a minimal one
+# (hidden 64: most lanes of a wave hold no weights); one whose hidden width is
+# not a multiple of 1024 (a partial second pass over k) with 16 timesteps.
+GAMMA_SHAPES = [
+    (S3, 10),
+    (S3.with_(name="gamma_small", cfg_id=71, num_layers=2, state_dim=8, hidden_dim=64, model_dim=64), 3),
+    (S3.with_(name="gamma_wide", cfg_id=72, num_layers=3, hidden_dim=1536, model_dim=128), 16),
+]
+
+
+@pytest.mark.parametrize("shape", range(len(GAMMA_SHAPES)))
+def test_ada_gamma_batched_over_layers_and_steps(shape):
     L = lib()
-    layers = list(range(S3.num_layers))
-    _banner("ada_gamma 18 layers x 10 steps")
-    mlp = _mlp_dev(S3, layers)
-    state = synth.robot_state(S3, 3)
-    ts = stack.timesteps(10)
-    gamma = torch.empty((len(layers), 10, S3.model_dim), dtype=torch.float32, device="cuda")
-    wsb = L.ada_gamma_workspace_bytes(mlp, 10)
+    s, n_t = GAMMA_SHAPES[shape]
+    layers = list(range(s.num_layers))
+    _banner(f"ada_gamma {s.num_layers} layers x {n_t} steps, cond {s.cond_emb}+{s.state_dim}, "
+            f"hidden {s.hidden_dim}, model {s.model_dim}")
+    mlp = _mlp_dev(s, layers)
+    state = synth.robot_state(s, 3)
+    ts = [1.0 - i / n_t for i in range(n_t)]
+    gamma = torch.empty((len(layers), n_t, s.model_dim), dtype=torch.float32, device="cuda")
+    wsb = L.ada_gamma_workspace_bytes(mlp, n_t)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     L.ada_gamma(mlp, ts, dev(state), gamma, ws, wsb)
     g = host(gamma).astype(np.float64)
     worst = 0.0
-    for l in (0, 7, 17):
-        for i in (0, 4, 9):
-            worst = max(worst, rel_err(g[l, i], _oracle_gamma(S3, l, ts[i], state)))
+    for l in sorted({0, len(layers) // 2, len(layers) - 1}):
+        for i in sorted({0, n_t // 2, n_t - 1}):
+            worst = max(worst, rel_err(g[l, i], _oracle_gamma(s, l, ts[i], state)))
     _banner(f"gamma worst rel {worst:.3e}")
     assert worst <= BAR
 
