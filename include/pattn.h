@@ -299,14 +299,14 @@ pa_status pattn_fused_step(const rb_ring* ring, const pattn_args* args, const vo
  * accumulation; gamma is kept in FP32.
  * ====================================================================== */
 typedef struct {
-    const void* w1;            /* bf16 [L][hidden][cond_emb + state_dim] */
+    const void* w1;            /* bf16 [L][hidden][cond_emb + state_dim], 16-byte aligned */
     const void* b1;            /* bf16 [L][hidden] */
-    const void* w2;            /* bf16 [L][model][hidden] */
+    const void* w2;            /* bf16 [L][model][hidden], 16-byte aligned */
     const void* b2;            /* bf16 [L][model] */
     int32_t num_layers;        /* L stacked MLPs (one per layer) */
-    int32_t cond_emb;          /* 128 */
-    int32_t state_dim;         /* s, 0 <= s <= 128 */
-    int32_t hidden_dim;        /* multiple of 64 */
+    int32_t cond_emb;          /* 128 (any even width is accepted) */
+    int32_t state_dim;         /* s, 0 <= s <= 128; cond_emb + s a multiple of 8, at most 512 */
+    int32_t hidden_dim;        /* multiple of 64 in [64, 4096] */
     int32_t model_dim;         /* multiple of 64 */
 } ada_mlp;
 
@@ -314,7 +314,10 @@ size_t ada_gamma_workspace_bytes(const ada_mlp* mlp, int32_t n_t);
 
 /* gamma[l][i][:] = 1 + MLP_l([emb(t[i]); state]) for every layer l and
  * timestep i (a frame's ten steps in one call). t: HOST array [n_t];
- * state: device bf16 [state_dim]; gamma: device f32 [L][n_t][model_dim]. */
+ * state: device bf16 [state_dim]; gamma: device f32 [L][n_t][model_dim].
+ * 1 <= n_t <= 16 and n_t * hidden_dim <= 32768 (a workgroup stages the n_t
+ * hidden activations of its layer, 64 KB at most); other sizes, or an MLP
+ * outside the limits above, return PA_ESHAPE before any launch. */
 pa_status ada_gamma(const ada_mlp* mlp, const float* t, int32_t n_t, const void* state,
                     float* gamma, void* workspace, size_t ws_bytes, void* stream);
 

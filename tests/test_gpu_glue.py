@@ -49,11 +49,14 @@ def _oracle_gamma(s, layer, t, state_bits):
 
 # The Pi0.5-like MLP (160 -> 1024 -> 1024, 18 layers, 10 steps); a minimal one
 # (hidden 64: most lanes of a wave hold no weights); one whose hidden width is
-# not a multiple of 1024 (a partial second pass over k) with 16 timesteps.
+# not a multiple of 1024 (a partial second pass over k) with 16 timesteps; the
+# maximum sizes.
 GAMMA_SHAPES = [
     (S3, 10),
     (S3.with_(name="gamma_small", cfg_id=71, num_layers=2, state_dim=8, hidden_dim=64, model_dim=64), 3),
     (S3.with_(name="gamma_wide", cfg_id=72, num_layers=3, hidden_dim=1536, model_dim=128), 16),
+    # the largest call the library accepts: 16 timesteps x hidden 2048 (64 KB of staged activations), state 128
+    (S3.with_(name="gamma_max", cfg_id=73, num_layers=1, state_dim=128, hidden_dim=2048, model_dim=64), 16),
 ]
 
 
@@ -72,6 +75,10 @@ def test_ada_gamma_batched_over_layers_and_steps(shape):
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     L.ada_gamma(mlp, ts, dev(state), gamma, ws, wsb)
     g = host(gamma).astype(np.float64)
+    if n_t * s.hidden_dim * 2 == 65536:      # one step past the staging limit is refused before any launch
+        wide = _mlp_dev(s.with_(hidden_dim=2 * s.hidden_dim), layers)
+        with pytest.raises(L.PattnError, match="PA_ESHAPE"):
+            L.ada_gamma(wide, ts, dev(state), gamma, ws, wsb)
     worst = 0.0
     for l in sorted({0, len(layers) // 2, len(layers) - 1}):
         for i in sorted({0, n_t // 2, n_t - 1}):
