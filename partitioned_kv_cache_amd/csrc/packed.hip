@@ -38,10 +38,13 @@ __global__ __launch_bounds__(256) void pack_weight(const uint4* __restrict__ w, 
 }
 
 // ------------------------------------------------ projection (packed) ----
-// A workgroup owns 32 output columns (W block nb) and all 64 row slots of the
-// packed operand y; its 8 waves split K into KS 16-k steps each, load their
-// operand fragments straight from y (1 KB contiguous per wave load) and meet
-// in LDS for the reduction over waves.
+// A workgroup owns 32 output columns (W block nb) and one 32-row half of the
+// packed operand y (both halves of a column block get ids congruent mod 8, so
+// they run on one XCD and its L2 serves the weight block to both; a call of at
+// most 32 rows launches the first halves only). Its 8 waves split K into KS
+// 16-k steps each, load their operand fragments straight from y (1 KB
+// contiguous per wave load) and meet in LDS for the reduction over waves, in
+// wave order.
 enum PackedMode { PK_QKV = 0, PK_GATEUP = 1 };
 
 template <int MODE, int KS>
@@ -50,17 +53,21 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t
                                                                   const uint16_t* __restrict__ wp2, int rows, int N,
                                                                   GemmOut out, uint16_t* __restrict__ act_p) {
     constexpr int K = GEMM_WAVES * KS * 16, S = K / 16;
-    __shared__ float red[GEMM_WAVES][2][16][64];
+    __shared__ float red[GEMM_WAVES][16][64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int nb = blockIdx.x, n0 = nb * 32;
-    const bool two = rows > 32;
-    bf16x8 a0[KS], a1[KS], w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
+    int nb = blockIdx.x, half = 0;
+    if (rows > 32) {     // ids 16 j + 8 h + x: column block 8 j + x, row half h
+        nb = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
+        half = (blockIdx.x >> 3) & 1;
+        if (nb >= N / 32) return;                                   // id padding, whole workgroup
+    }
+    const int n0 = nb * 32;
+    bf16x8 a0[KS], w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
         const long long st = wave * KS + i;
-        a0[i] = *reinterpret_cast<const bf16x8*>(y + ((st * 2) * 64 + lane) * 8);
-        a1[i] = two ? *reinterpret_cast<const bf16x8*>(y + ((st * 2 + 1) * 64 + lane) * 8) : bf16x8{};
+        a0[i] = *reinterpret_cast<const bf16x8*>(y + ((st * 2 + half) * 64 + lane) * 8);
     }
     const long long wb = ((long long)nb * S + wave * KS) * 512 + lane * 8;
 #pragma unroll
@@ -68,44 +75,34 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t
         w1[i] = *reinterpret_cast<const bf16x8*>(wp1 + wb + i * 512);
         if (MODE == PK_GATEUP) w2[i] = *reinterpret_cast<const bf16x8*>(wp2 + wb + i * 512);
     }
-    f32x16 c0 = f32x16{}, c1 = f32x16{}, u0 = f32x16{}, u1 = f32x16{};
+    f32x16 c0 = f32x16{}, u0 = f32x16{};
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
         c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], w1[i], c0, 0, 0, 0);
-        if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], w1[i], c1, 0, 0, 0);
-        if (MODE == PK_GATEUP) {
-            u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], w2[i], u0, 0, 0, 0);
-            if (two) u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], w2[i], u1, 0, 0, 0);
-        }
+        if (MODE == PK_GATEUP) u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], w2[i], u0, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        red[wave][0][r][lane] = c0[r];
-        red[wave][1][r][lane] = c1[r];
-    }
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = c0[r];
     __syncthreads();
-    float cs[4];
+    float cs[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
+    for (int u = 0; u < 2; ++u) {
+        const int r = wave * 2 + u;
         float v = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][r][lane];
         cs[u] = v;
     }
     if (MODE == PK_GATEUP) {
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            red[wave][0][r][lane] = u0[r];
-            red[wave][1][r][lane] = u1[r];
-        }
+        for (int r = 0; r < 16; ++r) red[wave][r][lane] = u0[r];
         __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
-        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+    for (int u = 0; u < 2; ++u) {
+        const int r = wave * 2 + u;
+        const int m = 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
         const int n = n0 + l32;
         if (MODE == PK_QKV && out.q_nrb && n < out.nq) {
             // packed q: the padding rows of its last 32-row block are written
@@ -127,7 +124,7 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t
         } else {
             float up = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < GEMM_WAVES; ++ww) up += red[ww][blk][r][lane];
+            for (int ww = 0; ww < GEMM_WAVES; ++ww) up += red[ww][r][lane];
             const float gt = cs[u];
             act_p[apack_index(m, n)] = f2bf(gt / (1.f + __expf(-gt)) * up);
         }
@@ -357,6 +354,10 @@ bool packed_residual_supported(int K, int N) {
     return K % 1024 == 0 && (kc == 1 || kc == 2 || kc == 3 || kc == 4 || kc == 6 || kc == 8) && N % 32 == 0;
 }
 
+// Workgroups of gemm_packed: one per column block, or per (column block, row
+// half) in groups of 16 ids when rows > 32.
+static int packed_grid(int rows, int n) { return rows > 32 ? 16 * ((n / 32 + 7) / 8) : n / 32; }
+
 pa_status packed_qkv(const void* y_p, int rows, int model_dim, const void* w_p, int hq, int hkv, int d, void* q,
                      void* k, void* v, bool q_packed, hipStream_t s) {
     GemmOut o{};
@@ -373,10 +374,11 @@ pa_status packed_qkv(const void* y_p, int rows, int model_dim, const void* w_p, 
     const int n = (hq + 2 * hkv) * d;
     const uint16_t* yy = static_cast<const uint16_t*>(y_p);
     const uint16_t* ww = static_cast<const uint16_t*>(w_p);
+    const int grid = packed_grid(rows, n);
     if (model_dim == 512)
-        gemm_packed<PK_QKV, 4><<<n / 32, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
+        gemm_packed<PK_QKV, 4><<<grid, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
     else
-        gemm_packed<PK_QKV, 8><<<n / 32, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
+        gemm_packed<PK_QKV, 8><<<grid, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
     PA_LAUNCHED();
     return PA_OK;
 }
@@ -388,10 +390,11 @@ pa_status packed_gateup(const void* y_p, int rows, int model_dim, int ffn_dim, c
     const uint16_t* g = static_cast<const uint16_t*>(wg_p);
     const uint16_t* u = static_cast<const uint16_t*>(wu_p);
     uint16_t* a = static_cast<uint16_t*>(act_p);
+    const int grid = packed_grid(rows, ffn_dim);
     if (model_dim == 512)
-        gemm_packed<PK_GATEUP, 4><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
+        gemm_packed<PK_GATEUP, 4><<<grid, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
     else
-        gemm_packed<PK_GATEUP, 8><<<ffn_dim / 32, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
+        gemm_packed<PK_GATEUP, 8><<<grid, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
     PA_LAUNCHED();
     return PA_OK;
 }
