@@ -132,59 +132,56 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t
 }
 
 // ------------------------------------------ split-K residual projection ---
-// Workgroup (column block nb, chunk c) sums k in [SPLITK_CHUNK c,
-// SPLITK_CHUNK (c + 1)): wave w the slice of KS MFMA steps from
-// SPLITK_CHUNK c + 16 KS w, the 8 waves merged in wave order, into
-// part[c][m][n] (FP32, rows m < rows).
+// Workgroup (column block nb, chunk c; with rows > 32 one per 32-row half,
+// placed as in gemm_packed) sums k in [SPLITK_CHUNK c, SPLITK_CHUNK (c + 1)):
+// wave w the slice of KS MFMA steps from SPLITK_CHUNK c + 16 KS w, the 8
+// waves merged in wave order, into part[c][m][n] (FP32, rows m < rows).
 template <bool PACKED>
 __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_splitk_part(const uint16_t* __restrict__ a,
                                                                      const uint16_t* __restrict__ w, int rows, int N,
                                                                      int K, float* __restrict__ part) {
     constexpr int KS = SPLITK_KS;
-    __shared__ float red[GEMM_WAVES][2][16][64];
+    __shared__ float red[GEMM_WAVES][16][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int nb = blockIdx.x, c = blockIdx.y, n0 = nb * 32;
-    const bool two = rows > 32;
-    bf16x8 wf[KS], a0[KS], a1[KS];
+    const int c = blockIdx.y;
+    int nb = blockIdx.x, half = 0;
+    if (rows > 32) {     // ids 16 j + 8 h + x: column block 8 j + x, row half h (as gemm_packed)
+        nb = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
+        half = (blockIdx.x >> 3) & 1;
+        if (nb >= N / 32) return;                                   // id padding, whole workgroup
+    }
+    const int n0 = nb * 32;
+    bf16x8 wf[KS], a0[KS];
     if (PACKED) {
         const long long S = K / 16;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
             const long long st = (c * GEMM_WAVES + wave) * KS + i;
             wf[i] = *reinterpret_cast<const bf16x8*>(w + ((nb * S + st) * 64 + lane) * 8);
-            a0[i] = *reinterpret_cast<const bf16x8*>(a + ((st * 2) * 64 + lane) * 8);
-            a1[i] = two ? *reinterpret_cast<const bf16x8*>(a + ((st * 2 + 1) * 64 + lane) * 8) : bf16x8{};
+            a0[i] = *reinterpret_cast<const bf16x8*>(a + ((st * 2 + half) * 64 + lane) * 8);
         }
     } else {
-        const int k0 = c * SPLITK_CHUNK + wave * KS * 16 + 8 * hi;
-        const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+        const int k0 = c * SPLITK_CHUNK + wave * KS * 16 + 8 * hi, row = 32 * half + l32;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
             wf[i] = *reinterpret_cast<const bf16x8*>(w + (long long)(n0 + l32) * K + k0 + 16 * i);
-            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(a + (long long)l32 * K + k0 + 16 * i) : bf16x8{};
-            a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
+            a0[i] = row < rows ? *reinterpret_cast<const bf16x8*>(a + (long long)row * K + k0 + 16 * i) : bf16x8{};
         }
     }
-    f32x16 c0 = f32x16{}, c1 = f32x16{};
+    f32x16 c0 = f32x16{};
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wf[i], c0, 0, 0, 0);
-        if (two) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wf[i], c1, 0, 0, 0);
-    }
+    for (int i = 0; i < KS; ++i) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wf[i], c0, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        red[wave][0][r][lane] = c0[r];
-        red[wave][1][r][lane] = c1[r];
-    }
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = c0[r];
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
-        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+    for (int u = 0; u < 2; ++u) {
+        const int r = wave * 2 + u;
+        const int m = 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (m >= rows) continue;
         float v = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][r][lane];
         part[((long long)c * rows + m) * N + n0 + l32] = v;
     }
 }
@@ -314,6 +311,10 @@ pa_status norm_rows(const void* h_in, void* h_out, int rows, int N, const NormNe
     return PA_OK;
 }
 
+// Workgroups of gemm_packed and gemm_splitk_part (per K chunk): one per column block, or per (column block, row
+// half) in groups of 16 ids when rows > 32.
+static int packed_grid(int rows, int n) { return rows > 32 ? 16 * ((n / 32 + 7) / 8) : n / 32; }
+
 pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, int rows, int K, int N, void* x,
                           float dt, uint32_t* nonfinite, float* part, hipStream_t s, const NormNext* nn) {
     const int kc = K / SPLITK_CHUNK;
@@ -323,7 +324,7 @@ pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, in
                  "residual projection: the fused norm needs N a multiple of 128, at most 2048 (got %d)", N);
     const uint16_t* aa = static_cast<const uint16_t*>(a);
     const uint16_t* ww = static_cast<const uint16_t*>(w);
-    const dim3 grid(N / 32, kc), block(GEMM_WAVES * 64);
+    const dim3 grid(packed_grid(rows, N), kc), block(GEMM_WAVES * 64);
     if (packed)
         gemm_splitk_part<true><<<grid, block, 0, s>>>(aa, ww, rows, N, K, part);
     else
@@ -353,10 +354,6 @@ bool packed_residual_supported(int K, int N) {
     const int kc = K / 1024;
     return K % 1024 == 0 && (kc == 1 || kc == 2 || kc == 3 || kc == 4 || kc == 6 || kc == 8) && N % 32 == 0;
 }
-
-// Workgroups of gemm_packed: one per column block, or per (column block, row
-// half) in groups of 16 ids when rows > 32.
-static int packed_grid(int rows, int n) { return rows > 32 ? 16 * ((n / 32 + 7) / 8) : n / 32; }
 
 pa_status packed_qkv(const void* y_p, int rows, int model_dim, const void* w_p, int hq, int hkv, int d, void* q,
                      void* k, void* v, bool q_packed, hipStream_t s) {
