@@ -295,8 +295,16 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
     constexpr int K = GEMM_WAVES * KS * 16;
     __shared__ float red[GEMM_WAVES][2][16][64];
     __shared__ float rinv_s[64];
+    // the QKV projection of an already normalised operand: one 32-row half per
+    // workgroup (row_half_grid); otherwise all 64 row slots
+    constexpr bool HALVES = MODE == GEMM_QKV && !NORM;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int n0 = blockIdx.x * 32;
+    int nb = blockIdx.x, half = 0;
+    if (HALVES) {
+        row_half_block(rows, nb, half);
+        if (nb >= N / 32) return;                                   // id padding, whole workgroup
+    }
+    const int n0 = nb * 32;
     const int k0 = wave * KS * 16 + 8 * hi;
 
     bf16x8 wf[KS];
@@ -304,12 +312,13 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
 #pragma unroll
     for (int i = 0; i < KS; ++i) wf[i] = *reinterpret_cast<const bf16x8*>(wp + 16 * i);
 
-    const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+    const bool r0 = 32 * half + l32 < rows, r1 = !HALVES && 32 + l32 < rows;
     bf16x8 a0[KS], a1[KS];
     if (!NORM) {
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(a + (long long)l32 * K + k0 + 16 * i) : bf16x8{};
+            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 * half + l32) * K + k0 + 16 * i)
+                       : bf16x8{};
             a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
         }
     } else {
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
     }
 
     f32x16 c0 = f32x16{}, c1 = f32x16{};
-    const bool two = rows > 32;
+    const bool two = !HALVES && rows > 32;
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
         c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wf[i], c0, 0, 0, 0);
@@ -332,12 +341,14 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
         red[wave][1][r][lane] = c1[r];
     }
     __syncthreads();
-    // wave w finishes 4 of the 32 (block, register) pairs
+    // wave w finishes 4 of the 32 (block, register) pairs (2 of the 16 of its
+    // row half with HALVES)
     if (MODE == GEMM_QKV) {
+        constexpr int NU = HALVES ? 2 : 4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
-            const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+        for (int u = 0; u < NU; ++u) {
+            const int idx = wave * NU + u, blk = idx >> 4, r = idx & 15;
+            const int m = 32 * (blk + half) + 8 * (r >> 2) + 4 * hi + (r & 3);
             const int n = n0 + l32;
             if (m >= rows) continue;
             float v = 0.f;
@@ -367,7 +378,8 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
 // gemm_gateup: a workgroup owns 32 act columns; its 8 waves split K = model
 // (KS k-steps of 16 each) and compute both products for those columns; the
 // gate and up partial sums meet in LDS one after the other. Without NORM, x
-// is the already normalised operand.
+// is the already normalised operand and a workgroup owns one 32-row half of
+// it (row_half_grid); with NORM it forms and uses all 64 row slots.
 template <int KS, bool NORM = true>
 __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t* __restrict__ x,
                                                                   const float* __restrict__ gamma, float eps,
@@ -378,7 +390,12 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
     __shared__ float red[GEMM_WAVES][2][16][64];
     __shared__ float rinv_s[64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int n0 = blockIdx.x * 32;
+    int nb = blockIdx.x, half = 0;
+    if (!NORM) {
+        row_half_block(rows, nb, half);
+        if (nb >= F / 32) return;                                   // id padding, whole workgroup
+    }
+    const int n0 = nb * 32;
     const int k0 = wave * KS * 16 + 8 * hi;
     bf16x8 wg[KS], wu[KS];
     const long long wrow = (long long)(n0 + l32) * K + k0;
@@ -392,14 +409,14 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
         norm_fragments<KS>(x, gamma, eps, rows, rinv_s, a0, a1);
         if (blockIdx.x == 0 && nonfinite) report_nonfinite<KS>(a0, a1, nonfinite);
     } else {
-        const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
+        const int row = 32 * half + l32;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(x + (long long)l32 * K + k0 + 16 * i) : bf16x8{};
-            a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(x + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
+            a0[i] = row < rows ? *reinterpret_cast<const bf16x8*>(x + (long long)row * K + k0 + 16 * i) : bf16x8{};
+            a1[i] = bf16x8{};
         }
     }
-    const bool two = rows > 32;
+    const bool two = NORM && rows > 32;
     f32x16 g0 = f32x16{}, g1 = f32x16{}, u0 = f32x16{}, u1 = f32x16{};
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
@@ -410,8 +427,10 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
             u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wu[i], u1, 0, 0, 0);
         }
     }
-    // wave w finishes 4 of the 32 (row block, register) pairs: the gate sums first
-    float gs[4];
+    // wave w finishes 4 of the 32 (row block, register) pairs (2 of the 16 of
+    // its row half without NORM): the gate sums first
+    constexpr int NU = NORM ? 4 : 2;
+    float gs[NU];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         red[wave][0][r][lane] = g0[r];
@@ -419,8 +438,8 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
     }
     __syncthreads();
 #pragma unroll
-    for (int uix = 0; uix < 4; ++uix) {
-        const int idx = wave * 4 + uix, blk = idx >> 4, r = idx & 15;
+    for (int uix = 0; uix < NU; ++uix) {
+        const int idx = wave * NU + uix, blk = idx >> 4, r = idx & 15;
         float v = 0.f;
 #pragma unroll
         for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
@@ -434,9 +453,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
     }
     __syncthreads();
 #pragma unroll
-    for (int uix = 0; uix < 4; ++uix) {
-        const int idx = wave * 4 + uix, blk = idx >> 4, r = idx & 15;
-        const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+    for (int uix = 0; uix < NU; ++uix) {
+        const int idx = wave * NU + uix, blk = idx >> 4, r = idx & 15;
+        const int m = 32 * (blk + half) + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (m >= rows) continue;
         float u = 0.f;
 #pragma unroll
@@ -456,7 +475,7 @@ static bool gemm_k_supported(int K) {
 template <int MODE, bool NORM>
 static hipError_t launch_gemm(const uint16_t* a, const float* gamma, float eps, const uint16_t* w, int rows, int K,
                               int N, const GemmOut& o, hipStream_t s) {
-    const dim3 grid(N / 32), block(GEMM_WAVES * 64);
+    const dim3 grid(MODE == GEMM_QKV && !NORM ? row_half_grid(rows, N) : N / 32), block(GEMM_WAVES * 64);
     switch (K / 128) {
         case 2: gemm_skinny<MODE, 2, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
         case 4: gemm_skinny<MODE, 4, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
@@ -525,10 +544,10 @@ pa_status gateup_proj(const void* y, int rows, int model_dim, int ffn_dim, const
     uint16_t* a = static_cast<uint16_t*>(act);
     const dim3 block(GEMM_WAVES * 64);
     switch (model_dim / 128) {
-        case 2: gemm_gateup<2, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
-        case 4: gemm_gateup<4, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
-        case 6: gemm_gateup<6, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
-        default: gemm_gateup<8, false><<<ffn_dim / 32, block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        case 2: gemm_gateup<2, false><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        case 4: gemm_gateup<4, false><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        case 6: gemm_gateup<6, false><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
+        default: gemm_gateup<8, false><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(yy, nullptr, 0.f, wg, wu, rows, ffn_dim, a, nullptr); break;
     }
     PA_LAUNCHED();
     return PA_OK;

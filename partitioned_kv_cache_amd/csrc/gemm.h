@@ -39,6 +39,21 @@ __device__ __forceinline__ bool nonfinite_seen(uint32_t acc) { return (acc & 0x8
 
 constexpr int GEMM_WAVES = 8;
 
+// Workgroups of a 64-row projection that gives each workgroup 32 output
+// columns and one 32-row half of the operand: ids 16 j + 8 h + x take column
+// block 8 j + x and half h (both halves of a block on one XCD, sharing its
+// weights in L2), padded to whole groups of 16; with at most 32 rows, one per
+// column block. row_half_block decodes an id (nb >= N / 32 marks padding).
+inline int row_half_grid(int rows, int n) { return rows > 32 ? 16 * ((n / 32 + 7) / 8) : n / 32; }
+__device__ __forceinline__ void row_half_block(int rows, int& nb, int& half) {
+    nb = blockIdx.x;
+    half = 0;
+    if (rows > 32) {
+        nb = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
+        half = (blockIdx.x >> 3) & 1;
+    }
+}
+
 struct GemmOut {
     // GEMM_QKV: columns [0, nq) -> q, [nq, nq+nk) -> k, [nq+nk, nq+2nk) -> v
     uint16_t* q; uint16_t* k; uint16_t* v; int nq; int nk;

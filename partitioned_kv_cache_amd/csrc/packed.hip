@@ -56,12 +56,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t
     __shared__ float red[GEMM_WAVES][16][64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    int nb = blockIdx.x, half = 0;
-    if (rows > 32) {     // ids 16 j + 8 h + x: column block 8 j + x, row half h
-        nb = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
-        half = (blockIdx.x >> 3) & 1;
-        if (nb >= N / 32) return;                                   // id padding, whole workgroup
-    }
+    int nb, half;
+    row_half_block(rows, nb, half);
+    if (nb >= N / 32) return;                                       // id padding, whole workgroup
     const int n0 = nb * 32;
     bf16x8 a0[KS], w1[KS], w2[MODE == PK_GATEUP ? KS : 1];
 #pragma unroll
@@ -144,12 +141,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_splitk_part(const uin
     __shared__ float red[GEMM_WAVES][16][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int c = blockIdx.y;
-    int nb = blockIdx.x, half = 0;
-    if (rows > 32) {     // ids 16 j + 8 h + x: column block 8 j + x, row half h (as gemm_packed)
-        nb = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
-        half = (blockIdx.x >> 3) & 1;
-        if (nb >= N / 32) return;                                   // id padding, whole workgroup
-    }
+    int nb, half;
+    row_half_block(rows, nb, half);
+    if (nb >= N / 32) return;                                       // id padding, whole workgroup
     const int n0 = nb * 32;
     bf16x8 wf[KS], a0[KS];
     if (PACKED) {
@@ -311,10 +305,6 @@ pa_status norm_rows(const void* h_in, void* h_out, int rows, int N, const NormNe
     return PA_OK;
 }
 
-// Workgroups of gemm_packed and gemm_splitk_part (per K chunk): one per column block, or per (column block, row
-// half) in groups of 16 ids when rows > 32.
-static int packed_grid(int rows, int n) { return rows > 32 ? 16 * ((n / 32 + 7) / 8) : n / 32; }
-
 pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, int rows, int K, int N, void* x,
                           float dt, uint32_t* nonfinite, float* part, hipStream_t s, const NormNext* nn) {
     const int kc = K / SPLITK_CHUNK;
@@ -324,7 +314,7 @@ pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, in
                  "residual projection: the fused norm needs N a multiple of 128, at most 2048 (got %d)", N);
     const uint16_t* aa = static_cast<const uint16_t*>(a);
     const uint16_t* ww = static_cast<const uint16_t*>(w);
-    const dim3 grid(packed_grid(rows, N), kc), block(GEMM_WAVES * 64);
+    const dim3 grid(row_half_grid(rows, N), kc), block(GEMM_WAVES * 64);
     if (packed)
         gemm_splitk_part<true><<<grid, block, 0, s>>>(aa, ww, rows, N, K, part);
     else
@@ -371,7 +361,7 @@ pa_status packed_qkv(const void* y_p, int rows, int model_dim, const void* w_p, 
     const int n = (hq + 2 * hkv) * d;
     const uint16_t* yy = static_cast<const uint16_t*>(y_p);
     const uint16_t* ww = static_cast<const uint16_t*>(w_p);
-    const int grid = packed_grid(rows, n);
+    const int grid = row_half_grid(rows, n);
     if (model_dim == 512)
         gemm_packed<PK_QKV, 4><<<grid, GEMM_WAVES * 64, 0, s>>>(yy, ww, nullptr, rows, n, o, nullptr);
     else
@@ -387,7 +377,7 @@ pa_status packed_gateup(const void* y_p, int rows, int model_dim, int ffn_dim, c
     const uint16_t* g = static_cast<const uint16_t*>(wg_p);
     const uint16_t* u = static_cast<const uint16_t*>(wu_p);
     uint16_t* a = static_cast<uint16_t*>(act_p);
-    const int grid = packed_grid(rows, ffn_dim);
+    const int grid = row_half_grid(rows, ffn_dim);
     if (model_dim == 512)
         gemm_packed<PK_GATEUP, 4><<<grid, GEMM_WAVES * 64, 0, s>>>(yy, g, u, rows, ffn_dim, o, a);
     else
