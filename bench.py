@@ -307,6 +307,59 @@ def bench_small(args, torch, L, cfg, n_calls=2000):
             "cached_tokens": cfg.max_seq_len, "suffix": cfg.n_dyn, "layers": cfg.num_layers}
 
 
+def bench_adanorm_qkv(args, torch, L, configs, synth, n_calls=2000):
+    """One layer's fused AdaRMSNorm + packed QKV projection (ada_rmsnorm_qkv)
+    at the Pi0.5-like shape: 51 rows of a 1024-wide stream, W_qkv 1024 ->
+    (8 + 2) x 256. Microseconds per call, eager and graph-replayed, and the
+    rate over the bytes the call must move (weights, x, gamma, q/k/v)."""
+    s = configs.PI05_18L
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    rows, model, hq, hkv, d = s.n_dyn, s.model_dim, s.n_q_heads, s.n_kv_heads, s.head_dim
+    x = dev(synth.normal((rows, model), "bf16", s.cfg_id, synth.T_X, 9))
+    w = dev(synth.proj_weights(s, 0)[0])
+    gam = torch.ones(model, dtype=torch.float32, device="cuda")
+    q = torch.empty((rows, hq, d), dtype=torch.int16, device="cuda")
+    k = torch.empty((rows, hkv, d), dtype=torch.int16, device="cuda")
+    v = torch.empty((rows, hkv, d), dtype=torch.int16, device="cuda")
+    wsb = L.ada_rmsnorm_qkv_workspace_bytes(rows, model)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(st):
+        L.ada_rmsnorm_qkv(x, rows, model, gam, s.eps, w, hq, hkv, d, q, k, v, None, ws, wsb, st)
+
+    for _ in range(50):
+        call(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        call(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    per_graph = 20
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        cs = torch.cuda.current_stream()
+        for _ in range(per_graph):
+            call(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, n_calls // per_graph)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    g_us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+    n_out = (hq + 2 * hkv) * d
+    algo = model * n_out * 2 + rows * model * 2 + model * 4 + rows * n_out * 2
+    return {"workload": "pi05_like_adarmsnorm_qkv_1L", "rows": rows, "model_dim": model, "qkv_dim": n_out,
+            "us_per_call": round(el / n_calls * 1e6, 2), "us_per_call_graph": round(g_us, 2),
+            "algo_bytes": algo, "gbs_graph": round(algo / (g_us * 1e-6) / 1e9, 1)}
+
+
 def bench_stack(args, torch, L, configs, synth, full_layer=False):
     """Whole 18-layer denoising step of the Pi0.5-like stack, graph-replayed;
     with full_layer, every layer also runs the SwiGLU FFN block (its own
@@ -666,13 +719,16 @@ def main():
     lh_op = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings, q_layout=L.PA_Q_OPERAND)
     log(f"long history, cold MALL, Q in operand order: {lh_op['steps_per_s']:.1f} steps/s, partial kernel "
         f"{lh_op['partial_us']:.1f} us")
-    warm = small = async_push = None
+    warm = small = async_push = ada_qkv = None
     if not args.headline_only:
         warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
         log(f"long history, warm MALL: {warm['steps_per_s']:.1f} steps/s, partial kernel {warm['partial_us']:.1f} us")
         small = [bench_small(args, torch, L, c) for c in (configs.TINY, configs.PI05_1L)]
         for sm in small:
             log(f"{sm['workload']}: {sm['us_per_call']:.1f} us per call eager, {sm['us_per_call_graph']:.1f} in a graph")
+        ada_qkv = bench_adanorm_qkv(args, torch, L, configs, synth)
+        log(f"ada_rmsnorm_qkv: {ada_qkv['us_per_call']:.1f} us per call eager, {ada_qkv['us_per_call_graph']:.1f} "
+            f"in a graph ({ada_qkv['gbs_graph']:.0f} GB/s)")
         async_push = bench_async_push(args, torch, L, configs, synth)
         log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
             f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
@@ -739,6 +795,8 @@ def main():
                                                   "calls": sm["calls"], "layers": sm["layers"],
                                                   "cached_tokens": sm["cached_tokens"], "suffix": sm["suffix"]}
                                  for sm in small}
+    if ada_qkv is not None:
+        line["adarmsnorm_qkv"] = ada_qkv
     if async_push is not None:
         line["async_push"] = async_push
     if stack is not None:

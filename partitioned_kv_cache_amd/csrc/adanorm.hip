@@ -219,21 +219,23 @@ enum GemmMode { GEMM_QKV = 0, GEMM_OPROJ = 1 };
 // GEMM_WAVES * KS * 16: the FP32 mean of squares of every row (wave w takes
 // rows w, w + 8, ..., all of its loads in flight before any is used), then
 // each lane's fragments bf16(x[m][k] * rsqrt(ms + eps) * gamma[k]) for rows
-// l32 and 32 + l32 and its k-range. Ends with every wave past a barrier.
-template <int KS>
+// l32 and 32 + l32 and its k-range. With HALVES, only the rows of 32-row half
+// `half` (fragments in a0, a1 zero): each row's arithmetic is the same. Ends
+// with every wave past a barrier.
+template <int KS, bool HALVES = false>
 __device__ __forceinline__ void norm_fragments(const uint16_t* __restrict__ a, const float* __restrict__ gamma,
                                                float eps, int rows, float* rinv_s, bf16x8 (&a0)[KS],
-                                               bf16x8 (&a1)[KS]) {
+                                               bf16x8 (&a1)[KS], int half = 0) {
     constexpr int K = GEMM_WAVES * KS * 16;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int k0 = wave * KS * 16 + 8 * hi;
-    const bool r0 = l32 < rows, r1 = 32 + l32 < rows;
-    constexpr int RPW = 64 / GEMM_WAVES;        // rows per wave
+    const int k0 = wave * KS * 16 + 8 * hi, base = HALVES ? 32 * half : 0;
+    const bool r0 = base + l32 < rows, r1 = !HALVES && 32 + l32 < rows;
+    constexpr int RPW = (HALVES ? 32 : 64) / GEMM_WAVES;        // rows per wave
     constexpr int LPR = (K + 511) / 512;        // 16-byte loads per lane and row
     uint4 raw[RPW][LPR];
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
-        const int r = wave + rr * GEMM_WAVES;
+        const int r = base + wave + rr * GEMM_WAVES;
 #pragma unroll
         for (int c = 0; c < LPR; ++c)
             raw[rr][c] = (r < rows && c * 512 + lane * 8 < K)
@@ -253,11 +255,11 @@ __device__ __forceinline__ void norm_fragments(const uint16_t* __restrict__ a, c
             }
         }
         ss = wsum(ss);
-        const int r = wave + rr * GEMM_WAVES;
+        const int r = base + wave + rr * GEMM_WAVES;
         if (lane == 0 && r < rows) rinv_s[r] = 1.f / sqrtf(ss / (float)K + eps);
     }
     __syncthreads();
-    const float ri0 = r0 ? rinv_s[l32] : 0.f, ri1 = r1 ? rinv_s[32 + l32] : 0.f;
+    const float ri0 = r0 ? rinv_s[base + l32] : 0.f, ri1 = r1 ? rinv_s[32 + l32] : 0.f;
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
         const int k = k0 + 16 * i;
@@ -265,7 +267,7 @@ __device__ __forceinline__ void norm_fragments(const uint16_t* __restrict__ a, c
         const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
         const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-        if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)l32 * K + k);
+        if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)(base + l32) * K + k);
         if (r1) x1 = *reinterpret_cast<const uint4*>(a + (long long)(32 + l32) * K + k);
         const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
         const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
@@ -295,9 +297,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
     constexpr int K = GEMM_WAVES * KS * 16;
     __shared__ float red[GEMM_WAVES][2][16][64];
     __shared__ float rinv_s[64];
-    // the QKV projection of an already normalised operand: one 32-row half per
-    // workgroup (row_half_grid); otherwise all 64 row slots
-    constexpr bool HALVES = MODE == GEMM_QKV && !NORM;
+    // the QKV projection: one 32-row half per workgroup (row_half_grid); the
+    // out-projection's residual epilogue takes all 64 row slots
+    constexpr bool HALVES = MODE == GEMM_QKV;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     int nb = blockIdx.x, half = 0;
     if (HALVES) {
@@ -322,10 +324,10 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
             a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
         }
     } else {
-        norm_fragments<KS>(a, gamma, eps, rows, rinv_s, a0, a1);
-        // every workgroup forms the same normalised rows; the first reports
-        // a non-finite element (padding rows are zeros)
-        if (blockIdx.x == 0 && out.nonfinite) report_nonfinite<KS>(a0, a1, out.nonfinite);
+        norm_fragments<KS, HALVES>(a, gamma, eps, rows, rinv_s, a0, a1, half);
+        // every workgroup of a row half forms the same normalised rows; those
+        // of column block 0 report a non-finite element (padding rows are zeros)
+        if (nb == 0 && out.nonfinite) report_nonfinite<KS>(a0, a1, out.nonfinite);
     }
 
     f32x16 c0 = f32x16{}, c1 = f32x16{};
@@ -377,9 +379,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
 //
 // gemm_gateup: a workgroup owns 32 act columns; its 8 waves split K = model
 // (KS k-steps of 16 each) and compute both products for those columns; the
-// gate and up partial sums meet in LDS one after the other. Without NORM, x
-// is the already normalised operand and a workgroup owns one 32-row half of
-// it (row_half_grid); with NORM it forms and uses all 64 row slots.
+// gate and up partial sums meet in LDS one after the other. A workgroup owns
+// one 32-row half of the operand (row_half_grid). Without NORM, x is the
+// already normalised operand.
 template <int KS, bool NORM = true>
 __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t* __restrict__ x,
                                                                   const float* __restrict__ gamma, float eps,
@@ -387,14 +389,12 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
                                                                   const uint16_t* __restrict__ w_up, int rows, int F,
                                                                   uint16_t* __restrict__ act, uint32_t* nonfinite) {
     constexpr int K = GEMM_WAVES * KS * 16;
-    __shared__ float red[GEMM_WAVES][2][16][64];
+    __shared__ float red[GEMM_WAVES][16][64];
     __shared__ float rinv_s[64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    int nb = blockIdx.x, half = 0;
-    if (!NORM) {
-        row_half_block(rows, nb, half);
-        if (nb >= F / 32) return;                                   // id padding, whole workgroup
-    }
+    int nb, half;
+    row_half_block(rows, nb, half);
+    if (nb >= F / 32) return;                                       // id padding, whole workgroup
     const int n0 = nb * 32;
     const int k0 = wave * KS * 16 + 8 * hi;
     bf16x8 wg[KS], wu[KS];
@@ -406,8 +406,8 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
     }
     bf16x8 a0[KS], a1[KS];
     if (NORM) {
-        norm_fragments<KS>(x, gamma, eps, rows, rinv_s, a0, a1);
-        if (blockIdx.x == 0 && nonfinite) report_nonfinite<KS>(a0, a1, nonfinite);
+        norm_fragments<KS, true>(x, gamma, eps, rows, rinv_s, a0, a1, half);
+        if (nb == 0 && nonfinite) report_nonfinite<KS>(a0, a1, nonfinite);
     } else {
         const int row = 32 * half + l32;
 #pragma unroll
@@ -416,50 +416,39 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_gateup(const uint16_t
             a1[i] = bf16x8{};
         }
     }
-    const bool two = NORM && rows > 32;
-    f32x16 g0 = f32x16{}, g1 = f32x16{}, u0 = f32x16{}, u1 = f32x16{};
+    f32x16 g0 = f32x16{}, u0 = f32x16{};
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
         g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wg[i], g0, 0, 0, 0);
         u0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], wu[i], u0, 0, 0, 0);
-        if (two) {
-            g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wg[i], g1, 0, 0, 0);
-            u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], wu[i], u1, 0, 0, 0);
-        }
     }
-    // wave w finishes 4 of the 32 (row block, register) pairs (2 of the 16 of
-    // its row half without NORM): the gate sums first
-    constexpr int NU = NORM ? 4 : 2;
+    // wave w finishes 2 of the 16 (register) rows of its row half: the gate
+    // sums first
+    constexpr int NU = 2;
     float gs[NU];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        red[wave][0][r][lane] = g0[r];
-        red[wave][1][r][lane] = g1[r];
-    }
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = g0[r];
     __syncthreads();
 #pragma unroll
     for (int uix = 0; uix < NU; ++uix) {
-        const int idx = wave * NU + uix, blk = idx >> 4, r = idx & 15;
+        const int r = wave * NU + uix;
         float v = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][r][lane];
         gs[uix] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        red[wave][0][r][lane] = u0[r];
-        red[wave][1][r][lane] = u1[r];
-    }
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = u0[r];
     __syncthreads();
 #pragma unroll
     for (int uix = 0; uix < NU; ++uix) {
-        const int idx = wave * NU + uix, blk = idx >> 4, r = idx & 15;
-        const int m = 32 * (blk + half) + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int r = wave * NU + uix;
+        const int m = 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (m >= rows) continue;
         float u = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < GEMM_WAVES; ++ww) u += red[ww][blk][r][lane];
+        for (int ww = 0; ww < GEMM_WAVES; ++ww) u += red[ww][r][lane];
         const float g = gs[uix];
         act[(long long)m * F + n0 + l32] = f2bf(g / (1.f + __expf(-g)) * u);
     }
@@ -475,7 +464,7 @@ static bool gemm_k_supported(int K) {
 template <int MODE, bool NORM>
 static hipError_t launch_gemm(const uint16_t* a, const float* gamma, float eps, const uint16_t* w, int rows, int K,
                               int N, const GemmOut& o, hipStream_t s) {
-    const dim3 grid(MODE == GEMM_QKV && !NORM ? row_half_grid(rows, N) : N / 32), block(GEMM_WAVES * 64);
+    const dim3 grid(MODE == GEMM_QKV ? row_half_grid(rows, N) : N / 32), block(GEMM_WAVES * 64);
     switch (K / 128) {
         case 2: gemm_skinny<MODE, 2, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
         case 4: gemm_skinny<MODE, 4, NORM><<<grid, block, 0, s>>>(a, gamma, eps, w, rows, N, o); break;
@@ -709,10 +698,10 @@ extern "C" pa_status ffn_swiglu(void* h, int32_t rows, int32_t model_dim, int32_
     const uint16_t* wu = static_cast<const uint16_t*>(w_up);
     const dim3 block(GEMM_WAVES * 64);
     switch (model_dim / 128) {
-        case 2: gemm_gateup<2><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
-        case 4: gemm_gateup<4><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
-        case 6: gemm_gateup<6><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
-        default: gemm_gateup<8><<<ffn_dim / 32, block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        case 2: gemm_gateup<2><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        case 4: gemm_gateup<4><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        case 6: gemm_gateup<6><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
+        default: gemm_gateup<8><<<row_half_grid(rows, ffn_dim), block, 0, s>>>(xin, gamma, eps, wg, wu, rows, ffn_dim, act, nonfinite); break;
     }
     PA_LAUNCHED();
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +

@@ -72,11 +72,13 @@ def test_ffn_swiglu_euler_update_and_nonfinite_flag():
                            synth.widen(wd))
     assert rel_err(synth.widen(host(x_d)), stack.euler(synth.widen(x), ref["h"], 0.1)) <= BAR
     assert int(host(flag)[0]) == 0
-    bad = h.copy()
-    bad[3, 17] = 0x7F80                     # +Inf in bf16
-    L.ffn_swiglu(dev(bad), 51, 1024, 4096, dev(gamma), s.eps, dev(wg), dev(wu), dev(wd), None, 0.0, flag, ws, wsb)
-    torch.cuda.synchronize()
-    assert int(host(flag)[0]) == 1
+    for row in (3, 40):                     # in either 32-row half of the operand
+        bad = h.copy()
+        bad[row, 17] = 0x7F80               # +Inf in bf16
+        flag.zero_()
+        L.ffn_swiglu(dev(bad), 51, 1024, 4096, dev(gamma), s.eps, dev(wg), dev(wu), dev(wd), None, 0.0, flag, ws, wsb)
+        torch.cuda.synchronize()
+        assert int(host(flag)[0]) == 1, row
 
 
 def test_ffn_rejects_unsupported_sizes():

@@ -163,6 +163,29 @@ def test_nonfinite_flag_trips_on_injected_inf_and_nan():
         assert int(host(flag)[0]) == (0 if bad is None else 1), bad
 
 
+@pytest.mark.parametrize("bad_row", [3, 40, None])
+def test_ada_rmsnorm_qkv_flags_a_nonfinite_row(bad_row):
+    """The fused norm + QKV projection reports a non-finite input in either
+    32-row half of its 51 rows, and nothing for finite input."""
+    L = lib()
+    s = S3
+    rows, model, hq, hkv, d = s.n_dyn, s.model_dim, s.n_q_heads, s.n_kv_heads, s.head_dim
+    x = synth.normal((rows, model), "bf16", s.cfg_id, synth.T_X, 9).copy()
+    if bad_row is not None:
+        x[bad_row, 5] = 0x7FC0              # NaN in bf16
+    wq, _ = synth.proj_weights(s, 0)
+    gam = np.ones(model, np.float32)
+    q = torch.empty((rows, hq, d), dtype=torch.int16, device="cuda")
+    k = torch.empty((rows, hkv, d), dtype=torch.int16, device="cuda")
+    v = torch.empty((rows, hkv, d), dtype=torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsb = L.ada_rmsnorm_qkv_workspace_bytes(rows, model)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    L.ada_rmsnorm_qkv(dev(x), rows, model, dev(gam), s.eps, dev(wq), hq, hkv, d, q, k, v, flag, ws, wsb)
+    torch.cuda.synchronize()
+    assert int(host(flag)[0]) == (0 if bad_row is None else 1)
+
+
 # ----------------------------------------------------------- decode readers --
 
 @pytest.mark.parametrize("odt", ["f32", "bf16"])
