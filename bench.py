@@ -360,6 +360,45 @@ def bench_adanorm_qkv(args, torch, L, configs, synth, n_calls=2000):
             "algo_bytes": algo, "gbs_graph": round(algo / (g_us * 1e-6) / 1e9, 1)}
 
 
+def bench_capsule(args, torch, L, configs, synth, n_calls=50):
+    """Row f4: rb_snapshot / rb_restore of the long-history ring (18 layers,
+    pin 256 + 8 x 768 tokens, window wrapped so each copy is split into its
+    physical runs) into a device capsule; microseconds per call and the copy
+    rate over 2 x capsule bytes (read and write)."""
+    s = configs.LONG_18L
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
+    shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
+    k_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    v_buf = torch.zeros(shp, dtype=torch.int16, device="cuda")
+    ring = L.Ring(L.rb_config(s.num_layers, s.n_kv_heads, s.head_dim, s.pin_tokens, s.num_slots,
+                              s.tokens_per_frame, L.PA_BF16), k_buf, v_buf)
+    pk, pv = synth.pin_kv(s)
+    ring.pin_prefix(dev(pk), dev(pv), s.pin_tokens)
+    pool = [tuple(dev(a) for a in synth.frame_kv(s, f)) for f in range(4)]
+    for f in range(s.num_slots + 3):
+        ring.push_frame(*pool[f % 4])
+    nb = ring.capsule_bytes()
+    cap = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    st = ring.snapshot(cap, stream=stream)
+    ring.restore(cap, st, stream=stream)
+    torch.cuda.synchronize()
+    res = {"workload": "long_history_18L ring capsule", "capsule_bytes": nb, "calls": n_calls}
+    for name, fn in (("snapshot", lambda: ring.snapshot(cap, stream=stream)),
+                     ("restore", lambda: ring.restore(cap, st, stream=stream))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_calls
+        res[f"{name}_us"] = round(us, 1)
+        res[f"{name}_gbs"] = round(2 * nb / (us * 1e-6) / 1e9, 1)
+    ring.close()
+    return res
+
+
 def bench_stack(args, torch, L, configs, synth, full_layer=False):
     """Whole 18-layer denoising step of the Pi0.5-like stack, graph-replayed;
     with full_layer, every layer also runs the SwiGLU FFN block (its own
@@ -719,7 +758,7 @@ def main():
     lh_op = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings, q_layout=L.PA_Q_OPERAND)
     log(f"long history, cold MALL, Q in operand order: {lh_op['steps_per_s']:.1f} steps/s, partial kernel "
         f"{lh_op['partial_us']:.1f} us")
-    warm = small = async_push = ada_qkv = None
+    warm = small = async_push = ada_qkv = capsule = None
     if not args.headline_only:
         warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
         log(f"long history, warm MALL: {warm['steps_per_s']:.1f} steps/s, partial kernel {warm['partial_us']:.1f} us")
@@ -729,6 +768,9 @@ def main():
         ada_qkv = bench_adanorm_qkv(args, torch, L, configs, synth)
         log(f"ada_rmsnorm_qkv: {ada_qkv['us_per_call']:.1f} us per call eager, {ada_qkv['us_per_call_graph']:.1f} "
             f"in a graph ({ada_qkv['gbs_graph']:.0f} GB/s)")
+        capsule = bench_capsule(args, torch, L, configs, synth)
+        log(f"capsule ({capsule['capsule_bytes'] / 1e6:.1f} MB): snapshot {capsule['snapshot_us']:.1f} us "
+            f"({capsule['snapshot_gbs']:.0f} GB/s), restore {capsule['restore_us']:.1f} us")
         async_push = bench_async_push(args, torch, L, configs, synth)
         log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
             f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
@@ -797,6 +839,8 @@ def main():
                                  for sm in small}
     if ada_qkv is not None:
         line["adarmsnorm_qkv"] = ada_qkv
+    if capsule is not None:
+        line["ring_capsule"] = capsule
     if async_push is not None:
         line["async_push"] = async_push
     if stack is not None:
