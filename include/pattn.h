@@ -47,6 +47,11 @@ typedef enum {
     PA_EDEVICE = 4,    /* a HIP runtime call failed                        */
     PA_ERANGE = 5      /* workspace too small, or a limit exceeded         */
 } pa_status;
+/* There is no "non-finite" status. Whether a value is NaN or Inf is only
+ * known on the device after the enqueue has returned, so the calls that
+ * check (the norms, the projections, the denoising step) OR bit 0 into a
+ * caller-owned device word, `nonfinite`, which the caller reads when it
+ * synchronises. A status describes only what the host validated. */
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
@@ -124,6 +129,27 @@ pa_status rb_stage_frame(rb_ring* ring, const void* k, const void* v, void* stre
 pa_status rb_commit_frame(rb_ring* ring, void* stream, int64_t* evicted_frame);
 
 pa_status rb_get_state(const rb_ring* ring, rb_state* out);
+
+/* Graph capture. Attention calls plan their launches from the ring's host
+ * metadata when they are enqueued, so a captured step is replayed with the
+ * window as it was at capture. That stays right across later pushes when
+ * the window is full (count = W) on a ring without a spare slot: the slots
+ * are read in physical order whatever `head` is. On a spare-slot ring the
+ * window's position moves with every commit: there the ring must keep its
+ * head in a device word that the kernels read when they run.
+ *   - pattn_step, pattn_step_timed, pattn_decode, pattn_fused_step and
+ *     pa_denoise_step return PA_ESTATE when `stream` is capturing and the
+ *     window is not full, or the ring has a spare slot and no state word.
+ *   - rb_pin_prefix, rb_push_frame, rb_stage_frame, rb_commit_frame,
+ *     rb_snapshot, rb_restore and rb_bind_state_word change or read host
+ *     metadata at enqueue time and return PA_ESTATE under capture.
+ * Replay captured steps on the stream that commits (or order them after it).
+ *
+ * rb_bind_state_word binds a caller-owned device buffer of four int32
+ * (16-byte aligned) and writes {head, count, pinned, 0} into it on `stream`;
+ * every later rb_pin_prefix, rb_push_frame, rb_commit_frame and rb_restore
+ * rewrites it on its own stream, after its copies. NULL unbinds. */
+pa_status rb_bind_state_word(rb_ring* ring, int32_t* state_word, void* stream);
 
 /* ------------------------------------------------------------------------
  * Capsules (FlashRT article, PaperDaily, "FlashRT开源：27倍加速…": the
@@ -315,6 +341,9 @@ size_t ada_gamma_workspace_bytes(const ada_mlp* mlp, int32_t n_t);
 /* gamma[l][i][:] = 1 + MLP_l([emb(t[i]); state]) for every layer l and
  * timestep i (a frame's ten steps in one call). t: HOST array [n_t];
  * state: device bf16 [state_dim]; gamma: device f32 [L][n_t][model_dim].
+ * The state is bf16, not f32: the MLP's input c = [emb(t); state] is
+ * rounded to bf16 before the first product anyway (the MLP runs in BF16),
+ * so a bf16 state loses nothing and matches how a bf16 model holds it.
  * 1 <= n_t <= 16 and n_t * hidden_dim <= 32768 (a workgroup stages the n_t
  * hidden activations of its layer, 64 KB at most); other sizes, or an MLP
  * outside the limits above, return PA_ESHAPE before any launch. */
@@ -438,6 +467,9 @@ typedef struct {
  * results are bit-identical to the unpacked stack's. */
 pa_status pa_pack_weight(const void* w, int32_t n, int32_t k, void* w_packed, void* stream);
 
+/* On return (in stream order) the first rows * model_dim bf16 words of the
+ * workspace hold the last layer's stream h_L, the velocity of the Euler
+ * step; a call with stack->num_layers = l leaves h_l there. */
 size_t pa_denoise_step_workspace_bytes(const rb_ring* ring, const pa_stack* stack);
 pa_status pa_denoise_step(const rb_ring* ring, const pa_stack* stack, void* x, const float* gamma,
                           const float* gamma_ffn, int64_t gamma_layer_stride, uint32_t* nonfinite,

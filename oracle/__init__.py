@@ -29,9 +29,9 @@ adanorm    sinusoidal embedding, gamma MLP and AdaRMSNorm (Eq. 2)
 stack      one layer of the denoising stack and the Euler update
 decode     the shared-KV multi-reader (OxyGen) decode attention
 
-Pin status of each function is listed in its docstring; the only function
-without an external pin is ``stack.denoise_step`` end to end ("parity
-unpinned": the pages give no layer glue; every op it chains is pinned).
+Pin status of each function is listed in its docstring. Every function has
+an external pin; the layer glue (a reading: the pages give none) is pinned
+end to end against the same step written with torch's float64 operators.
 """
 
 from . import attention, ring, adanorm, stack, decode  # noqa: F401

@@ -9,8 +9,13 @@ denoised over K steps), §3 Architecture (Eq. 1 attention, Eq. 2 AdaRMSNorm),
 §4 Innovations / §2 (a packed QKV kernel is one of the fused operators), and
 §6 Table 7 (ten denoising steps per action chunk).
 
-The pages give no layer glue, so everything below is a reading, and the
-end-to-end step is "parity unpinned" (each op it chains is pinned on its own):
+The pages give no layer glue, so everything below is a reading. Each op is
+pinned on its own, and the end-to-end step (``denoise_step``, with and
+without the FFN block) is pinned against the same step written with torch's
+float64 operators (rms_norm, matmul, scaled_dot_product_attention, silu, bf16
+conversion) on inputs where a miswired chain -- the wrong stream fed to the
+next layer, one gamma for every layer, the velocity from another layer, a
+dropped attention region -- fails the comparison:
 * layer l at step k: y = bf16(AdaRMSNorm(h, gamma_{l,k})); [q|k|v] = y W_qkv^T
   with W_qkv packed [(Hq + 2 Hkv) * D][model] as q heads, then k heads, then
   v heads, each stored bf16; o = Eq. 1 attention over [cache; k_dyn] stored
@@ -99,7 +104,8 @@ def timesteps(n_steps: int = 10):
 
 def denoise_step(x, gammas, eps, w_qkv, w_o, caches_k, caches_v, scale,
                  n_q_heads, n_kv_heads, head_dim, ffns=None):
-    """All layers at one step, then the Euler update. Parity unpinned end to end.
+    """All layers at one step, then the Euler update (pinned end to end against
+    a torch float64 chain of the same step).
 
     ``gammas[l]`` is gamma_{l,k}; ``caches_k[l]`` the chronological cached
     context of layer l; ``ffns[l]`` (optional) layer l's FFN block as in

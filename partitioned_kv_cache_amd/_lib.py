@@ -38,7 +38,7 @@ EXPORTS = (
     "ada_rmsnorm_qkv_workspace_bytes", "ada_rmsnorm_qkv", "oproj_residual", "pattn_step_timed",
     "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
     "rb_stage_frame", "rb_commit_frame", "ffn_swiglu_workspace_bytes", "ffn_swiglu", "pattn_fused_workspace_bytes",
-    "pattn_fused_step", "pa_pack_weight", "pattn_operand_q_bytes", "pattn_pack_q",
+    "pattn_fused_step", "pa_pack_weight", "pattn_operand_q_bytes", "pattn_pack_q", "rb_bind_state_word",
 )
 
 
@@ -102,6 +102,7 @@ _sig("rb_push_frame", _i32, _vp, _vp, _vp, _vp, C.POINTER(C.c_int64))
 _sig("rb_get_state", _i32, _vp, C.POINTER(RbState))
 _sig("rb_stage_frame", _i32, _vp, _vp, _vp, _vp)
 _sig("rb_commit_frame", _i32, _vp, _vp, C.POINTER(C.c_int64))
+_sig("rb_bind_state_word", _i32, _vp, _vp, _vp)
 _sig("rb_capsule_bytes", _sz, _vp)
 _sig("rb_snapshot", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
 _sig("rb_restore", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
@@ -191,6 +192,11 @@ class Ring:
         ev = C.c_int64(0)
         _check(_lib.rb_commit_frame(self.handle, _stream(stream), C.byref(ev)), "rb_commit_frame")
         return ev.value
+
+    def bind_state_word(self, word, stream=None):
+        """Keep {head, count, pinned, 0} in a device int32[4] the kernels read (rb_bind_state_word)."""
+        self.state_word = word                     # keep the tensor alive
+        _check(_lib.rb_bind_state_word(self.handle, ptr(word), _stream(stream)), "rb_bind_state_word")
 
     def state(self) -> dict:
         s = RbState()

@@ -186,9 +186,11 @@ __global__ __launch_bounds__(256) void partial_valu(const float* q, long long q_
     const float* rv = static_cast<const float*>(src.ring_v);
     const float* dk = static_cast<const float*>(src.dyn_k);
     const float* dv = static_cast<const float*>(src.dyn_v);
+    KvSource sr = src;
+    sr.skip_at = src.window_skip();
     auto row_of = [&](int j, bool v) -> const float* {
         bool dyn;
-        const long long off = src.offset(lb, g, j, dyn);
+        const long long off = sr.offset(lb, g, j, dyn);
         return (dyn ? (v ? dv : dk) : (v ? rv : rk)) + off;
     };
     float m = -INFINITY, l = 0.f;
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     const uint16_t* dk = static_cast<const uint16_t*>(src.dyn_k) + lb * src.dyn_layer + g * D;
     const uint16_t* dv = static_cast<const uint16_t*>(src.dyn_v) + lb * src.dyn_layer + g * D;
     const int n_cached = src.pinned + src.n_slide, pinned = src.pinned, gap = src.pin_cap - src.pinned;
-    const int skip_at = pinned + src.skip_at, skip_len = src.skip_len;   // in context-key units
+    const int skip_at = pinned + src.window_skip(), skip_len = src.skip_len;   // in context-key units
 
     // Direct-to-LDS loads: one 1 KB load = 16 keys x 64 B of one plane, lane
     // -> (key, 16-byte chunk). Wave w loads blocks w, w + WAVES, ... of a
@@ -875,6 +877,7 @@ static KvSource source_for(const Ring* r, int layer_begin, const void* k_dyn, co
     s.n_slide = r->count * r->cfg.tokens_per_frame;
     s.skip_at = r->skip_at();
     s.skip_len = r->cfg.spare_slots ? r->cfg.tokens_per_frame : 0;
+    s.head_word = r->cfg.spare_slots ? r->state_word : nullptr;
     s.n_dyn = n_dyn;
     s.hkv = r->cfg.num_kv_heads;
     s.d = r->cfg.head_dim;
@@ -1053,6 +1056,8 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
     const size_t need = partial_bytes(p, r->cfg.head_dim);
     PA_CHECK_ARG(ws_bytes >= need, PA_ERANGE, "pattn_step: workspace %zu bytes < %zu needed", ws_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = check_capture(r, s, "pattn_step");
+    if (st != PA_OK) return st;
     const KvSource src = source_for(r, a->layer_begin, k_dyn, v_dyn, a->n_dyn);
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
     const long long q_layer = (long long)a->n_dyn * a->n_q_heads * r->cfg.head_dim;
@@ -1218,6 +1223,8 @@ extern "C" pa_status pattn_decode(const rb_ring* ring, const pattn_decode_args* 
     const size_t need = partial_bytes(p, r->cfg.head_dim);
     PA_CHECK_ARG(ws_bytes >= need, PA_ERANGE, "pattn_decode: workspace %zu bytes < %zu needed", ws_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = check_capture(r, s, "pattn_decode");
+    if (st != PA_OK) return st;
     const KvSource src = source_for(r, a->layer_begin, nullptr, nullptr, 0);
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
     const int d = r->cfg.head_dim;
@@ -1285,6 +1292,8 @@ extern "C" pa_status pattn_fused_step(const rb_ring* ring, const pattn_args* a, 
     const size_t need = partial_bytes(p, r->cfg.head_dim);
     PA_CHECK_ARG(ws_bytes >= need, PA_ERANGE, "pattn_fused_step: workspace %zu bytes < %zu needed", ws_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    st = check_capture(r, s, "pattn_fused_step");
+    if (st != PA_OK) return st;
     const KvSource src = source_for(r, a->layer_begin, k_dyn, v_dyn, a->n_dyn);
     const Partials part = partials_in(ws, p, r->cfg.head_dim);
     const int D = r->cfg.head_dim;

@@ -54,6 +54,11 @@ struct Ring {
     bool free_recorded = false;
     hipEvent_t ev_staged = nullptr;   // the staging copy is done
     hipEvent_t ev_free = nullptr;     // every step that could read the freed slot is done
+    // Optional caller-owned device copy of the state, int32 {head, count,
+    // pinned, 0}, rewritten stream-ordered by every call that moves head.
+    // Attention kernels on a spare-slot ring read the window position from
+    // it when it is bound, so a captured step stays valid across commits.
+    int32_t* state_word = nullptr;
     int64_t elem_bytes() const { return cfg.dtype == PA_F32 ? 4 : 2; }
     int32_t phys_slots() const { return cfg.num_slots + cfg.spare_slots; }
     int64_t seq_len() const { return (int64_t)cfg.pin_capacity + (int64_t)phys_slots() * cfg.tokens_per_frame; }
@@ -99,10 +104,19 @@ struct KvSource {
     int pinned, pin_cap, n_slide, n_dyn;
     int skip_at, skip_len;     // window token u >= skip_at sits skip_len tokens further on
     int hkv, d;
+    // Spare-slot rings with a bound state word: skip_at is head * F, read
+    // from the word (element 0 = head) when the kernel runs, not when it is
+    // enqueued. Null otherwise.
+    const int32_t* head_word;
 
     __device__ __forceinline__ int total() const { return pinned + n_slide + n_dyn; }
+    // skip_at as the kernel must use it (reads the state word when bound)
+    __device__ __forceinline__ int window_skip() const {
+        return head_word ? *head_word * skip_len : skip_at;
+    }
 
-    // element offset of (call-layer lb, kv head g, logical key j) and which buffer
+    // element offset of (call-layer lb, kv head g, logical key j) and which
+    // buffer; skip_at must already be resolved (window_skip)
     __device__ __forceinline__ long long offset(int lb, int g, int j, bool& is_dyn) const {
         if (j < pinned + n_slide) {
             const int u = j - pinned;
@@ -114,5 +128,14 @@ struct KvSource {
         return (long long)lb * dyn_layer + ((long long)(j - pinned - n_slide) * hkv + g) * d;
     }
 };
+
+// Is `stream` being captured into a graph? (false when HIP cannot tell.)
+pa_status stream_capturing(hipStream_t stream, bool* capturing);
+
+// Attention reads the ring's host metadata (window length, and the window
+// position of a spare-slot ring) when it is enqueued. A captured launch
+// stays valid across later pushes only if neither can change under it: the
+// window must be full, and a spare-slot ring must have a bound state word.
+pa_status check_capture(const Ring* r, hipStream_t stream, const char* who);
 
 }  // namespace pa

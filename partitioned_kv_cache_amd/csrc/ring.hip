@@ -9,8 +9,13 @@
 //
 // The buffers are the caller's. A push is one strided device-to-device copy
 // of the frame's [L][F][Hkv][D] block into slot `head` of every layer; only
-// host metadata changes otherwise. Nothing is ever allocated or moved, so a
-// captured graph that reads the ring stays valid across pushes.
+// host metadata changes otherwise. Nothing is ever allocated or moved. A
+// captured attention launch reads the window length and (on a spare-slot
+// ring) its position as they were when it was enqueued, so capture is
+// allowed only where neither can change under a replay: the window must be
+// full, and a spare-slot ring must keep its head in a bound device state
+// word, which the kernels read when they run (rb_bind_state_word). The calls
+// that change the ring's host metadata cannot be captured at all.
 
 #include <stdarg.h>
 
@@ -32,14 +37,80 @@ pa_status fail(pa_status st, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = 0; }
 
+pa_status stream_capturing(hipStream_t stream, bool* capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    // A runtime that cannot answer (no device) cannot be capturing either;
+    // the call's own launches then report the device error.
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        cs = hipStreamCaptureStatusNone;
+    }
+    *capturing = cs != hipStreamCaptureStatusNone;
+    return PA_OK;
+}
+
+pa_status check_capture(const Ring* r, hipStream_t stream, const char* who) {
+    bool cap = false;
+    pa_status st = stream_capturing(stream, &cap);
+    if (st != PA_OK || !cap) return st;
+    PA_CHECK_ARG(r->count == r->cfg.num_slots, PA_ESTATE,
+                 "%s: capture needs a full window (%d of %d frames): a replay after the next push would read a "
+                 "stale window length", who, r->count, r->cfg.num_slots);
+    PA_CHECK_ARG(!r->cfg.spare_slots || r->state_word, PA_ESTATE,
+                 "%s: capture on a spare-slot ring needs a bound state word (rb_bind_state_word): a replay after "
+                 "the next commit would read a stale window position", who);
+    return PA_OK;
+}
+
+// The calls that change host metadata at enqueue time cannot be captured.
+static pa_status refuse_capture(hipStream_t stream, const char* who) {
+    bool cap = false;
+    pa_status st = stream_capturing(stream, &cap);
+    if (st != PA_OK) return st;
+    PA_CHECK_ARG(!cap, PA_ESTATE, "%s: changes the ring's host metadata when enqueued and cannot be captured", who);
+    return PA_OK;
+}
+
+// One thread writes the ring's state word {head, count, pinned, 0} (a
+// vector store; 16-byte aligned).
+__global__ void write_state_word(int4* w, int head, int count, int pinned) {
+    *w = make_int4(head, count, pinned, 0);
+}
+
+static pa_status publish_state(Ring* r, hipStream_t s) {
+    if (!r->state_word) return PA_OK;
+    write_state_word<<<1, 1, 0, s>>>(reinterpret_cast<int4*>(r->state_word), r->head, r->count, r->pinned);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
+static pa_status ensure_events(Ring* r) {
+    if (!r->ev_staged) {
+        PA_HIP(hipEventCreateWithFlags(&r->ev_staged, hipEventDisableTiming));
+        PA_HIP(hipEventCreateWithFlags(&r->ev_free, hipEventDisableTiming));
+    }
+    return PA_OK;
+}
+
+// A spare-slot ring's next spare (slot `head`) may still be read by steps
+// enqueued on `s` before this point: the next rb_stage_frame waits for them.
+static pa_status fence_spare(Ring* r, hipStream_t s) {
+    if (!r->cfg.spare_slots) return PA_OK;
+    pa_status st = ensure_events(r);
+    if (st != PA_OK) return st;
+    PA_HIP(hipEventRecord(r->ev_free, s));
+    r->free_recorded = true;
+    return PA_OK;
+}
+
 }  // namespace pa
 
-using pa::Ring;
+using namespace pa;
 
 extern "C" const char* pa_last_error(void) { return pa::g_err; }
 
 extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, rb_ring** out) {
-    pa::clear_error();
+    clear_error();
     PA_CHECK_ARG(cfg && k_buf && v_buf && out, PA_EINVAL, "rb_create: null argument");
     PA_CHECK_ARG(cfg->dtype == PA_F32 || cfg->dtype == PA_BF16, PA_EINVAL, "rb_create: bad dtype %d", cfg->dtype);
     PA_CHECK_ARG(cfg->num_layers > 0 && cfg->num_kv_heads > 0 && cfg->head_dim > 0 && cfg->num_slots > 0 &&
@@ -62,7 +133,7 @@ extern "C" pa_status rb_create(const rb_config* cfg, void* k_buf, void* v_buf, r
 }
 
 extern "C" pa_status rb_destroy(rb_ring* ring) {
-    pa::clear_error();
+    clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     if (r) {
         if (r->ev_staged) (void)hipEventDestroy(r->ev_staged);
@@ -83,19 +154,21 @@ static pa_status copy_tokens(Ring* r, void* dst_base, const void* src, int64_t t
 }
 
 extern "C" pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, int32_t n_tokens, void* stream) {
-    pa::clear_error();
+    clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_pin_prefix: null argument");
     PA_CHECK_ARG(r->pinned == 0, PA_ESTATE, "rb_pin_prefix: prefix already pinned (%d tokens)", r->pinned);
     PA_CHECK_ARG(n_tokens > 0 && n_tokens <= r->cfg.pin_capacity, PA_ESHAPE,
                  "rb_pin_prefix: n_tokens %d not in [1, %d]", n_tokens, r->cfg.pin_capacity);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    pa_status st = copy_tokens(r, r->k, k, 0, n_tokens, s);
+    pa_status st = refuse_capture(s, "rb_pin_prefix");
+    if (st != PA_OK) return st;
+    st = copy_tokens(r, r->k, k, 0, n_tokens, s);
     if (st != PA_OK) return st;
     st = copy_tokens(r, r->v, v, 0, n_tokens, s);
     if (st != PA_OK) return st;
     r->pinned = n_tokens;
-    return PA_OK;
+    return publish_state(r, s);
 }
 
 // Copy a frame into slot `head` of every layer.
@@ -117,30 +190,36 @@ static int64_t advance(Ring* r) {
 }
 
 extern "C" pa_status rb_push_frame(rb_ring* ring, const void* k, const void* v, void* stream, int64_t* evicted) {
-    pa::clear_error();
+    clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_push_frame: null argument");
     PA_CHECK_ARG(!r->staged, PA_ESTATE, "rb_push_frame: a staged frame is pending; commit it first");
-    pa_status st = write_head_slot(r, k, v, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pa_status st = refuse_capture(s, "rb_push_frame");
+    if (st != PA_OK) return st;
+    st = write_head_slot(r, k, v, s);
     if (st != PA_OK) return st;
     const int64_t ev = advance(r);
+    st = fence_spare(r, s);
+    if (st == PA_OK) st = publish_state(r, s);
+    if (st != PA_OK) return st;
     if (evicted) *evicted = ev;
     return PA_OK;
 }
 
 extern "C" pa_status rb_stage_frame(rb_ring* ring, const void* k, const void* v, void* stream) {
-    pa::clear_error();
+    clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r && k && v, PA_EINVAL, "rb_stage_frame: null argument");
     PA_CHECK_ARG(r->cfg.spare_slots == 1, PA_ESTATE, "rb_stage_frame: the ring has no spare slot");
     PA_CHECK_ARG(!r->staged, PA_ESTATE, "rb_stage_frame: a staged frame is already pending");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!r->ev_staged) {
-        PA_HIP(hipEventCreateWithFlags(&r->ev_staged, hipEventDisableTiming));
-        PA_HIP(hipEventCreateWithFlags(&r->ev_free, hipEventDisableTiming));
-    }
+    pa_status st = refuse_capture(s, "rb_stage_frame");
+    if (st != PA_OK) return st;
+    st = ensure_events(r);
+    if (st != PA_OK) return st;
     if (r->free_recorded) PA_HIP(hipStreamWaitEvent(s, r->ev_free, 0));
-    pa_status st = write_head_slot(r, k, v, s);
+    st = write_head_slot(r, k, v, s);
     if (st != PA_OK) return st;
     PA_HIP(hipEventRecord(r->ev_staged, s));
     r->staged = true;
@@ -148,11 +227,13 @@ extern "C" pa_status rb_stage_frame(rb_ring* ring, const void* k, const void* v,
 }
 
 extern "C" pa_status rb_commit_frame(rb_ring* ring, void* stream, int64_t* evicted) {
-    pa::clear_error();
+    clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r, PA_EINVAL, "rb_commit_frame: null argument");
     PA_CHECK_ARG(r->staged, PA_ESTATE, "rb_commit_frame: no staged frame");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    pa_status st = refuse_capture(s, "rb_commit_frame");
+    if (st != PA_OK) return st;
     // Everything enqueued on the consumer so far may read the slot this
     // commit frees (the oldest of the window): the next stage waits for it.
     PA_HIP(hipEventRecord(r->ev_free, s));
@@ -160,12 +241,26 @@ extern "C" pa_status rb_commit_frame(rb_ring* ring, void* stream, int64_t* evict
     r->free_recorded = true;
     r->staged = false;
     const int64_t ev = advance(r);
+    st = publish_state(r, s);
+    if (st != PA_OK) return st;
     if (evicted) *evicted = ev;
     return PA_OK;
 }
 
+extern "C" pa_status rb_bind_state_word(rb_ring* ring, int32_t* state_word, void* stream) {
+    clear_error();
+    Ring* r = reinterpret_cast<Ring*>(ring);
+    PA_CHECK_ARG(r, PA_EINVAL, "rb_bind_state_word: null ring");
+    PA_CHECK_ARG(aligned16(state_word), PA_EINVAL, "rb_bind_state_word: the state word must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pa_status st = refuse_capture(s, "rb_bind_state_word");
+    if (st != PA_OK) return st;
+    r->state_word = state_word;
+    return publish_state(r, s);
+}
+
 extern "C" pa_status rb_get_state(const rb_ring* ring, rb_state* out) {
-    pa::clear_error();
+    clear_error();
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     PA_CHECK_ARG(r && out, PA_EINVAL, "rb_get_state: null argument");
     out->head = r->head;
@@ -226,28 +321,30 @@ static pa_status capsule_copy(Ring* r, char* cap, int32_t pinned, int64_t count,
 }
 
 extern "C" size_t rb_capsule_bytes(const rb_ring* ring) {
-    pa::clear_error();
+    clear_error();
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     return r ? capsule_bytes_of(r, capsule_tokens(r)) : 0;
 }
 
 extern "C" pa_status rb_snapshot(const rb_ring* ring, void* capsule, size_t capsule_bytes, rb_state* state,
                                  void* stream) {
-    pa::clear_error();
+    clear_error();
     Ring* r = const_cast<Ring*>(reinterpret_cast<const Ring*>(ring));
     PA_CHECK_ARG(r && state, PA_EINVAL, "rb_snapshot: null argument");
     const size_t need = capsule_bytes_of(r, capsule_tokens(r));
     PA_CHECK_ARG(capsule || need == 0, PA_EINVAL, "rb_snapshot: null capsule");
     PA_CHECK_ARG(capsule_bytes >= need, PA_ERANGE, "rb_snapshot: capsule %zu bytes < %zu needed", capsule_bytes, need);
-    pa_status st = capsule_copy(r, static_cast<char*>(capsule), r->pinned, r->count, r->head, true,
-                                static_cast<hipStream_t>(stream));
+    pa_status st = refuse_capture(static_cast<hipStream_t>(stream), "rb_snapshot");
+    if (st != PA_OK) return st;
+    st = capsule_copy(r, static_cast<char*>(capsule), r->pinned, r->count, r->head, true,
+                      static_cast<hipStream_t>(stream));
     if (st != PA_OK) return st;
     return rb_get_state(ring, state);
 }
 
 extern "C" pa_status rb_restore(rb_ring* ring, const void* capsule, size_t capsule_bytes, const rb_state* state,
                                 void* stream) {
-    pa::clear_error();
+    clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
     PA_CHECK_ARG(r && state, PA_EINVAL, "rb_restore: null argument");
     PA_CHECK_ARG(!r->staged, PA_ESTATE, "rb_restore: a staged frame is pending; commit it first");
@@ -261,13 +358,18 @@ extern "C" pa_status rb_restore(rb_ring* ring, const void* capsule, size_t capsu
     const size_t need = capsule_bytes_of(r, state->pinned + (int64_t)state->count * r->cfg.tokens_per_frame);
     PA_CHECK_ARG(capsule || need == 0, PA_EINVAL, "rb_restore: null capsule");
     PA_CHECK_ARG(capsule_bytes >= need, PA_ERANGE, "rb_restore: capsule %zu bytes < %zu needed", capsule_bytes, need);
-    pa_status st = capsule_copy(r, const_cast<char*>(static_cast<const char*>(capsule)), state->pinned, state->count,
-                                state->head, false, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pa_status st = refuse_capture(s, "rb_restore");
+    if (st != PA_OK) return st;
+    st = capsule_copy(r, const_cast<char*>(static_cast<const char*>(capsule)), state->pinned, state->count,
+                      state->head, false, s);
     if (st != PA_OK) return st;
     r->head = state->head;
     r->count = state->count;
     r->pinned = state->pinned;
     r->frames_pushed = fp;
-    return PA_OK;
+    st = fence_spare(r, s);
+    if (st != PA_OK) return st;
+    return publish_state(r, s);
 }
 

@@ -84,3 +84,171 @@ def test_overlapped_pushes_match_synchronous_pushes():
         assert torch.equal(x, y), f"step {i}: overlapped result differs from the synchronous one"
     assert torch.equal(a_sc.k_buf, b_sc.k_buf) and torch.equal(a_sc.v_buf, b_sc.v_buf)
     assert a_sc.ring.state() == b_sc.ring.state()
+
+
+# ------------------------------------------------- graph capture on a spare ring
+# A spare-slot ring moves its window with every commit. With a bound state
+# word the kernels read the window position when they run, so ten steps
+# captured once replay correctly over many stage/commit cycles.
+
+def _spare_setup(s, word=True):
+    sc = Scenario(s, spare_slots=1)
+    if word:
+        sc.word = torch.zeros(4, dtype=torch.int32, device="cuda")
+        sc.ring.bind_state_word(sc.word)
+    return sc
+
+
+def test_captured_steps_replay_across_commits():
+    L = lib()
+    s = configs.PI05_1L.with_(name="spare_graph", cfg_id=61, num_layers=2, tokens_per_frame=256)
+    _banner("captured 10-step loop on a spare-slot ring, replayed over 7 stage/commit cycles")
+    sc = _spare_setup(s)
+    producer, consumer = torch.cuda.Stream(), torch.cuda.current_stream()
+    W = s.num_slots
+    for f in range(W):                            # fill the window: capture needs it full
+        sc.stage(f, producer)
+        sc.commit(consumer)
+    steps = s.steps_per_frame
+    args = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_F32, 0)
+    wsb = L.pattn_workspace_bytes(sc.ring, args)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    qkv_h = [synth.suffix_qkv(s, 0, k) for k in range(steps)]
+    qkv = [tuple(dev(a) for a in t) for t in qkv_h]
+    shape = (s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim)
+    outs = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(steps)]
+    eager = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(steps)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        cs = torch.cuda.current_stream()
+        for k in range(steps):
+            L.pattn_step(sc.ring, args, *qkv[k], outs[k], ws, wsb, cs)
+    state = np.asarray(sc.word.cpu())
+    assert list(state[:3]) == [sc.ring.state()["head"], W, s.pin_tokens]
+    for f in range(W, W + 7):
+        sc.stage(f, producer)
+        sc.commit(consumer)
+        g.replay()                                 # on the consumer (current) stream, after the commit
+        torch.cuda.synchronize()
+        replayed = [o.clone() for o in outs]
+        for k in range(steps):
+            L.pattn_step(sc.ring, args, *qkv[k], eager[k], ws, wsb, consumer)
+        torch.cuda.synchronize()
+        for k in range(steps):
+            assert torch.equal(replayed[k], eager[k]), f"frame {f} step {k}: replay differs from eager"
+        for k in (0, steps - 1):
+            got = replayed[k].cpu().numpy().astype(np.float64)
+            for layer in range(s.num_layers):
+                ref = sc.oracle_step(*qkv_h[k], layer)
+                assert rel_err(got[layer], ref) <= 2e-2, (f, k, layer)
+        assert list(np.asarray(sc.word.cpu())[:2]) == [sc.ring.state()["head"], W]
+    del g
+
+
+def _refused_under_capture(fn):
+    """Run fn inside a stream capture; return the PattnError it raised (the
+    capture itself is closed normally around a small kernel)."""
+    L = lib()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    pad = torch.zeros(16, device="cuda")
+    torch.cuda.synchronize()
+    err = None
+    with torch.cuda.graph(g, stream=side):
+        pad.add_(1.0)
+        try:
+            fn(torch.cuda.current_stream())
+        except L.PattnError as e:
+            err = e
+    del g
+    return err
+
+
+def test_capture_is_refused_where_a_replay_would_be_stale():
+    L = lib()
+    s = configs.PI05_1L.with_(name="spare_refuse", cfg_id=62, num_layers=1, tokens_per_frame=128)
+    _banner("capture refusals: spare ring without a state word, window not full, ring calls")
+    producer, consumer = torch.cuda.Stream(), torch.cuda.current_stream()
+    args = L.pattn_args(0, 1, s.n_q_heads, s.n_dyn, s.scale, L.PA_F32, 0)
+    q, kd, vd = (dev(a) for a in synth.suffix_qkv(s, 0, 0))
+    out = torch.empty((1, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+
+    def step_on(sc):
+        wsb = L.pattn_workspace_bytes(sc.ring, args)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        return lambda st: L.pattn_step(sc.ring, args, q, kd, vd, out, ws, wsb, st)
+
+    nowrd = _spare_setup(s, word=False)            # full window, no state word
+    for f in range(s.num_slots):
+        nowrd.stage(f, producer)
+        nowrd.commit(consumer)
+    e = _refused_under_capture(step_on(nowrd))
+    assert e is not None and e.status == L.PA_ESTATE and "state word" in str(e)
+    partial = Scenario(s)                          # no spare slot, window not full yet
+    partial.push(0)
+    e = _refused_under_capture(step_on(partial))
+    assert e is not None and e.status == L.PA_ESTATE and "full window" in str(e)
+    k0, v0 = (dev(a) for a in synth.frame_kv(s, 5))
+    e = _refused_under_capture(lambda st: partial.ring.push_frame(k0, v0, st))
+    assert e is not None and e.status == L.PA_ESTATE
+    assert partial.ring.state()["frames_pushed"] == 1       # the refused push changed nothing
+    full = Scenario(s)                             # no spare slot, full window: allowed
+    for f in range(s.num_slots):
+        full.push(f)
+    assert _refused_under_capture(step_on(full)) is None
+
+
+def _steps_then(sc, s, stage_after, n_steps=10):
+    """Enqueue n_steps attention steps on the consumer, then `stage_after()`
+    (which moves the spare slot onto a frame those steps read) and a stage
+    on the producer; returns the steps' outputs."""
+    L = lib()
+    consumer = torch.cuda.current_stream()
+    args = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, 0)
+    wsb = L.pattn_workspace_bytes(sc.ring, args)
+    wss = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(n_steps)]
+    q, kd, vd = (dev(a) for a in synth.suffix_qkv(s, 0, 3))
+    outs = [torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+            for _ in range(n_steps)]
+    for i in range(n_steps):
+        L.pattn_step(sc.ring, args, q, kd, vd, outs[i], wss[i], wsb, consumer)
+    stage_after()
+    return outs, (q, kd, vd), args
+
+
+@pytest.mark.parametrize("move", ["push", "restore"])
+def test_stage_after_push_or_restore_waits_for_earlier_steps(move):
+    """rb_push_frame and rb_restore move the spare slot onto a frame that
+    steps enqueued before them still read; a stage on another stream right
+    after must wait for those steps (their results equal a synchronous run)."""
+    L = lib()
+    s = configs.PI05_18L.with_(name=f"spare_fence_{move}", cfg_id=63, model_dim=0, hidden_dim=0)
+    _banner(f"stage after {move} waits for earlier steps (18 layers)")
+    producer, consumer = torch.cuda.Stream(), torch.cuda.current_stream()
+    sc = Scenario(s, spare_slots=1)
+    for f in range(s.num_slots + 1):
+        sc.push(f)
+    cap = torch.empty(sc.ring.capsule_bytes(), dtype=torch.uint8, device="cuda")
+    snap = sc.ring.snapshot(cap)
+    for f in range(s.num_slots + 1, s.num_slots + 3):
+        sc.push(f)
+    torch.cuda.synchronize()
+    # reference: the same steps on the same window, alone
+    ref_outs, qkv, args = _steps_then(sc, s, lambda: None, n_steps=1)
+    torch.cuda.synchronize()
+    nxt = tuple(dev(a) for a in synth.frame_kv(s, 99))
+
+    def move_then_stage():
+        if move == "push":
+            sc.ring.push_frame(*nxt, consumer)
+        else:
+            sc.ring.restore(cap, snap, stream=consumer)
+        sc.ring.stage_frame(*tuple(dev(a) for a in synth.frame_kv(s, 100)), producer)
+
+    outs, _, _ = _steps_then(sc, s, move_then_stage)
+    sc.ring.commit_frame(consumer)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref_outs[0]), f"{move}: step {i} enqueued before the {move} saw a staged frame"

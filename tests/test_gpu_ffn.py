@@ -116,11 +116,23 @@ def test_denoise_step_with_ffn_matches_oracle_chain():
     torch.cuda.synchronize()
     caches = [sc.cached_context(l) for l in range(s.num_layers)]
     ffns = [(gf32[l].astype(np.float64), *(synth.widen(w) for w in wf[l])) for l in range(s.num_layers)]
-    x1, _ = stack.denoise_step(synth.widen(x), [g.astype(np.float64) for g in ga32], s.eps,
-                               [synth.widen(w[0]) for w in wq], [synth.widen(w[1]) for w in wq],
-                               [c[0] for c in caches], [c[1] for c in caches], s.scale, s.n_q_heads, s.n_kv_heads,
-                               s.head_dim, ffns=ffns)
+    x1, trace = stack.denoise_step(synth.widen(x), [g.astype(np.float64) for g in ga32], s.eps,
+                                   [synth.widen(w[0]) for w in wq], [synth.widen(w[1]) for w in wq],
+                                   [c[0] for c in caches], [c[1] for c in caches], s.scale, s.n_q_heads,
+                                   s.n_kv_heads, s.head_dim, ffns=ffns)
     err = rel_err(synth.widen(host(x_d)), x1)
     _banner(f"  full-layer step x rel {err:.3e}")
     assert err <= BAR
     assert int(host(flag)[0]) == 0
+    # every layer's stream (after its FFN): an l-layer step leaves h_l at the
+    # head of the workspace
+    rows, model = s.n_dyn, s.model_dim
+    for nl in range(1, s.num_layers + 1):
+        st_l = L.pa_stack(nl, s.n_dyn, s.model_dim, s.n_q_heads, keep[0], keep[1], s.eps, s.scale, 0.1, 0,
+                          s.ffn_dim, keep[2], keep[3], keep[4])
+        L.pa_denoise_step(sc.ring, st_l, dev(x), dev(ga32), s.model_dim, flag, ws, wsb, gamma_ffn=dev(gf32))
+        torch.cuda.synchronize()
+        h_l = synth.widen(host(ws[: rows * model * 2].view(torch.int16).reshape(rows, model)))
+        e = rel_err(h_l, trace[nl - 1]["h"])
+        _banner(f"  full-layer step h_{nl} rel {e:.3e}")
+        assert e <= BAR

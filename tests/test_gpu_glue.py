@@ -389,6 +389,26 @@ def test_denoise_step_matches_oracle_chain(hq, layers, model):
     _banner(f"denoise step x rel {err:.3e}")
     assert err <= BAR
     assert int(host(flag)[0]) == 0
+    # every layer's stream: a step over layers [0, l) leaves h_l at the head
+    # of the workspace (the velocity an l-layer stack would use)
+    worst = 0.0
+    for nl in range(1, s.num_layers + 1):
+        st = L.pa_stack(nl, s.n_dyn, s.model_dim, s.n_q_heads, rig.wqkv_d, rig.wo_d, s.eps, s.scale, 0.1)
+        xl = dev(x)
+        L.pa_denoise_step(rig.sc.ring, st, xl, dev(gam32), s.model_dim, flag, rig.ws, rig.wsb)
+        h_l = stream_h(rig.ws, s.n_dyn, s.model_dim)
+        e = rel_err(h_l, trace[nl - 1]["h"])
+        worst = max(worst, e)
+        assert e <= BAR, f"layer {nl}: h rel {e:.3e}"
+        assert rel_err(synth.widen(host(xl)), stack.euler(synth.widen(x), trace[nl - 1]["h"])) <= BAR
+    _banner(f"denoise step worst per-layer h rel {worst:.3e}")
+    assert int(host(flag)[0]) == 0
+
+
+def stream_h(ws, rows, model):
+    """h_L as pa_denoise_step leaves it: the workspace's first rows x model bf16 words."""
+    torch.cuda.synchronize()
+    return synth.widen(host(ws[: rows * model * 2].view(torch.int16).reshape(rows, model)))
 
 
 def test_graph_replay_matches_eager():

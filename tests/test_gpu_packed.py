@@ -113,6 +113,8 @@ class PackedRig:
         L.pa_denoise_step(self.sc.ring, st, x_d, self.g_d, self.s.model_dim, flag, self.ws, wsb,
                           gamma_ffn=self.gf_d if self.wf else None)
         torch.cuda.synchronize()
+        rows, model = self.s.n_dyn, self.s.model_dim
+        self.last_h = host(self.ws[: rows * model * 2].view(torch.int16).reshape(rows, model)).copy()
         return host(x_d), int(host(flag)[0])
 
     def oracle(self, x: np.ndarray):
@@ -122,11 +124,11 @@ class PackedRig:
         if self.wf:
             ffns = [(self.gamma_ffn[l].astype(np.float64), *(synth.widen(w) for w in self.wf[l]))
                     for l in range(s.num_layers)]
-        x1, _ = stack.denoise_step(synth.widen(x), [g.astype(np.float64) for g in self.gamma], s.eps,
-                                   [synth.widen(w[0]) for w in self.wq], [synth.widen(w[1]) for w in self.wq],
-                                   [c[0] for c in caches], [c[1] for c in caches], s.scale, s.n_q_heads,
-                                   s.n_kv_heads, s.head_dim, ffns=ffns)
-        return x1
+        x1, trace = stack.denoise_step(synth.widen(x), [g.astype(np.float64) for g in self.gamma], s.eps,
+                                       [synth.widen(w[0]) for w in self.wq], [synth.widen(w[1]) for w in self.wq],
+                                       [c[0] for c in caches], [c[1] for c in caches], s.scale, s.n_q_heads,
+                                       s.n_kv_heads, s.head_dim, ffns=ffns)
+        return x1, trace[-1]["h"]
 
 
 CASES = {
@@ -149,13 +151,17 @@ def test_packed_stack_is_bit_identical_to_unpacked(case):
     rig = PackedRig(s, frames, ffn)
     x = synth.flow_x(s, 1)
     x_plain, f_plain = rig.run(x, packed=False)
+    h_plain = rig.last_h
     x_packed, f_packed = rig.run(x, packed=True)
     np.testing.assert_array_equal(x_packed, x_plain)
+    np.testing.assert_array_equal(rig.last_h, h_plain)        # the velocity h_L, bit for bit
     assert f_plain == 0 and f_packed == 0
     if check_oracle:
-        err = rel_err(synth.widen(x_packed), rig.oracle(x))
-        _banner(f"  packed x rel {err:.3e}")
-        assert err <= BAR
+        x1, h_last = rig.oracle(x)
+        err = rel_err(synth.widen(x_packed), x1)
+        err_h = rel_err(synth.widen(rig.last_h), h_last)
+        _banner(f"  packed x rel {err:.3e}, h_L rel {err_h:.3e}")
+        assert err <= BAR and err_h <= BAR
 
 
 def test_packed_stack_flags_nonfinite_input():

@@ -1,7 +1,8 @@
 """Pins of the layer glue oracle (QKV split, out-projection, Euler) and of the
-shared-KV decode oracle. The end-to-end denoising step chains pinned ops and
-is itself "parity unpinned" (the pages give no layer glue); the checks here
-fix its wiring with cases whose answer is known in closed form.
+shared-KV decode oracle. The end-to-end denoising step is pinned against the
+same step written with torch's own float64 operators, on inputs chosen so
+that a wiring mistake (wrong stream fed forward, wrong gamma, wrong velocity,
+a dropped attention region) fails it; closed forms fix the pieces.
 """
 
 import numpy as np
@@ -69,17 +70,154 @@ def test_denoise_step_with_zero_out_projection_is_x_times_0_9():
 
 
 def test_layer_attention_appends_step_kv_after_cache():
-    """With the cache's values all equal to c, and W_v producing c too, o = c."""
-    hq, hkv, d, model, n = 2, 1, 4, 4, 3
-    c = np.array([0.5, -1.0, 2.0, 0.25])
+    """All keys zero, so every logit is 0 and attention is the plain mean of
+    the values over the whole context [cache; step]. The cache's values are
+    c1 (T rows) and the step's own values are c2 (n rows, produced by W_v from
+    a row-constant y), so o = (T c1 + n c2) / (T + n). Dropping the step's
+    K/V would give c1, dropping the cache c2."""
+    hq, hkv, d, model, n, T = 2, 1, 4, 4, 3, 5
+    c1 = np.array([0.5, -1.0, 2.0, 0.25])
+    c2 = np.array([-2.0, 1.5, 0.75, 3.0])
     w = np.zeros(((hq + 2) * d, model))
-    w[(hq + hkv) * d:, :] = 0.0
-    # y has unit RMS rows; make v = y @ Wv^T = const c by using a row-constant y
-    h = np.ones((n, model))
-    w[(hq + hkv) * d:, 0] = c              # v = c * y[:, 0] = c * 1
-    res = stack.layer(h, np.ones(model), 0.0, w, np.zeros((5, hkv, d)), np.broadcast_to(c, (5, hkv, d)),
+    h = np.ones((n, model))                 # unit RMS, so y = 1 in every column
+    w[(hq + hkv) * d:, 0] = c2              # v_step = c2 * y[:, 0] = c2
+    res = stack.layer(h, np.ones(model), 0.0, w, np.zeros((T, hkv, d)), np.broadcast_to(c1, (T, hkv, d)),
                       np.zeros((model, hq * d)), 1.0, hq, hkv, d)
-    np.testing.assert_allclose(res["o"], np.broadcast_to(round_bf16(c), (n, hq, d)))
+    want = round_bf16((T * c1 + n * c2) / (T + n))
+    np.testing.assert_allclose(res["o"], np.broadcast_to(want, (n, hq, d)))
+    assert not np.allclose(want, round_bf16(c1)) and not np.allclose(want, round_bf16(c2))
+
+
+# ------------------------------------------- the denoising step end to end ----
+# An independent pin of the layer glue: the same step written with torch's
+# own float64 operators (F.rms_norm with the gamma as its weight, a matmul
+# for the packed projection, F.scaled_dot_product_attention over
+# cat([cache, step K/V]) with the KV heads repeated for their query heads,
+# F.silu for the FFN, and torch's bf16 conversion at every bf16 store). The
+# inputs make every part of the wiring matter: a nonzero out-projection,
+# a different gamma per layer, different cache and step K/V, two KV heads.
+
+def _torch_denoise_step(x, gammas, eps, wqkv, wo, ck, cv, scale, hq, hkv, d, ffns=None, dt=0.1):
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.tensor(np.asarray(a, np.float64), dtype=torch.float64)   # noqa: E731
+    bf = lambda v: v.to(torch.bfloat16).to(torch.float64)                          # noqa: E731
+    n, model = x.shape
+    h = t(x)
+    hs, os_ = [], []
+    for l in range(len(wqkv)):
+        y = bf(F.rms_norm(h, (model,), weight=t(gammas[l]), eps=eps))
+        qkv = y @ t(wqkv[l]).T
+        q = bf(qkv[:, :hq * d]).reshape(n, hq, d)
+        k = bf(qkv[:, hq * d:(hq + hkv) * d]).reshape(n, hkv, d)
+        v = bf(qkv[:, (hq + hkv) * d:]).reshape(n, hkv, d)
+        K = torch.cat([t(ck[l]), k], 0).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+        V = torch.cat([t(cv[l]), v], 0).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+        o = F.scaled_dot_product_attention(q.permute(1, 0, 2), K, V, scale=scale)
+        o = bf(o.permute(1, 0, 2).reshape(n, hq * d))
+        h = bf(h + o @ t(wo[l]).T)
+        if ffns is not None:
+            g2, wg, wu, wd = ffns[l]
+            y2 = bf(F.rms_norm(h, (model,), weight=t(g2), eps=eps))
+            act = bf(F.silu(y2 @ t(wg).T) * (y2 @ t(wu).T))
+            h = bf(h + act @ t(wd).T)
+        os_.append(o.numpy().reshape(n, hq, d))
+        hs.append(h.numpy())
+    return bf(t(x) - dt * h).numpy(), hs, os_
+
+
+def _glue_case(L=3, n=5, model=32, hq=4, hkv=2, d=8, T=7, ffn=0, seed=21):
+    rng = np.random.default_rng(seed)
+    r = lambda *s: rng.standard_normal(s)          # noqa: E731
+    x = round_bf16(r(n, model))
+    gammas = [1.0 + 0.4 * r(model) for _ in range(L)]
+    wqkv = [round_bf16(r((hq + 2 * hkv) * d, model) / np.sqrt(model)) for _ in range(L)]
+    wo = [round_bf16(r(model, hq * d) / np.sqrt(hq * d)) for _ in range(L)]
+    ck = [round_bf16(r(T, hkv, d)) for _ in range(L)]
+    cv = [round_bf16(r(T, hkv, d)) for _ in range(L)]
+    ffns = None
+    if ffn:
+        ffns = [(1.0 + 0.3 * r(model), round_bf16(r(ffn, model) / np.sqrt(model)),
+                 round_bf16(r(ffn, model) / np.sqrt(model)), round_bf16(r(model, ffn) / np.sqrt(ffn)))
+                for _ in range(L)]
+    return dict(x=x, gammas=gammas, eps=1e-6, wqkv=wqkv, wo=wo, ck=ck, cv=cv, scale=1 / np.sqrt(d), hq=hq,
+                hkv=hkv, d=d, ffns=ffns)
+
+
+def _oracle_step(c):
+    x1, trace = stack.denoise_step(c["x"], c["gammas"], c["eps"], c["wqkv"], c["wo"], c["ck"], c["cv"], c["scale"],
+                                   c["hq"], c["hkv"], c["d"], c["ffns"])
+    return x1, [tr["h"] for tr in trace], [tr["o"] for tr in trace]
+
+
+def _glue_error(c):
+    """Worst relative difference (per tensor, max|a - b| / max|b|) between the
+    oracle's step and the torch chain over x_{k+1}, every layer's h and o."""
+    x1, hs, os_ = _oracle_step(c)
+    tx1, ths, tos = _torch_denoise_step(c["x"], c["gammas"], c["eps"], c["wqkv"], c["wo"], c["ck"], c["cv"],
+                                        c["scale"], c["hq"], c["hkv"], c["d"], c["ffns"])
+    rel = lambda a, b: float(np.max(np.abs(a - b)) / np.max(np.abs(b)))   # noqa: E731
+    return max([rel(x1, tx1)] + [rel(a, b) for a, b in zip(hs, ths)] + [rel(a, b) for a, b in zip(os_, tos)])
+
+
+# Both sides compute in float64 and round to bf16 at the same points, so they
+# differ only where a float64 summation-order difference flips a bf16
+# rounding; one flip moves a value by at most 2^-8 of itself.
+GLUE_TOL = 2.0 ** -8
+
+
+@pytest.mark.parametrize("ffn", [0, 64])
+def test_denoise_step_matches_a_torch_float64_chain(ffn):
+    c = _glue_case(ffn=ffn)
+    assert _glue_error(c) <= GLUE_TOL
+
+
+def test_denoise_step_pin_catches_planted_wiring_mistakes(monkeypatch):
+    """Each mistake below is planted in the oracle (by patching the names the
+    oracle's step calls) and must make the torch-chain pin fail."""
+    c = _glue_case()
+    assert _glue_error(c) <= GLUE_TOL
+    real_layer, real_attn, real_euler = stack.layer, stack.full_attention, stack.euler
+
+    def plant(name, fn):
+        with monkeypatch.context() as m:
+            m.setattr(stack, name, fn)
+            err = _glue_error(c)
+        assert err > 10 * GLUE_TOL, f"the pin did not catch the planted mistake ({name}): {err:.3g}"
+
+    first = {}
+
+    def layer_fed_x(h, *a, **k):               # every layer reads x instead of h_{l-1}
+        first.setdefault("h", h)
+        return real_layer(first["h"], *a, **k)
+    plant("layer", layer_fed_x)
+
+    first.clear()
+
+    def layer_gamma0(h, g, *a, **k):            # every layer uses gamma_0
+        first.setdefault("g", g)
+        return real_layer(h, first["g"], *a, **k)
+    plant("layer", layer_gamma0)
+
+    hist = []
+
+    def layer_rec(*a, **k):
+        r = real_layer(*a, **k)
+        hist.append(r["h"])
+        return r
+
+    def euler_h1(x, v, dt=0.1):                 # velocity taken from h_1
+        return real_euler(x, hist[0], dt)
+    with monkeypatch.context() as m:
+        m.setattr(stack, "layer", layer_rec)
+        m.setattr(stack, "euler", euler_h1)
+        err = _glue_error(c)
+    assert err > 10 * GLUE_TOL
+
+    n = c["x"].shape[0]
+    plant("full_attention", lambda q, k, v, s: real_attn(q, k[:-n], v[:-n], s))    # step K/V dropped
+    plant("full_attention", lambda q, k, v, s: real_attn(q, k[-n:], v[-n:], s))    # cache dropped
+    plant("full_attention", lambda q, k, v, s: real_attn(q, k, v, s * 2))          # scale applied twice
 
 
 def test_decode_streams_see_only_their_own_tail():
