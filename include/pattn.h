@@ -251,6 +251,23 @@ pa_status pattn_step_timed(const rb_ring* ring, const pattn_args* args, const vo
                            void* workspace, size_t ws_bytes, void* stream,
                            void* ev_begin, void* ev_end);
 
+/* pattn_step for callers that cannot allocate device memory or pass a
+ * workspace (code under graph capture that must not hold a buffer of its
+ * own, tight serving loops, harnesses that forbid allocation). Same
+ * arguments, results and errors as pattn_step, without the workspace: the
+ * split partials go to a fixed device array of pattn_noalloc_scratch_bytes()
+ * bytes (32 MiB) that the library holds on every GPU it runs on until the
+ * process ends; it allocates nothing, here or later. PA_ERANGE when the call
+ * needs more than that (pattn_workspace_bytes > pattn_noalloc_scratch_bytes;
+ * the 18-layer long-history step with bf16 partials fits). Nothing in the
+ * array needs clearing between calls: every partial a call reads it writes
+ * first. All calls on one GPU share the array: calls that can overlap on one
+ * GPU (different streams with no ordering between them) race on it, so
+ * order them or use pattn_step. */
+size_t pattn_noalloc_scratch_bytes(void);
+pa_status pattn_step_noalloc(const rb_ring* ring, const pattn_args* args, const void* q,
+                             const void* k_dyn, const void* v_dyn, void* out, void* stream);
+
 /* ========================================================================
  * Shared-KV decode readers (OxyGen review, core method and method
  * details): G decode streams, one query token each, read the same cached

@@ -39,6 +39,7 @@ EXPORTS = (
     "pa_denoise_step_workspace_bytes", "pa_denoise_step", "rb_capsule_bytes", "rb_snapshot", "rb_restore",
     "rb_stage_frame", "rb_commit_frame", "ffn_swiglu_workspace_bytes", "ffn_swiglu", "pattn_fused_workspace_bytes",
     "pattn_fused_step", "pa_pack_weight", "pattn_operand_q_bytes", "pattn_pack_q", "rb_bind_state_word",
+    "pattn_noalloc_scratch_bytes", "pattn_step_noalloc",
 )
 
 
@@ -108,6 +109,8 @@ _sig("rb_snapshot", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
 _sig("rb_restore", _i32, _vp, _vp, _sz, C.POINTER(RbState), _vp)
 _sig("pattn_workspace_bytes", _sz, _vp, C.POINTER(PattnArgs))
 _sig("pattn_step", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("pattn_noalloc_scratch_bytes", _sz)
+_sig("pattn_step_noalloc", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp)
 _sig("pattn_step_timed", _i32, _vp, C.POINTER(PattnArgs), _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp)
 _sig("pa_denoise_step_workspace_bytes", _sz, _vp, C.POINTER(PaStack))
 _sig("pa_denoise_step", _i32, _vp, C.POINTER(PaStack), _vp, _vp, _vp, C.c_int64, _vp, _vp, _sz, _vp)
@@ -247,6 +250,16 @@ def pattn_workspace_bytes(ring: Ring, args: PattnArgs) -> int:
 def pattn_step(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, workspace, ws_bytes: int, stream=None):
     _check(_lib.pattn_step(ring.handle, C.byref(args), ptr(q), ptr(k_dyn), ptr(v_dyn), ptr(out), ptr(workspace),
                            ws_bytes, _stream(stream)), "pattn_step")
+
+
+def pattn_noalloc_scratch_bytes() -> int:
+    return _lib.pattn_noalloc_scratch_bytes()
+
+
+def pattn_step_noalloc(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, stream=None):
+    """pattn_step with the partials in the library's fixed device scratch (no workspace, no allocation)."""
+    _check(_lib.pattn_step_noalloc(ring.handle, C.byref(args), ptr(q), ptr(k_dyn), ptr(v_dyn), ptr(out),
+                                   _stream(stream)), "pattn_step_noalloc")
 
 
 def pattn_step_timed(ring: Ring, args: PattnArgs, q, k_dyn, v_dyn, out, workspace, ws_bytes: int, stream=None,

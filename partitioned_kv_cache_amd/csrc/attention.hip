@@ -21,6 +21,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gemm.h"
@@ -1090,6 +1091,54 @@ extern "C" pa_status pattn_step_timed(const rb_ring* ring, const pattn_args* a, 
                                       const void* v_dyn, void* out, void* ws, size_t ws_bytes, void* stream,
                                       void* ev_begin, void* ev_end) {
     return step_impl(ring, a, q, k_dyn, v_dyn, out, ws, ws_bytes, stream, ev_begin, ev_end);
+}
+
+// ---------------------------------------------------------------------------
+// pattn_step for callers that cannot allocate: the split partials go to a
+// file-scope device array instead of a caller workspace. Each GPU holds its
+// own copy of the array (allocated with the code object, kept until the
+// process ends); its address on a device is looked up once, with that
+// device current, and cached. The array's name is only a host-side stand-in:
+// host code uses the looked-up address, never the name.
+namespace pa {
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(32) << 20;   // covers 18 layers x 416 rows x 7 splits, bf16
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+static void* g_scratch_dev[NOALLOC_MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+static pa_status noalloc_scratch(void** out) {
+    int dev = -1;
+    PA_HIP(hipGetDevice(&dev));
+    PA_CHECK_ARG(dev >= 0 && dev < NOALLOC_MAX_DEVICES, PA_EDEVICE, "pattn_step_noalloc: device %d beyond %d", dev,
+                 NOALLOC_MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        PA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        PA_CHECK_ARG(p, PA_EDEVICE, "pattn_step_noalloc: no address for the scratch array on device %d", dev);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return PA_OK;
+}
+}  // namespace pa
+
+extern "C" size_t pattn_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" pa_status pattn_step_noalloc(const rb_ring* ring, const pattn_args* a, const void* q, const void* k_dyn,
+                                        const void* v_dyn, void* out, void* stream) {
+    clear_error();
+    PA_CHECK_ARG(ring && a, PA_EINVAL, "pattn_step_noalloc: null argument");
+    const size_t need = pattn_workspace_bytes(ring, a);
+    PA_CHECK_ARG(need > 0, PA_ESHAPE, "pattn_step_noalloc: arguments rejected (see pattn_workspace_bytes)");
+    PA_CHECK_ARG(need <= NOALLOC_SCRATCH_BYTES, PA_ERANGE,
+                 "pattn_step_noalloc: the call needs %zu bytes of partials, above the fixed %zu-byte scratch; "
+                 "use pattn_step with a workspace", need, NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    pa_status st = noalloc_scratch(&ws);
+    if (st != PA_OK) return st;
+    return step_impl(ring, a, q, k_dyn, v_dyn, out, ws, NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 // Chunks of 16 bytes in the PA_Q_OPERAND form of q, 0 if not applicable.
