@@ -1,30 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of partitioned attention over a ring-buffer KV cache on one MI355X.
 
-Headline workload (``--workload long_history_18L``, the default): 18 layers,
+Headline workload (the default): the long-history configuration, 18 layers,
 8 query heads sharing 1 KV head of width 256, bf16; a pinned prefix of 256
 tokens and a sliding window of 8 frames x 768 tokens in the ring; a 51-token
-dynamic suffix; 10 denoising steps per frame; a new frame pushed (and the
-oldest evicted) every 10 steps. One step = one partitioned-attention pass
-over all 18 layers (split-KV partials + log-sum-exp combine) with that
-step's suffix Q/K/V; the frame push is inside the timed loop, once per 10
-steps. Inputs are seeded synthetic tensors already resident in HBM. The
-headline is the cold case: three independent rings (sessions) are served
-round-robin, so each step's 118 MB of K/V comes from HBM rather than the
-256 MB last-level cache; the single-ring (warm) figure is reported beside it,
-as are microseconds per call on the two small configurations.
+dynamic suffix; 10 denoising steps per frame. One headline step is one
+partitioned-attention pass over all 18 layers at once (layer-batched: every
+layer's suffix Q/K/V of the step is given; split-KV partials + log-sum-exp
+combine). Each ring pushes a new frame (evicting the oldest) before every
+10th of its own steps, and the rings' frame boundaries are staggered so that
+pushes fall inside any timed window of 10 or more steps; the push count in
+the timed region is reported. Inputs are seeded synthetic tensors already
+resident in HBM. The headline is the cold case: three independent rings
+(sessions) are served round-robin, so each step's 118 MB of K/V comes from
+HBM rather than the 256 MB last-level cache; the single-ring (warm) figure
+is reported beside it, as are microseconds per call on the two small
+configurations.
 
-Reported beside it in the same JSON line: the whole denoising step of the
-Pi0.5-like 18-layer stack (AdaRMSNorm fused into the packed QKV projection,
-partitioned attention over a 48 + 2 x 768 token cache, out-projection with
-residual, Euler update; the gamma MLP batched once per frame), replayed as
-a captured graph, in microseconds per step; and the shared-KV multi-reader
-frame (the action suffix plus 16 decode streams with private tails over the
-long-history cache), in frames/s and decode tokens/s.
+Reported beside it in the same JSON line:
+* the chained denoising step on the long-history cache (norm -> packed QKV ->
+  attention -> out-projection with residual, layer by layer, 18 layers,
+  Euler update), replayed as a captured graph, in microseconds per step:
+  this is the step a real loop runs, since layer l + 1's Q needs layer l's
+  output;
+* the same chained step of the Pi0.5-like 18-layer stack (48 + 2 x 768
+  token cache), with and without the SwiGLU FFN;
+* the shared-KV multi-reader frame (the action suffix plus 16 decode streams
+  with private tails over the long-history cache), in frames/s and decode
+  tokens/s.
 
-``roofline`` describes the split-KV partial kernel, timed live with HIP
-events recorded around it on the launch stream. ``cpu_baseline`` is the
-float64 CPU oracle timed on a bounded sample of the same workload.
+``roofline`` describes the split-KV partial kernel of the headline step,
+timed in a separate pass of at least 20 launches with HIP events recorded
+around it on the launch stream (same cold round-robin). ``cpu_baseline`` is
+the float64 CPU oracle timed on bounded samples of the long-history step,
+the Pi0.5-like single-layer step and the Pi0.5-like 18-layer stack step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -105,7 +114,7 @@ def attention_work(s, cached_tokens):
     return kv_cached + q_bytes + dyn, flops, kv_cached
 
 
-def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0):
+def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0, partials_f32=0):
     """The headline step. With n_rings > 1, that many independent rings (one
     per session) are served round-robin, one step each in turn; three rings
     hold 354 MB of K/V, more than the 256 MB last-level cache (MALL), so
@@ -129,7 +138,8 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0):
             ring.push_frame(*pool[(f + r) % 4])
         rings.append(ring)
         bufs.append((k_buf, v_buf))
-    args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits, q_layout)
+    args_ = L.pattn_args(0, s.num_layers, s.n_q_heads, s.n_dyn, s.scale, L.PA_BF16, args.splits, q_layout,
+                         partials_f32)
     if q_layout == L.PA_Q_OPERAND:
         # Q in the kernel's operand order, as a producer that writes Q (the
         # stack's QKV projection) lays it out; converted once, before timing
@@ -143,13 +153,21 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0):
     out = torch.empty((s.num_layers, s.n_dyn, s.n_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     frame = [s.num_slots] * n_rings
+    spf = s.steps_per_frame
+    # Ring r serves global steps i = j * n_rings + r (its own step j) and
+    # pushes before its own steps j with (j + phase_r) % spf == 0; the phases
+    # spread the rings' frame boundaries evenly, so globally a push falls
+    # about every spf steps and any timed window of spf or more steps holds one.
+    phase = [(r * spf) // n_rings for r in range(n_rings)]
+    pushes = [0]
 
     def one_step(i, ev=None):
         r, j = i % n_rings, i // n_rings         # ring, and that ring's own step count
-        if j % s.steps_per_frame == 0:
+        if (j + phase[r]) % spf == 0:
             rings[r].push_frame(*pool[frame[r] % 4])
             frame[r] += 1
-        q, kd, vd = steps_in[j % s.steps_per_frame]
+            pushes[0] += 1
+        q, kd, vd = steps_in[(j + phase[r]) % spf]
         if ev is None:
             L.pattn_step(rings[r], args_, q, kd, vd, out, ws, wsb, stream)
         else:
@@ -157,38 +175,62 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0):
 
     for i in range(args.warmup):
         one_step(i)
-    # The partial kernel is timed on one step of every frame (the middle
-    # one): an event pair on every launch would add dispatch latency to every
-    # step of the timed loop.
-    half = s.steps_per_frame // 2
-    sampled = [i for i in range(args.steps) if ((args.warmup + i) // n_rings) % s.steps_per_frame == half]
-    kev = KernelEvents()
-    events = {i: kev.pair() for i in sampled}
     torch.cuda.synchronize()
+    pushes[0] = 0
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(args.warmup + i, events.get(i))
+        one_step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_ms = [kev.elapsed_ms(a, b) for a, b in events.values()]
+    pushes_timed = pushes[0]
+    # Roofline pass: the partial kernel timed alone on every launch of a
+    # further stretch of the same loop (an event pair around every launch
+    # adds dispatch latency, so this pass is kept out of the throughput).
+    n_kern = max(args.kernel_launches, 20)
+    kev = KernelEvents()
+    evs = [kev.pair() for _ in range(n_kern)]
+    base = args.warmup + args.steps
+    for i in range(n_kern):
+        one_step(base + i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [kev.elapsed_ms(a, b) for a, b in evs]
     kev.close()
+    if not kern_ms:
+        raise RuntimeError("no partial-kernel launch was timed")
     avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    sd = (sum((k / 1e3 - avg_kern_s) ** 2 for k in kern_ms) / len(kern_ms)) ** 0.5
+    # one push alone (both tensors of all 18 layers), averaged over a few
+    push_ev0, push_ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_push = 8
+    push_ev0.record()
+    for i in range(n_push):
+        rings[i % n_rings].push_frame(*pool[i % 4])
+    push_ev1.record()
+    torch.cuda.synchronize()
+    t_push = push_ev0.elapsed_time(push_ev1) / n_push / 1e3
     cached = s.pin_tokens + s.num_slots * s.tokens_per_frame
     algo_bytes, flops, kv_bytes = attention_work(s, cached)
+    t_step = elapsed / args.steps
     res = {
         "elapsed_s": elapsed,
         "steps_per_s": args.steps / elapsed,
-        "ms_per_step": elapsed / args.steps * 1e3,
+        "ms_per_step": t_step * 1e3,
+        "pushes_timed": pushes_timed,
+        "push_us": t_push * 1e6,
         "partial_us": avg_kern_s * 1e6,
+        "partial_us_sd": sd * 1e6,
+        "partial_us_min": min(kern_ms) * 1e3,
+        "partial_us_max": max(kern_ms) * 1e3,
         "timed_launches": len(kern_ms),
         "partial_tflops": flops / avg_kern_s / 1e12,
         "partial_gbs": algo_bytes / avg_kern_s / 1e9,
-        "kv_gbs_step": kv_bytes / (elapsed / args.steps) / 1e9,
+        "kv_gbs_step": kv_bytes / t_step / 1e9,
         "algo_bytes": algo_bytes,
         "flops": flops,
         "splits": args.splits,
         "rings": n_rings,
         "q_layout": "operand" if q_layout else "token_major",
+        "partials": "fp32" if partials_f32 else "bf16",
     }
     for ring in rings:
         ring.close()
@@ -399,11 +441,13 @@ def bench_capsule(args, torch, L, configs, synth, n_calls=50):
     return res
 
 
-def bench_stack(args, torch, L, configs, synth, full_layer=False):
-    """Whole 18-layer denoising step of the Pi0.5-like stack, graph-replayed;
-    with full_layer, every layer also runs the SwiGLU FFN block (its own
-    AdaRMSNorm gamma, gate/up 1024 -> 4096, down 4096 -> 1024)."""
-    s = configs.PI05_18L_FFN if full_layer else configs.PI05_18L
+def bench_stack(args, torch, L, configs, synth, full_layer=False, shape=None):
+    """Whole 18-layer denoising step, chained layer by layer, graph-replayed:
+    the Pi0.5-like stack by default, or `shape` (the long-history cache with
+    the same layer dims); with full_layer, every layer also runs the SwiGLU
+    FFN block (its own AdaRMSNorm gamma, gate/up 1024 -> 4096, down 4096 ->
+    1024)."""
+    s = shape if shape is not None else (configs.PI05_18L_FFN if full_layer else configs.PI05_18L)
     dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()  # noqa: E731
     import numpy as np
     shp = (s.num_layers, s.max_seq_len, s.n_kv_heads, s.head_dim)
@@ -516,9 +560,10 @@ def bench_stack(args, torch, L, configs, synth, full_layer=False):
         "us_per_frame_incl_push_gamma": el / n_frames * 1e6,
         "frames_timed": n_frames,
         "nonfinite_flag": int(flag.item()),
-        "config": {"layers": 18, "model_dim": 1024, "q_heads": 8, "kv_heads": 1, "head_dim": 256,
-                   "pin_tokens": 48, "window": "2x768", "suffix": 51, "steps_per_frame": 10,
-                   "ffn": f"SwiGLU {s.ffn_dim}" if s.ffn_dim else "none"},
+        "config": {"layers": s.num_layers, "model_dim": s.model_dim, "q_heads": s.n_q_heads,
+                   "kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "pin_tokens": s.pin_tokens,
+                   "window": f"{s.num_slots}x{s.tokens_per_frame}", "suffix": s.n_dyn,
+                   "steps_per_frame": s.steps_per_frame, "ffn": f"SwiGLU {s.ffn_dim}" if s.ffn_dim else "none"},
     }
 
 
@@ -627,47 +672,84 @@ def bench_shared_kv(args, torch, L, configs, synth, budgets=(1, 5, 10), n_frames
 
 
 def cpu_baseline(budget_s):
-    """Time the float64 CPU oracle on a bounded sample of the long-history step."""
+    """Time the float64 CPU oracle on bounded samples of three workloads: the
+    long-history 18-layer attention step (the headline), the Pi0.5-like
+    single-layer attention step, and the Pi0.5-like 18-layer stack step
+    (norm, QKV, attention, out-projection per layer, then the Euler update).
+    Each gets its share of budget_s; the long-history step is also timed on
+    one BLAS thread."""
     import numpy as np
     from oracle.attention import full_attention
+    from oracle import stack as ostack
     from partitioned_kv_cache_amd import configs, synth
-    s = configs.LONG_18L
-    pk, pv = synth.pin_kv(s)
-    frames = [synth.frame_kv(s, f % 4) for f in range(s.num_slots)]
-    q, kd, vd = synth.suffix_qkv(s, 0, 0)
-    ctx = []
-    for l in range(s.num_layers):
-        ck = np.concatenate([synth.widen(pk[l])] + [synth.widen(f[0][l]) for f in frames] + [synth.widen(kd[l])])
-        cv = np.concatenate([synth.widen(pv[l])] + [synth.widen(f[1][l]) for f in frames] + [synth.widen(vd[l])])
-        ctx.append((synth.widen(q[l]), ck, cv))
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
 
-    def timed(budget):
-        layers_done = 0
+    def attention_ctx(s):
+        pk, pv = synth.pin_kv(s)
+        frames = [synth.frame_kv(s, f % 4) for f in range(s.num_slots)]
+        q, kd, vd = synth.suffix_qkv(s, 0, 0)
+        ctx = []
+        for l in range(s.num_layers):
+            ck = np.concatenate([synth.widen(pk[l])] + [synth.widen(f[0][l]) for f in frames] + [synth.widen(kd[l])])
+            cv = np.concatenate([synth.widen(pv[l])] + [synth.widen(f[1][l]) for f in frames] + [synth.widen(vd[l])])
+            ctx.append((synth.widen(q[l]), ck, cv))
+        return ctx
+
+    def timed_layers(s, ctx, budget):
+        done = 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 <= budget:
-            l = layers_done % s.num_layers
+            l = done % s.num_layers
             full_attention(ctx[l][0], ctx[l][1], ctx[l][2], s.scale)
-            layers_done += 1
-        return layers_done, time.perf_counter() - t0
+            done += 1
+        return done, time.perf_counter() - t0
 
-    layers_done, el = timed(budget_s)
-    steps = layers_done / s.num_layers
-    res = {"value": steps / el, "unit": "denoise steps/s", "cores": threads, "kind": "oracle",
-           "sample": f"{layers_done} layer-attentions ({steps:.2f} 18-layer steps) of the long-history step, "
-                     f"float64 NumPy, {el:.1f} s; cpu: {_cpu_model()}"}
     try:
-        from threadpoolctl import threadpool_limits
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threadpool_limits = None
+        threads = os.cpu_count() or 1
+    cpu = _cpu_model()
+    # the headline: long-history 18-layer attention step
+    s4 = configs.LONG_18L
+    ctx4 = attention_ctx(s4)
+    n4, el4 = timed_layers(s4, ctx4, budget_s * 0.45)
+    res = {"value": n4 / s4.num_layers / el4, "unit": "denoise steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"long-history 18-layer attention step: {n4} layer-attentions ({n4 / s4.num_layers:.2f} steps) "
+                     f"of frame 0 step 0, float64 NumPy, {el4:.1f} s; cpu: {cpu}; "
+                     f"{len(os.sched_getaffinity(0))} host threads available"}
+    if threadpool_limits is not None:
         with threadpool_limits(1):
-            n1, el1 = timed(budget_s / 2)
-        res["value_1_thread"] = n1 / s.num_layers / el1
-        res["sample_1_thread"] = f"{n1} layer-attentions, one BLAS thread, {el1:.1f} s"
-    except ImportError:
-        pass
+            n1, el1 = timed_layers(s4, ctx4, budget_s * 0.15)
+        res["value_1_thread"] = n1 / s4.num_layers / el1
+        res["sample_1_thread"] = f"{n1} layer-attentions of the long-history step, one BLAS thread, {el1:.1f} s"
+    del ctx4
+    # Pi0.5-like single-layer attention step
+    s2 = configs.PI05_1L
+    ctx2 = attention_ctx(s2)
+    n2, el2 = timed_layers(s2, ctx2, budget_s * 0.15)
+    res["pi05_like_1L"] = {"steps_per_s": n2 / el2, "sample": f"{n2} single-layer steps, {el2:.1f} s"}
+    # Pi0.5-like 18-layer stack step (the whole chained step, gamma given)
+    s3 = configs.PI05_18L
+    pk, pv = synth.pin_kv(s3)
+    frames = [synth.frame_kv(s3, f) for f in range(s3.num_slots)]
+    caches_k = [np.concatenate([synth.widen(pk[l])] + [synth.widen(f[0][l]) for f in frames])
+                for l in range(s3.num_layers)]
+    caches_v = [np.concatenate([synth.widen(pv[l])] + [synth.widen(f[1][l]) for f in frames])
+                for l in range(s3.num_layers)]
+    pw = [synth.proj_weights(s3, l) for l in range(s3.num_layers)]
+    wq, wo = [synth.widen(w[0]) for w in pw], [synth.widen(w[1]) for w in pw]
+    gam = [np.ones(s3.model_dim)] * s3.num_layers
+    x = synth.widen(synth.flow_x(s3, 0))
+    n3 = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 <= budget_s * 0.25 or n3 == 0:
+        x, _ = ostack.denoise_step(x, gam, s3.eps, wq, wo, caches_k, caches_v, s3.scale, s3.n_q_heads,
+                                   s3.n_kv_heads, s3.head_dim)
+        n3 += 1
+    el3 = time.perf_counter() - t0
+    res["pi05_like_18L_stack_step"] = {"steps_per_s": n3 / el3, "us_per_step": el3 / n3 * 1e6,
+                                       "sample": f"{n3} chained 18-layer steps, {el3:.1f} s"}
     return res
 
 
@@ -710,13 +792,23 @@ def copy_calibration(torch, mb):
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, plus family, model
+    and stepping (a virtualised host may report only a short model name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
+            if not line.strip() and fields:
+                break
     except OSError:
         pass
-    return "unknown"
+    if not fields:
+        return "unknown"
+    return (f"{fields.get('model name', '?')} (family {fields.get('cpu family', '?')}, model "
+            f"{fields.get('model', '?')}, stepping {fields.get('stepping', '?')})")
 
 
 def main():
@@ -733,6 +825,10 @@ def main():
                     help="run only the cold-MALL headline step (for profiler passes)")
     ap.add_argument("--cold-rings", type=int, default=3,
                     help="independent rings served round-robin for the cold-MALL headline (3 x 118 MB > 256 MB)")
+    ap.add_argument("--kernel-launches", type=int, default=30,
+                    help="partial-kernel launches timed one by one for the roofline (at least 20)")
+    ap.add_argument("--no-fp32-partials", action="store_true",
+                    help="skip the headline variant with FP32 split partials")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB five times (traffic-counter calibration)")
     args = ap.parse_args()
@@ -758,6 +854,11 @@ def main():
     lh_op = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings, q_layout=L.PA_Q_OPERAND)
     log(f"long history, cold MALL, Q in operand order: {lh_op['steps_per_s']:.1f} steps/s, partial kernel "
         f"{lh_op['partial_us']:.1f} us")
+    lh_f32 = None
+    if not args.headline_only and not args.no_fp32_partials:
+        lh_f32 = bench_long_history(args, torch, L, configs, synth, n_rings=args.cold_rings, partials_f32=1)
+        log(f"long history, cold MALL, FP32 partials: {lh_f32['steps_per_s']:.1f} steps/s, partial kernel "
+            f"{lh_f32['partial_us']:.1f} us")
     warm = small = async_push = ada_qkv = capsule = None
     if not args.headline_only:
         warm = bench_long_history(args, torch, L, configs, synth, n_rings=1)
@@ -774,8 +875,10 @@ def main():
         async_push = bench_async_push(args, torch, L, configs, synth)
         log(f"async push: {async_push['frames_per_s_sync_push']:.1f} frames/s synchronous, "
             f"{async_push['frames_per_s_overlapped_push']:.1f} overlapped")
-    stack = full = None
+    stack = full = chained = None
     if not args.no_stack:
+        chained = bench_stack(args, torch, L, configs, synth, shape=configs.LONG_18L_FULL)
+        log(f"long history chained 18-layer denoise step: {chained['us_per_step']:.1f} us/step")
         stack = bench_stack(args, torch, L, configs, synth)
         log(f"pi05 18L stack: {stack['us_per_step']:.1f} us/step")
         full = bench_stack(args, torch, L, configs, synth, full_layer=True)
@@ -804,16 +907,27 @@ def main():
         "dtype": "bf16",
         "data": f"synthetic (seeded N(0,1) K/V/Q, resident in HBM; {lh['rings']} rings served round-robin, "
                 "so K/V streams from HBM, not the MALL)",
-        "config": {"workload": "long_history_18L", "layers": s.num_layers, "q_heads": s.n_q_heads,
+        "config": {"workload": "long_history_18L", "step": "layer-batched partitioned attention: all 18 layers' "
+                   "split-KV partials in one launch, then the log-sum-exp combine (every layer's suffix Q/K/V "
+                   "given); a frame push before every 10th step of each ring",
+                   "layers": s.num_layers, "q_heads": s.n_q_heads,
                    "kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "pin_tokens": s.pin_tokens,
                    "window": f"{s.num_slots}x{s.tokens_per_frame}", "suffix": s.n_dyn,
                    "steps_per_frame": s.steps_per_frame, "kv_splits": lh["splits"] or "default",
-                   "rings": lh["rings"], "mall": "cold"},
+                   "rings": lh["rings"], "mall": "cold", "pushes_timed": lh["pushes_timed"]},
+        # frames/s = 1 / (t_push + 10 t_step): the timed steps include their
+        # pushes (one per 10 steps of each ring), so this is steps/s / 10; the
+        # push alone and the step without its share of pushes are timed beside it
         "frames_per_s": lh["steps_per_s"] / s.steps_per_frame,
+        "push_us": round(lh["push_us"], 2),
+        "step_us_excl_push": round(lh["ms_per_step"] * 1e3 - lh["pushes_timed"] / max(args.steps, 1) * lh["push_us"],
+                                   2),
         "roofline": {"bound": "mfma", "achieved": round(lh["partial_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(lh["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": stored_traffic(), "kernel": "partial_mfma<256>",
-                     "kernel_us": round(lh["partial_us"], 3), "timed_launches": lh["timed_launches"],
+                     "kernel_us": round(lh["partial_us"], 3), "kernel_us_sd": round(lh["partial_us_sd"], 3),
+                     "kernel_us_min": round(lh["partial_us_min"], 3), "kernel_us_max": round(lh["partial_us_max"], 3),
+                     "timed_launches": lh["timed_launches"],
                      "flops_per_launch": lh["flops"], "algo_bytes_per_launch": lh["algo_bytes"]},
         "hbm": {"achieved": round(lh["partial_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lh["partial_gbs"] / HBM_PEAK_GBS, 4),
@@ -826,6 +940,15 @@ def main():
                                  "partial_tflops": round(lh_op["partial_tflops"], 2),
                                  "frac": round(lh_op["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
+    if lh_f32 is not None:
+        # the same cold step with the split partials' accumulator kept in FP32
+        # (pattn_args.partials_f32 = 1) instead of bf16
+        line["cold_fp32_partials"] = {"steps_per_s": lh_f32["steps_per_s"], "ms_per_step": lh_f32["ms_per_step"],
+                                      "partial_us": round(lh_f32["partial_us"], 3),
+                                      "partial_tflops": round(lh_f32["partial_tflops"], 2),
+                                      "frac": round(lh_f32["partial_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if chained is not None:
+        line["long_history_18L_chained_step"] = chained
     if warm is not None:
         line["warm_mall"] = {"rings": 1, "steps_per_s": warm["steps_per_s"], "ms_per_step": warm["ms_per_step"],
                              "partial_us": round(warm["partial_us"], 3),

@@ -202,6 +202,9 @@ typedef struct {
     int32_t out_dtype;         /* PA_F32 or PA_BF16 */
     int32_t num_splits;        /* KV splits per layer, 0..127; 0 = library's choice */
     int32_t q_layout;          /* PA_Q_TOKEN_MAJOR or PA_Q_OPERAND (bf16 rings) */
+    int32_t partials_f32;      /* 0: the library's choice (bf16 partial acc on bf16 rings, FP32 on f32
+                                  rings); 1: FP32 partial acc on bf16 rings too (twice the partial bytes;
+                                  pattn_step / pattn_step_timed / pattn_step_noalloc only) */
 } pattn_args;
 
 /* Layouts of q for pattn_step / pattn_step_timed.

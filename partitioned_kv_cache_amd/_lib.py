@@ -64,7 +64,7 @@ class RbState(C.Structure):
 class PattnArgs(C.Structure):
     _fields_ = [("layer_begin", C.c_int32), ("num_layers", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_dyn", C.c_int32), ("scale", C.c_float), ("out_dtype", C.c_int32), ("num_splits", C.c_int32),
-                ("q_layout", C.c_int32)]
+                ("q_layout", C.c_int32), ("partials_f32", C.c_int32)]
 
 
 class PattnDecodeArgs(C.Structure):
@@ -230,8 +230,8 @@ def rb_config(num_layers, num_kv_heads, head_dim, pin_capacity, num_slots, token
 # ------------------------------------------------------------ attention ------
 
 def pattn_args(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype=PA_F32, num_splits=0,
-               q_layout=0) -> PattnArgs:
-    return PattnArgs(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype, num_splits, q_layout)
+               q_layout=0, partials_f32=0) -> PattnArgs:
+    return PattnArgs(layer_begin, num_layers, n_q_heads, n_dyn, scale, out_dtype, num_splits, q_layout, partials_f32)
 
 
 def pattn_operand_q_bytes(ring: Ring, args: PattnArgs) -> int:

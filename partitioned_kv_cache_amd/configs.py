@@ -77,9 +77,10 @@ LONG_18L = Shape("long_history_18L", 4, num_layers=18, n_q_heads=8, n_kv_heads=1
 SHARED_KV = LONG_18L.with_(name="shared_kv_multitask", cfg_id=5, frames=100, n_streams=16,
                            tail_capacity=30)
 
-# The full denoising step (norm + QKV + attention + out-projection) on the
-# long-history cache: the layer dims of the 18-layer stack over the
-# long-history ring. This is what the benchmark times.
+# The full denoising step (norm + QKV + attention + out-projection, chained
+# layer by layer) on the long-history cache: the layer dims of the 18-layer
+# stack over the long-history ring. The benchmark reports its microseconds
+# per step beside the layer-batched attention step.
 LONG_18L_FULL = LONG_18L.with_(name="long_history_18L_full_step", cfg_id=6, model_dim=1024,
                                hidden_dim=1024)
 

@@ -355,7 +355,7 @@ __device__ __forceinline__ void wait_vmem() {
 // WAVES: 8 (two per SIMD, the throughput form) or 4 (one per SIMD, for
 // launches too small to fill the chip: each wave's key loop then runs at the
 // single-wave rate).
-template <int D, bool FUSED = false, bool QPK = false, int WAVES = MFMA_WAVES>
+template <int D, bool FUSED = false, bool QPK = false, int WAVES = MFMA_WAVES, bool F32P = false>
 __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
                                                                           long long q_layer, int hq, int group,
                                                                           int m_rows, KvSource src, int chunk,
@@ -501,18 +501,30 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     }
 
     l_run += __shfl_xor(l_run, 32);
-    if (active) {       // whole 32-row block, fragment order: each store is 512 B contiguous
+    if (active) {       // whole 32-row block, fragment order: each store is contiguous across the wave
         // Non-temporal: the partials are read once, by the combine kernel,
         // which runs on other CUs (measured 1.5% faster than plain stores).
-        uint16_t* op = part.optr<uint16_t>() + part.oblock(split, lg, row0) + lane * 4;
+        if constexpr (F32P) {       // FP32 partial O (16 B per lane and store)
+            float* op = part.optr<float>() + part.oblock(split, lg, row0) + lane * 4;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+            for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const unsigned long long w = (unsigned long long)pack_bf16(acc[b][4 * j], acc[b][4 * j + 1]) |
-                                             ((unsigned long long)pack_bf16(acc[b][4 * j + 2], acc[b][4 * j + 3]) << 32);
-                __builtin_nontemporal_store(w, reinterpret_cast<unsigned long long*>(op + (b * 4 + j) * 256));
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 w = {acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]};
+                    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(op + (b * 4 + j) * 256));
+                }
+        } else {                    // bf16 partial O (8 B per lane and store)
+            uint16_t* op = part.optr<uint16_t>() + part.oblock(split, lg, row0) + lane * 4;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const unsigned long long w =
+                        (unsigned long long)pack_bf16(acc[b][4 * j], acc[b][4 * j + 1]) |
+                        ((unsigned long long)pack_bf16(acc[b][4 * j + 2], acc[b][4 * j + 3]) << 32);
+                    __builtin_nontemporal_store(w, reinterpret_cast<unsigned long long*>(op + (b * 4 + j) * 256));
+                }
+        }
         if (hi == 0 && row < m_rows) part.ml[part.idx(split, lg, row)] = make_float2(m_run, l_run);
     }
 }
@@ -829,7 +841,7 @@ static Partials partials_in(void* ws, const Plan& p, int d) {
 
 // `extra` is the number of extra partial slots after the cached-key splits.
 static pa_status plan_for(const Ring* r, int layer_begin, int num_layers, int hq, int n_rows_tokens, int n_dyn,
-                          int req_splits, int extra, Plan* p) {
+                          int req_splits, int extra, Plan* p, bool f32_partials = false) {
     const rb_config& c = r->cfg;
     PA_CHECK_ARG(num_layers >= 1 && layer_begin >= 0 && layer_begin + num_layers <= c.num_layers, PA_ESHAPE,
                  "layers [%d, %d) outside the ring's %d layers", layer_begin, layer_begin + num_layers, c.num_layers);
@@ -838,7 +850,7 @@ static pa_status plan_for(const Ring* r, int layer_begin, int num_layers, int hq
     PA_CHECK_ARG(n_rows_tokens >= 1, PA_ESHAPE, "need at least one query token");
     PA_CHECK_ARG(req_splits >= 0 && req_splits <= 127, PA_EINVAL, "num_splits %d not in [0, 127]", req_splits);
     p->mfma = c.dtype == PA_BF16;
-    p->o_bytes = p->mfma ? 2 : 4;
+    p->o_bytes = p->mfma && !f32_partials ? 2 : 4;
     if (p->mfma)
         PA_CHECK_ARG(c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256, PA_ESHAPE,
                      "bf16 attention supports head_dim 64, 128 or 256 (got %d)", c.head_dim);
@@ -927,27 +939,40 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
         const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         const uint16_t* qq2 = static_cast<const uint16_t*>(q2);
-#define PA_MFMA(DD, FU, QP, ...)                                                                                 \
-    partial_mfma<DD, FU, QP, ##__VA_ARGS__><<<grid, rpw * 2, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
+#define PA_MFMA_(DD, FU, QP, WV, FP)                                                                          \
+    partial_mfma<DD, FU, QP, WV, FP><<<grid, rpw * 2, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
                                                                    scale_log2, part, p.parts, row_blocks, qq2,       \
                                                                    q2_layer, m1)
+#define PA_MFMA(DD, FU, QP, ...) PA_MFMA_(DD, FU, QP, ##__VA_ARGS__)
+        // FP32 partial O (optional, single-reader steps): the same kernels
+        // with wider partial stores; the combine reads FP32 partials
+        const bool f32p = p.o_bytes == 4;
+        if (f32p && q2) return fail(PA_EINVAL, "FP32 partials are for the single-reader step");
         if (narrow) {
-            if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES / 2);
-            else PA_MFMA(256, false, false, MFMA_WAVES / 2);
+            if (f32p) {
+                if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES / 2, true);
+                else PA_MFMA(256, false, false, MFMA_WAVES / 2, true);
+            } else if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES / 2, false);
+            else PA_MFMA(256, false, false, MFMA_WAVES / 2, false);
+        } else if (f32p) {
+            if (d == 256) { if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES, true); else PA_MFMA(256, false, false, MFMA_WAVES, true); }
+            else if (d == 128) { if (q_packed) PA_MFMA(128, false, true, MFMA_WAVES, true); else PA_MFMA(128, false, false, MFMA_WAVES, true); }
+            else { if (q_packed) PA_MFMA(64, false, true, MFMA_WAVES, true); else PA_MFMA(64, false, false, MFMA_WAVES, true); }
         } else if (q_packed) {
-            if (d == 256) PA_MFMA(256, false, true);
-            else if (d == 128) PA_MFMA(128, false, true);
-            else PA_MFMA(64, false, true);
+            if (d == 256) PA_MFMA(256, false, true, MFMA_WAVES, false);
+            else if (d == 128) PA_MFMA(128, false, true, MFMA_WAVES, false);
+            else PA_MFMA(64, false, true, MFMA_WAVES, false);
         } else if (q2) {
-            if (d == 256) PA_MFMA(256, true, false);
-            else if (d == 128) PA_MFMA(128, true, false);
-            else PA_MFMA(64, true, false);
+            if (d == 256) PA_MFMA(256, true, false, MFMA_WAVES, false);
+            else if (d == 128) PA_MFMA(128, true, false, MFMA_WAVES, false);
+            else PA_MFMA(64, true, false, MFMA_WAVES, false);
         } else {
-            if (d == 256) PA_MFMA(256, false, false);
-            else if (d == 128) PA_MFMA(128, false, false);
-            else PA_MFMA(64, false, false);
+            if (d == 256) PA_MFMA(256, false, false, MFMA_WAVES, false);
+            else if (d == 128) PA_MFMA(128, false, false, MFMA_WAVES, false);
+            else PA_MFMA(64, false, false, MFMA_WAVES, false);
         }
 #undef PA_MFMA
+#undef PA_MFMA_
     } else {
         dim3 grid(p.parts, valu_row_blocks(p.m_rows), p.lg_count);
         const float* qf = static_cast<const float*>(q);
@@ -1030,7 +1055,9 @@ extern "C" size_t pattn_workspace_bytes(const rb_ring* ring, const pattn_args* a
     const Ring* r = reinterpret_cast<const Ring*>(ring);
     if (!r || !a) return 0;
     Plan p;
-    if (plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_dyn, a->n_dyn, a->num_splits, 0, &p) != PA_OK)
+    if (a->partials_f32 != 0 && a->partials_f32 != 1) return 0;
+    if (plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_dyn, a->n_dyn, a->num_splits, 0, &p,
+                 a->partials_f32 == 1) != PA_OK)
         return 0;
     return partial_bytes(p, r->cfg.head_dim);
 }
@@ -1049,8 +1076,10 @@ static pa_status step_impl(const rb_ring* ring, const pattn_args* a, const void*
                  PA_EINVAL, "pattn_step: q_layout must be PA_Q_TOKEN_MAJOR, or PA_Q_OPERAND on a bf16 ring");
     PA_CHECK_ARG(a->scale > 0.f && a->scale < 1e30f, PA_EINVAL, "pattn_step: scale must be positive and finite");
     PA_CHECK_ARG(a->n_dyn >= 1, PA_ESHAPE, "pattn_step: n_dyn must be >= 1");
+    PA_CHECK_ARG(a->partials_f32 == 0 || a->partials_f32 == 1, PA_EINVAL, "pattn_step: partials_f32 must be 0 or 1");
     Plan p;
-    pa_status st = plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_dyn, a->n_dyn, a->num_splits, 0, &p);
+    pa_status st = plan_for(r, a->layer_begin, a->num_layers, a->n_q_heads, a->n_dyn, a->n_dyn, a->num_splits, 0, &p,
+                            a->partials_f32 == 1);
     if (st != PA_OK) return st;
     PA_CHECK_ARG(!(r->cfg.pin_capacity > 0 && r->pinned == 0), PA_ESTATE,
                  "pattn_step: the prefix is not pinned yet (rb_pin_prefix first)");
@@ -1304,6 +1333,7 @@ static pa_status check_fused(const Ring* r, const pattn_args* a, const pattn_dec
     PA_CHECK_ARG(a->out_dtype == PA_F32 || a->out_dtype == PA_BF16, PA_EINVAL, "pattn_fused_step: bad out_dtype");
     PA_CHECK_ARG(a->n_dyn >= 1, PA_ESHAPE, "pattn_fused_step: n_dyn must be >= 1");
     PA_CHECK_ARG(a->q_layout == PA_Q_TOKEN_MAJOR, PA_EINVAL, "pattn_fused_step: queries are token-major");
+    PA_CHECK_ARG(a->partials_f32 == 0, PA_EINVAL, "pattn_fused_step: FP32 partials are for pattn_step");
     return PA_OK;
 }
 

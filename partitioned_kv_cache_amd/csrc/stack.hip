@@ -103,6 +103,7 @@ static pattn_args attn_args(const pa_stack* st, int layer) {
     a.out_dtype = PA_BF16;
     a.num_splits = st->num_splits;
     a.q_layout = PA_Q_TOKEN_MAJOR;       // the packed path passes its operand-order Q internally
+    a.partials_f32 = 0;
     return a;
 }
 

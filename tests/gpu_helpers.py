@@ -125,14 +125,16 @@ class Scenario:
             return np.zeros((0, h, d)), np.zeros((0, h, d))
         return np.concatenate(parts_k), np.concatenate(parts_v)
 
-    def run_step(self, q, k_dyn, v_dyn, out_dtype=None, num_splits=0, layer_begin=0, num_layers=None, q_layout=0):
+    def run_step(self, q, k_dyn, v_dyn, out_dtype=None, num_splits=0, layer_begin=0, num_layers=None, q_layout=0,
+                 partials_f32=0):
         """pattn_step on host arrays; returns the output as float64 [Lb][N][Hq][D].
         With q_layout = PA_Q_OPERAND the token-major q is converted by pattn_pack_q first."""
         L = lib()
         s = self.s
         nl = s.num_layers if num_layers is None else num_layers
         od = L.PA_F32 if out_dtype is None else out_dtype
-        args = L.pattn_args(layer_begin, nl, s.n_q_heads, q.shape[1], s.scale, od, num_splits, q_layout)
+        args = L.pattn_args(layer_begin, nl, s.n_q_heads, q.shape[1], s.scale, od, num_splits, q_layout,
+                            partials_f32)
         ws_bytes = L.pattn_workspace_bytes(self.ring, args)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         out = torch.empty((nl, q.shape[1], s.n_q_heads, s.head_dim),

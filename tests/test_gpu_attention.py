@@ -112,6 +112,30 @@ def test_attention_long_history_18_layers_bench_launch():
     assert worst <= BF16_REL
 
 
+@pytest.mark.parametrize("shape,q_layout", [(configs.LONG_18L, 0), (configs.LONG_18L, 1), (configs.PI05_1L, 0),
+                                            (configs.PI05_1L, 1)])
+def test_fp32_partials(shape, q_layout):
+    """partials_f32 = 1 keeps the split partials' accumulator in FP32 between
+    the per-split sum and the FP32 combine (the default rounds it to bf16).
+    Both meet the bar; the FP32 form is at least as close to the oracle."""
+    s = shape
+    _banner(f"fp32 partials {s.name} q_layout={q_layout}")
+    sc = Scenario(s)
+    for f in range(s.num_slots + 1):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s, s.num_slots, 6)
+    o16 = sc.run_step(q, kd, vd, q_layout=q_layout)
+    o32 = sc.run_step(q, kd, vd, q_layout=q_layout, partials_f32=1)
+    e16 = e32 = 0.0
+    for l in sorted({0, s.num_layers // 2, s.num_layers - 1}):
+        ref = sc.oracle_step(q, kd, vd, l)
+        e16, e32 = max(e16, rel_err(o16[l], ref)), max(e32, rel_err(o32[l], ref))
+    _banner(f"  rel err: bf16 partials {e16:.3e}, fp32 partials {e32:.3e}")
+    assert e16 <= BF16_REL and e32 <= BF16_REL
+    assert e32 <= e16 * 1.05
+    assert not np.array_equal(o16, o32)           # the option really changes the partials
+
+
 def test_attention_bf16_output_dtype():
     s = configs.PI05_1L
     sc = Scenario(s)
