@@ -591,15 +591,21 @@ template <> struct CombineRaw<uint16_t> {
 // A wave takes JW of the four 8-dim slices of a (32-row, 32-dim) block: 4
 // (256 B contiguous per slice and split) when the launch is large, 1 when it
 // would leave most CUs idle, so that the per-wave merge is a quarter as long.
-template <typename TO, int D, typename PO, bool APK = false, int JW = 4>
+// SW > 1 (many splits): the SW waves of a workgroup share one slice, wave w
+// merging splits w, w + SW, ... (each set in one batch, one memory round
+// trip, where one wave alone would need several in sequence); the SW
+// partial merges are then merged through LDS by the first wave.
+template <typename TO, int D, typename PO, bool APK = false, int JW = 4, int SW = 1>
 __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int row_lo, int row_hi, int group, int hq,
                                                int hkv, long long out_layer, TO* out) {
-    constexpr int DB = D / 32, NJ = 4 / JW;
+    constexpr int DB = D / 32, NJ = 4 / JW, UPB = 4 / SW;
     static_assert(JW == 1 || JW == 2 || JW == 4, "slices per wave");
+    static_assert(SW == 1 || SW == 2 || SW == 4, "split waves per slice");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int unit = blockIdx.x * 4 + wave, lg = blockIdx.y;
+    const int sub = wave % SW;                          // this wave's share of the splits
+    const int unit = blockIdx.x * UPB + wave / SW, lg = blockIdx.y;
     const int row0 = (row_lo & ~31) + (unit / (DB * NJ)) * 32, b = (unit / NJ) % DB, j0 = (unit % NJ) * JW;
-    if (row0 >= row_hi) return;
+    if (row0 >= row_hi) return;                         // with SW > 1, the same for every wave of the block
     const int row = row0 + l32;
     const bool ok = row >= row_lo && row < row_hi;
     const int lb = lg / hkv, g = lg % hkv;
@@ -611,13 +617,14 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     for (int j = 0; j < JW; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     using R = CombineRaw<PO>;
     constexpr int BATCH = R::BATCH;
-    for (int s0 = 0; s0 < n_parts; s0 += BATCH) {
+    const int n_mine = (n_parts - sub + SW - 1) / SW;   // splits sub, sub + SW, ...
+    for (int s0 = 0; s0 < n_mine; s0 += BATCH) {
         float2 ml[BATCH];
         typename R::T v[BATCH][JW];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-            const bool has = s0 + i < n_parts;         // uniform: slots past the end load nothing, weigh 0
-            const int s = has ? s0 + i : 0;
+            const bool has = s0 + i < n_mine;          // uniform: slots past the end load nothing, weigh 0
+            const int s = has ? (s0 + i) * SW + sub : 0;
             ml[i] = ok && has ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
             const PO* op = part.optr<PO>() + part.oblock(s, lg, row0) + (b * 4 + j0) * 256 + lane * 4;
 #pragma unroll
@@ -643,6 +650,35 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
             }
         }
         mx = bm;
+    }
+    if constexpr (SW > 1) {
+        // merge the SW waves' (mx, lsum, acc), referenced to the largest mx
+        __shared__ float2 sh_ml[SW][64];
+        __shared__ float4 sh_acc[SW][JW][64];
+        sh_ml[sub][lane] = make_float2(mx, lsum);
+#pragma unroll
+        for (int j = 0; j < JW; ++j) sh_acc[sub][j][lane] = acc[j];
+        __syncthreads();
+        if (sub != 0) return;
+        float m_all = mx;
+#pragma unroll
+        for (int w = 1; w < SW; ++w) m_all = fmaxf(m_all, sh_ml[w][lane].x);
+        if (m_all != -INFINITY) {
+            lsum = 0.f;
+#pragma unroll
+            for (int j = 0; j < JW; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < SW; ++w) {
+                const float2 mlw = sh_ml[w][lane];
+                const float wt = mlw.x == -INFINITY ? 0.f : exp2f(mlw.x - m_all);
+                lsum += wt * mlw.y;
+#pragma unroll
+                for (int j = 0; j < JW; ++j) {
+                    const float4 a = sh_acc[w][j][lane];
+                    acc[j].x += wt * a.x; acc[j].y += wt * a.y; acc[j].z += wt * a.z; acc[j].w += wt * a.w;
+                }
+            }
+        }
     }
     if (!ok) return;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -939,10 +975,9 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
         const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         const uint16_t* qq2 = static_cast<const uint16_t*>(q2);
-#define PA_MFMA_(DD, FU, QP, WV, FP)                                                                          \
-    partial_mfma<DD, FU, QP, WV, FP><<<grid, rpw * 2, 0, stream>>>(qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, \
-                                                                   scale_log2, part, p.parts, row_blocks, qq2,       \
-                                                                   q2_layer, m1)
+#define PA_MFMA_(DD, FU, QP, WV, FP, ...)                                                                     \
+    partial_mfma<DD, FU, QP, WV, FP, ##__VA_ARGS__><<<grid, rpw * 2, 0, stream>>>(                            \
+        qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, scale_log2, part, p.parts, row_blocks, qq2, q2_layer, m1)
 #define PA_MFMA(DD, FU, QP, ...) PA_MFMA_(DD, FU, QP, ##__VA_ARGS__)
         // FP32 partial O (optional, single-reader steps): the same kernels
         // with wider partial stores; the combine reads FP32 partials
@@ -1001,10 +1036,19 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
     // per wave instead (larger launches, the 18-layer decode pass included,
     // measured no gain)
     const bool thin = units * p.lg_count <= 256;
-    const dim3 grid((units * (thin ? 4 : 1) + 3) / 4, p.lg_count);
+    // more splits than one batch of loads holds (16 bf16 or 8 FP32 partials):
+    // four waves share each slice, one batch each
+    const bool sw = n_parts > (p.o_bytes == 2 ? 16 : 8);
+    const dim3 grid(sw ? units * (thin ? 4 : 1) : (units * (thin ? 4 : 1) + 3) / 4, p.lg_count);
 #define PA_COMBINE_JW(TO, DD, PO, APK)                                                                         \
     do {                                                                                                       \
-        if (thin)                                                                                              \
+        if (sw && thin)                                                                                        \
+            combine<TO, DD, PO, APK, 1, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
+                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+        else if (sw)                                                                                           \
+            combine<TO, DD, PO, APK, 4, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
+                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+        else if (thin)                                                                                         \
             combine<TO, DD, PO, APK, 1><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,  \
                                                                   hkv, out_layer, static_cast<TO*>(out));      \
         else                                                                                                   \

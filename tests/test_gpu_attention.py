@@ -136,6 +136,27 @@ def test_fp32_partials(shape, q_layout):
     assert not np.array_equal(o16, o32)           # the option really changes the partials
 
 
+@pytest.mark.parametrize("splits,f32p", [(0, 0), (100, 0), (20, 1), (0, 1)])
+def test_single_layer_long_history_many_splits(splits, f32p):
+    """One layer of the long-history cache: the library picks ~50 splits, so
+    the combine merges more partials than one batch of loads holds and
+    splits each slice's merge over four waves (also with 100 splits, and
+    FP32 partials past 8 splits)."""
+    s = configs.LONG_18L.with_(name="lh_1L", cfg_id=48, num_layers=3)
+    _banner(f"long-history single layer splits={splits} f32 partials={f32p}")
+    sc = Scenario(s)
+    for f in range(s.num_slots + 2):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s.with_(num_layers=1), 3, 2)
+    out = sc.run_step(q, kd, vd, num_splits=splits, layer_begin=1, num_layers=1, partials_f32=f32p)
+    ck, cv = sc.cached_context(1)
+    ref = full_attention(synth.widen(q[0]), np.concatenate([ck, synth.widen(kd[0])]),
+                         np.concatenate([cv, synth.widen(vd[0])]), s.scale)
+    err = rel_err(out[0], ref)
+    _banner(f"  rel {err:.3e}")
+    assert err <= BF16_REL
+
+
 def test_attention_bf16_output_dtype():
     s = configs.PI05_1L
     sc = Scenario(s)
