@@ -844,10 +844,13 @@ static int valu_row_blocks(int m) { return (m + VALU_ROWS - 1) / VALU_ROWS; }
 
 // Choose the split count: as many workgroups as fit at once (one per CU on
 // 256 CUs) without a partial second wave, and no split shorter than
-// min_keys: three 32-key tiles for the matrix-core kernel; half a tile for
-// the vector kernel, whose waves walk their keys one at a time (splits are
-// still whole 32-key chunks: the 88-key fp32 call went from 1 to 3 splits,
-// 24.6 to 12.7 us).
+// min_keys: 48 keys for the matrix-core kernel, which the 32-key rounding of
+// the split length makes two tiles (a single-layer call of the Pi0.5-like
+// stack then runs 26 splits of 2 tiles: 496 -> 458 us per 18-layer step,
+// against 13 splits of 4 tiles, once the combine merged many splits in one
+// round trip); half a tile for the vector kernel, whose waves walk their
+// keys one at a time (splits are still whole 32-key chunks: the 88-key fp32
+// call went from 1 to 3 splits, 24.6 to 12.7 us).
 static int default_splits(int lg_count, int row_blocks, int max_keys, int min_keys) {
     const int base = lg_count * row_blocks;
     int s = 256 * MFMA_OCC / base;
@@ -896,7 +899,7 @@ static pa_status plan_for(const Ring* r, int layer_begin, int num_layers, int hq
     const int row_blocks = p->mfma ? (p->m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG : valu_row_blocks(p->m_rows);
     p->mpad = (p->m_rows + 31) / 32 * 32;
     const int max_keys = (int)(r->seq_len() + n_dyn);
-    const int s_max = req_splits ? req_splits : default_splits(p->lg_count, row_blocks, max_keys, p->mfma ? 96 : KT / 2);
+    const int s_max = req_splits ? req_splits : default_splits(p->lg_count, row_blocks, max_keys, p->mfma ? 48 : KT / 2);
     p->max_parts = s_max + extra;
     p->total = r->cached_tokens() + n_dyn;
     if (p->total > 0) {
