@@ -436,14 +436,35 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     const int kq = wave & 1;
     const int key_in_tile = kq * 16 + dma_key;
     const int kchunk = (dma_pos ^ ((key_in_tile >> 2) & 3)) << 3;   // K plane rotation
+    // this lane's element offsets inside a tile whose keys are consecutive tokens
+    const int lane_k = key_in_tile * stride + (wave >> 1) * 32 + kchunk;
+    const int lane_v = key_in_tile * stride + (wave >> 1) * 32 + (dma_pos << 3);
     auto issue_tile = [&](int t, char* kbuf, char* vbuf) {
         if (DPW * WAVES > NBLK && wave >= NBLK) return;               // fewer blocks than waves
-        const int j = min(k_begin + t * KT + key_in_tile, k_end - 1);  // ragged tail: a valid key, masked later
-        const bool dyn = j >= n_cached;
-        const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap + (j >= skip_at ? skip_len : 0));
-        const int off = tok * stride + (wave >> 1) * 32;
-        const uint16_t* kp = (dyn ? dk : rk) + off + kchunk;
-        const uint16_t* vp = (dyn ? dv : rv) + off + (dma_pos << 3);
+        const int j0 = k_begin + t * KT;                               // the tile's first key (uniform)
+        const uint16_t* kp;
+        const uint16_t* vp;
+        // A tile inside one region (pin, a window run, or the suffix) and
+        // inside the split maps to KT consecutive tokens: one scalar base
+        // address plus this lane's fixed offset (scalar work instead of
+        // per-lane vector work). Otherwise (the ragged tail, a tile across a
+        // region boundary) each lane maps its own key.
+        const bool in_pin = j0 + KT <= pinned;
+        const bool in_win = j0 >= pinned && j0 + KT <= n_cached && (j0 + KT <= skip_at || j0 >= skip_at);
+        const bool in_dyn = j0 >= n_cached;
+        if (j0 + KT <= k_end && (in_pin || in_win || in_dyn)) {
+            const int tok0 = in_dyn ? j0 - n_cached : (in_pin ? j0 : j0 + gap + (j0 >= skip_at ? skip_len : 0));
+            const long long base = (long long)tok0 * stride;
+            kp = (in_dyn ? dk : rk) + base + lane_k;
+            vp = (in_dyn ? dv : rv) + base + lane_v;
+        } else {
+            const int j = min(j0 + key_in_tile, k_end - 1);            // ragged tail: a valid key, masked later
+            const bool dyn = j >= n_cached;
+            const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap + (j >= skip_at ? skip_len : 0));
+            const int off = tok * stride + (wave >> 1) * 32;
+            kp = (dyn ? dk : rk) + off + kchunk;
+            vp = (dyn ? dv : rv) + off + (dma_pos << 3);
+        }
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             const int blk = __builtin_amdgcn_readfirstlane(wave + i * WAVES);
