@@ -190,6 +190,12 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0, pa
     kev = KernelEvents()
     evs = [kev.pair() for _ in range(n_kern)]
     base = args.warmup + args.steps
+    # The pass is enqueued behind a short spin kernel (about 2 ms), so that
+    # the host is far enough ahead that no launch waits for its enqueue: with
+    # the queue empty, an event pair measured a launch plus the gap to the
+    # host's next submission (71-72 us after a 20-step run, against 59-62 us
+    # after a 600-step run on the same box).
+    torch.cuda._sleep(4_000_000)
     for i in range(n_kern):
         one_step(base + i, evs[i])
     torch.cuda.synchronize()
