@@ -626,7 +626,10 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     const int sub = wave % SW;                          // this wave's share of the splits
     const int unit = blockIdx.x * UPB + wave / SW, lg = blockIdx.y;
     const int row0 = (row_lo & ~31) + (unit / (DB * NJ)) * 32, b = (unit / NJ) % DB, j0 = (unit % NJ) * JW;
-    if (row0 >= row_hi) return;                         // with SW > 1, the same for every wave of the block
+    // a slice past the end (the last workgroup of an odd count) merges
+    // nothing; with SW > 1 its waves still meet the others at the barrier
+    const bool live = row0 < row_hi;
+    if (SW == 1 && !live) return;
     const int row = row0 + l32;
     const bool ok = row >= row_lo && row < row_hi;
     const int lb = lg / hkv, g = lg % hkv;
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     for (int j = 0; j < JW; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     using R = CombineRaw<PO>;
     constexpr int BATCH = R::BATCH;
-    const int n_mine = (n_parts - sub + SW - 1) / SW;   // splits sub, sub + SW, ...
+    const int n_mine = live ? (n_parts - sub + SW - 1) / SW : 0;   // splits sub, sub + SW, ...
     for (int s0 = 0; s0 < n_mine; s0 += BATCH) {
         float2 ml[BATCH];
         typename R::T v[BATCH][JW];
@@ -673,29 +676,31 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
         mx = bm;
     }
     if constexpr (SW > 1) {
-        // merge the SW waves' (mx, lsum, acc), referenced to the largest mx
-        __shared__ float2 sh_ml[SW][64];
-        __shared__ float4 sh_acc[SW][JW][64];
-        sh_ml[sub][lane] = make_float2(mx, lsum);
+        // merge the SW waves' (mx, lsum, acc) of this slice (waves w0 ..
+        // w0 + SW - 1 of the block), referenced to the largest mx
+        __shared__ float2 sh_ml[4][64];
+        __shared__ float4 sh_acc[4][JW][64];
+        const int w0 = wave - sub;
+        sh_ml[wave][lane] = make_float2(mx, lsum);
 #pragma unroll
-        for (int j = 0; j < JW; ++j) sh_acc[sub][j][lane] = acc[j];
+        for (int j = 0; j < JW; ++j) sh_acc[wave][j][lane] = acc[j];
         __syncthreads();
-        if (sub != 0) return;
+        if (sub != 0 || !live) return;
         float m_all = mx;
 #pragma unroll
-        for (int w = 1; w < SW; ++w) m_all = fmaxf(m_all, sh_ml[w][lane].x);
+        for (int w = 1; w < SW; ++w) m_all = fmaxf(m_all, sh_ml[w0 + w][lane].x);
         if (m_all != -INFINITY) {
             lsum = 0.f;
 #pragma unroll
             for (int j = 0; j < JW; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int w = 0; w < SW; ++w) {
-                const float2 mlw = sh_ml[w][lane];
+                const float2 mlw = sh_ml[w0 + w][lane];
                 const float wt = mlw.x == -INFINITY ? 0.f : exp2f(mlw.x - m_all);
                 lsum += wt * mlw.y;
 #pragma unroll
                 for (int j = 0; j < JW; ++j) {
-                    const float4 a = sh_acc[w][j][lane];
+                    const float4 a = sh_acc[w0 + w][j][lane];
                     acc[j].x += wt * a.x; acc[j].y += wt * a.y; acc[j].z += wt * a.z; acc[j].w += wt * a.w;
                 }
             }
@@ -1061,16 +1066,24 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
     // measured no gain)
     const bool thin = units * p.lg_count <= 256;
     // more splits than one batch of loads holds (16 bf16 or 8 FP32 partials):
-    // four waves share each slice, one batch each
-    const bool sw = n_parts > (p.o_bytes == 2 ? 16 : 8);
-    const dim3 grid(sw ? units * (thin ? 4 : 1) : (units * (thin ? 4 : 1) + 3) / 4, p.lg_count);
+    // two or four waves share each slice, one batch each
+    const int batch = p.o_bytes == 2 ? 16 : 8;
+    const int sw = n_parts <= batch ? 1 : (n_parts <= 2 * batch ? 2 : 4);
+    const int slices = units * (thin ? 4 : 1);
+    const dim3 grid((slices * sw + 3) / 4, p.lg_count);
 #define PA_COMBINE_JW(TO, DD, PO, APK)                                                                         \
     do {                                                                                                       \
-        if (sw && thin)                                                                                        \
+        if (sw == 4 && thin)                                                                                   \
             combine<TO, DD, PO, APK, 1, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
                                                                      hkv, out_layer, static_cast<TO*>(out));   \
-        else if (sw)                                                                                           \
+        else if (sw == 4)                                                                                      \
             combine<TO, DD, PO, APK, 4, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
+                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+        else if (sw == 2 && thin)                                                                              \
+            combine<TO, DD, PO, APK, 1, 2><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
+                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+        else if (sw == 2)                                                                                      \
+            combine<TO, DD, PO, APK, 4, 2><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
                                                                      hkv, out_layer, static_cast<TO*>(out));   \
         else if (thin)                                                                                         \
             combine<TO, DD, PO, APK, 1><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,  \
