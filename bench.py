@@ -17,6 +17,13 @@ HBM rather than the 256 MB last-level cache; the single-ring (warm) figure
 is reported beside it, as are microseconds per call on the two small
 configurations.
 
+Each workload first runs its own loop untimed for --settle-ms (250 ms by
+default) before its warmup steps: the matrix-core kernels run 15-25% slower
+for their first few hundred launches after the GPU has idled, so without it
+a short timed region measures that transient rather than the steady state of
+a running loop. The headline reports the mean of its first 100 launches
+(config.settle) beside the settled figures.
+
 Reported beside it in the same JSON line:
 * the chained denoising step on the long-history cache (norm -> packed QKV ->
   attention -> out-projection with residual, layer by layer, 18 layers,
@@ -53,6 +60,37 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def settle(torch, ms, step, chunk):
+    """Run the workload's own loop, step(i) for i = 0, 1, ..., untimed, for
+    `ms` milliseconds of wall time; return the number of calls made.
+
+    On this GPU the matrix-core kernels run 15-25% slower for their first few
+    hundred launches after the device has been idle for as little as 0.2 s,
+    while the shader clock and HBM copy bandwidth hold steady; the slowdown
+    fades over about 40 ms of continuous work whatever the K/V footprint (the
+    same with 118 MB and 708 MB of rings). A serving loop runs continuously,
+    so the settle phase runs before the warmup steps and the timed steps
+    measure the steady state. The host keeps one chunk of calls queued
+    behind the running one, so the GPU does not idle in between."""
+    if ms <= 0:
+        return 0
+    i, pending = 0, None
+    t_end = time.perf_counter() + ms / 1e3
+    while True:
+        for _ in range(chunk):
+            step(i)
+            i += 1
+        ev = torch.cuda.Event()
+        ev.record()
+        if pending is not None:
+            pending.synchronize()
+        pending = ev
+        if time.perf_counter() >= t_end:
+            break
+    torch.cuda.synchronize()
+    return i
 
 
 class KernelEvents:
@@ -173,13 +211,29 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0, pa
         else:
             L.pattn_step_timed(rings[r], args_, q, kd, vd, out, ws, wsb, stream, ev[0], ev[1])
 
+    # The first launches of the loop, each timed (enqueued behind a spin
+    # kernel, as the roofline pass below is): the unsettled figure. One
+    # untimed step goes first, so that the runtime's one-time loading of the
+    # kernels' code objects on their first launch is not in it.
+    n_first = 100 if args.settle_ms > 0 else 0
+    kev = KernelEvents()
+    evs = [kev.pair() for _ in range(n_first)]
+    if n_first:
+        one_step(0)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(4_000_000)
+    for i in range(n_first):
+        one_step(1 + i, evs[i])
+    n_first += 1 if n_first else 0
+    n_settle = n_first + settle(torch, args.settle_ms, lambda i: one_step(n_first + i), 50)
     for i in range(args.warmup):
-        one_step(i)
+        one_step(n_settle + i)
     torch.cuda.synchronize()
+    first_ms = [kev.elapsed_ms(a, b) for a, b in evs]
     pushes[0] = 0
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(args.warmup + i)
+        one_step(n_settle + args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     pushes_timed = pushes[0]
@@ -187,9 +241,8 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0, pa
     # further stretch of the same loop (an event pair around every launch
     # adds dispatch latency, so this pass is kept out of the throughput).
     n_kern = max(args.kernel_launches, 20)
-    kev = KernelEvents()
     evs = [kev.pair() for _ in range(n_kern)]
-    base = args.warmup + args.steps
+    base = n_settle + args.warmup + args.steps
     # The pass is enqueued behind a short spin kernel (about 2 ms), so that
     # the host is far enough ahead that no launch waits for its enqueue: with
     # the queue empty, an event pair measured a launch plus the gap to the
@@ -237,6 +290,8 @@ def bench_long_history(args, torch, L, configs, synth, n_rings=1, q_layout=0, pa
         "rings": n_rings,
         "q_layout": "operand" if q_layout else "token_major",
         "partials": "fp32" if partials_f32 else "bf16",
+        "settle_steps": n_settle,
+        "first_launches_us": sum(first_ms) / len(first_ms) * 1e3 if first_ms else None,
     }
     for ring in rings:
         ring.close()
@@ -533,6 +588,7 @@ def bench_stack(args, torch, L, configs, synth, full_layer=False, shape=None):
         x.copy_(xs[i % n_frames])
         g.replay()
 
+    settle(torch, args.settle_ms, frame, 2)
     for i in range(2):
         frame(i)
     torch.cuda.synchronize()
@@ -635,6 +691,8 @@ def bench_shared_kv(args, torch, L, configs, synth, budgets=(1, 5, 10), n_frames
             else:
                 L.pattn_step(ring, a_args, *steps_in[k], a_out, a_ws, a_wsb)
 
+    tail_len = dev(np.array([(2 * j) % cap for j in range(G)], dtype=np.int32))
+    settle(torch, args.settle_ms, lambda i: frame_fused(i, 1), 10)
     sweep, sweep_fused = {}, {}
     for k_dec in budgets:
         tail_len = dev(np.array([(2 * j) % cap for j in range(G)], dtype=np.int32))
@@ -831,6 +889,8 @@ def main():
                     help="run only the cold-MALL headline step (for profiler passes)")
     ap.add_argument("--cold-rings", type=int, default=3,
                     help="independent rings served round-robin for the cold-MALL headline (3 x 118 MB > 256 MB)")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="untimed run of each workload's own loop before its warmup steps (0 = none)")
     ap.add_argument("--kernel-launches", type=int, default=30,
                     help="partial-kernel launches timed one by one for the roofline (at least 20)")
     ap.add_argument("--no-fp32-partials", action="store_true",
@@ -920,7 +980,12 @@ def main():
                    "kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "pin_tokens": s.pin_tokens,
                    "window": f"{s.num_slots}x{s.tokens_per_frame}", "suffix": s.n_dyn,
                    "steps_per_frame": s.steps_per_frame, "kv_splits": lh["splits"] or "default",
-                   "rings": lh["rings"], "mall": "cold", "pushes_timed": lh["pushes_timed"]},
+                   "rings": lh["rings"], "mall": "cold", "pushes_timed": lh["pushes_timed"],
+                   "settle": {"ms": args.settle_ms, "steps": lh["settle_steps"],
+                              "what": "the same step loop run untimed before the warmup steps (matrix-core kernels "
+                                      "run slower for their first few hundred launches after the GPU idles)",
+                              "partial_us_first_100_launches": None if lh["first_launches_us"] is None
+                              else round(lh["first_launches_us"], 3)}},
         # frames/s = 1 / (t_push + 10 t_step): the timed steps include their
         # pushes (one per 10 steps of each ring), so this is steps/s / 10; the
         # push alone and the step without its share of pushes are timed beside it
