@@ -616,12 +616,16 @@ template <> struct CombineRaw<uint16_t> {
 // merging splits w, w + SW, ... (each set in one batch, one memory round
 // trip, where one wave alone would need several in sequence); the SW
 // partial merges are then merged through LDS by the first wave.
-template <typename TO, int D, typename PO, bool APK = false, int JW = 4, int SW = 1>
+// NB: splits per batch (at most the raw type's BATCH; the launch picks the
+// smallest that holds a wave's splits, so no registers sit idle).
+template <typename TO, int D, typename PO, bool APK = false, int JW = 4, int SW = 1,
+          int NB = CombineRaw<PO>::BATCH>
 __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int row_lo, int row_hi, int group, int hq,
                                                int hkv, long long out_layer, TO* out) {
     constexpr int DB = D / 32, NJ = 4 / JW, UPB = 4 / SW;
     static_assert(JW == 1 || JW == 2 || JW == 4, "slices per wave");
     static_assert(SW == 1 || SW == 2 || SW == 4, "split waves per slice");
+    static_assert(NB >= 1 && NB <= CombineRaw<PO>::BATCH, "splits per batch");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
     const int sub = wave % SW;                          // this wave's share of the splits
     const int unit = blockIdx.x * UPB + wave / SW, lg = blockIdx.y;
@@ -633,6 +637,11 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
     const int row = row0 + l32;
     const bool ok = row >= row_lo && row < row_hi;
     const int lb = lg / hkv, g = lg % hkv;
+    // Split s of this lane's row and slice: (m, l) at ml0 + s * ml_stride,
+    // the O words at o0 + s * o_stride (rows of padded blocks are in bounds).
+    const long long ml_stride = (long long)part.lg_count * part.mpad, o_stride = ml_stride * part.d;
+    const float2* ml0 = part.ml + part.idx(0, lg, row);
+    const PO* o0 = part.optr<PO>() + part.oblock(0, lg, row0) + (b * 4 + j0) * 256 + lane * 4;
     // Online merge over batches of splits: (mx, lsum, acc) is the merge of
     // the splits seen so far, referenced to mx.
     float mx = -INFINITY, lsum = 0.f;
@@ -640,31 +649,45 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
 #pragma unroll
     for (int j = 0; j < JW; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     using R = CombineRaw<PO>;
-    constexpr int BATCH = R::BATCH;
     const int n_mine = live ? (n_parts - sub + SW - 1) / SW : 0;   // splits sub, sub + SW, ...
-    for (int s0 = 0; s0 < n_mine; s0 += BATCH) {
-        float2 ml[BATCH];
-        typename R::T v[BATCH][JW];
+    for (int s0 = 0; s0 < n_mine; s0 += NB) {
+        // Every load of the batch is issued, in order: the (m, l) of all
+        // slots, then their O words, so the merge of slot i waits only for
+        // its own words. A slot past the end re-reads the batch's first
+        // split (in bounds, cached) and weighs 0.
+        float2 ml[NB];
+        typename R::T v[NB][JW];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const bool has = s0 + i < n_mine;          // uniform: slots past the end load nothing, weigh 0
-            const int s = has ? (s0 + i) * SW + sub : 0;
-            ml[i] = ok && has ? part.ml[part.idx(s, lg, row)] : make_float2(-INFINITY, 0.f);
-            const PO* op = part.optr<PO>() + part.oblock(s, lg, row0) + (b * 4 + j0) * 256 + lane * 4;
-#pragma unroll
-            for (int j = 0; j < JW; ++j) v[i][j] = has ? R::load(op + j * 256) : typename R::T{};
+        for (int i = 0; i < NB; ++i) {
+            const int s = (s0 + i < n_mine ? s0 + i : s0) * SW + sub;
+            ml[i] = ml0[s * ml_stride];
         }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int s = (s0 + i < n_mine ? s0 + i : s0) * SW + sub;
+#pragma unroll
+            for (int j = 0; j < JW; ++j) v[i][j] = R::load(o0 + s * o_stride + j * 256);
+        }
+        // all of the batch's loads leave before any merging starts (the
+        // scheduler would otherwise hold some back to save registers)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (!ok || s0 + i >= n_mine) ml[i] = make_float2(-INFINITY, 0.f);
         float bm = mx;
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) bm = fmaxf(bm, ml[i].x);
-        if (bm == -INFINITY) continue;                  // nothing non-empty yet
-        const float sc = exp2f(mx - bm);                // 0 while mx is -inf
+        for (int i = 0; i < NB; ++i) bm = fmaxf(bm, ml[i].x);
+        // Weights 2^(m - bm) <= 1 on the hardware exp2 (results below 2^-126
+        // flush to zero, far below what the merge can carry). With nothing
+        // non-empty yet (bm = -inf) every weight and the rescale are 0.
+        const float bref = bm == -INFINITY ? 0.f : bm;
+        const float sc = __builtin_amdgcn_exp2f(mx - bref);   // 0 while mx is -inf
         lsum *= sc;
 #pragma unroll
         for (int j = 0; j < JW; ++j) { acc[j].x *= sc; acc[j].y *= sc; acc[j].z *= sc; acc[j].w *= sc; }
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const float w = ml[i].x == -INFINITY ? 0.f : exp2f(ml[i].x - bm);   // an empty partial weighs 0
+        for (int i = 0; i < NB; ++i) {
+            const float w = ml[i].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[i].x - bref);   // empty: 0
             lsum += w * ml[i].y;
 #pragma unroll
             for (int j = 0; j < JW; ++j) {
@@ -696,7 +719,7 @@ __global__ __launch_bounds__(256) void combine(Partials part, int n_parts, int r
 #pragma unroll
             for (int w = 0; w < SW; ++w) {
                 const float2 mlw = sh_ml[w0 + w][lane];
-                const float wt = mlw.x == -INFINITY ? 0.f : exp2f(mlw.x - m_all);
+                const float wt = mlw.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlw.x - m_all);
                 lsum += wt * mlw.y;
 #pragma unroll
                 for (int j = 0; j < JW; ++j) {
@@ -1069,28 +1092,35 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
     // two or four waves share each slice, one batch each
     const int batch = p.o_bytes == 2 ? 16 : 8;
     const int sw = n_parts <= batch ? 1 : (n_parts <= 2 * batch ? 2 : 4);
+    // a wave's splits fit a batch of 8 (fewer registers, more waves resident)?
+    const bool nb8 = (n_parts + sw - 1) / sw <= 8;
     const int slices = units * (thin ? 4 : 1);
     const dim3 grid((slices * sw + 3) / 4, p.lg_count);
-#define PA_COMBINE_JW(TO, DD, PO, APK)                                                                         \
+#define PA_COMBINE_NB(TO, DD, PO, APK, NB)                                                                     \
     do {                                                                                                       \
         if (sw == 4 && thin)                                                                                   \
-            combine<TO, DD, PO, APK, 1, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
-                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+            combine<TO, DD, PO, APK, 1, 4, NB><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, \
+                                                                         hq, hkv, out_layer, static_cast<TO*>(out)); \
         else if (sw == 4)                                                                                      \
-            combine<TO, DD, PO, APK, 4, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
-                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+            combine<TO, DD, PO, APK, 4, 4, NB><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, \
+                                                                         hq, hkv, out_layer, static_cast<TO*>(out)); \
         else if (sw == 2 && thin)                                                                              \
-            combine<TO, DD, PO, APK, 1, 2><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
-                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+            combine<TO, DD, PO, APK, 1, 2, NB><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, \
+                                                                         hq, hkv, out_layer, static_cast<TO*>(out)); \
         else if (sw == 2)                                                                                      \
-            combine<TO, DD, PO, APK, 4, 2><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq, \
-                                                                     hkv, out_layer, static_cast<TO*>(out));   \
+            combine<TO, DD, PO, APK, 4, 2, NB><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, \
+                                                                         hq, hkv, out_layer, static_cast<TO*>(out)); \
         else if (thin)                                                                                         \
-            combine<TO, DD, PO, APK, 1><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,  \
-                                                                  hkv, out_layer, static_cast<TO*>(out));      \
+            combine<TO, DD, PO, APK, 1, 1, NB><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, \
+                                                                         hq, hkv, out_layer, static_cast<TO*>(out)); \
         else                                                                                                   \
-            combine<TO, DD, PO, APK, 4><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, hq,  \
-                                                                  hkv, out_layer, static_cast<TO*>(out));      \
+            combine<TO, DD, PO, APK, 4, 1, NB><<<grid, 256, 0, stream>>>(part, n_parts, row_lo, row_hi, p.group, \
+                                                                         hq, hkv, out_layer, static_cast<TO*>(out)); \
+    } while (0)
+#define PA_COMBINE_JW(TO, DD, PO, APK)                                                                         \
+    do {                                                                                                       \
+        if (nb8 || CombineRaw<PO>::BATCH == 8) PA_COMBINE_NB(TO, DD, PO, APK, 8);                              \
+        else PA_COMBINE_NB(TO, DD, PO, APK, CombineRaw<PO>::BATCH);                                            \
     } while (0)
 #define PA_COMBINE(TO, DD)                                                                                  \
     do {                                                                                                    \
@@ -1124,6 +1154,7 @@ static pa_status launch_combine(const Ring* r, const Plan& p, int n_parts, int h
 #undef PA_COMBINE
 #undef PA_COMBINE_APK
 #undef PA_COMBINE_JW
+#undef PA_COMBINE_NB
     PA_LAUNCHED();
     return PA_OK;
 }
