@@ -181,23 +181,27 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_splitk_part(const uin
 }
 
 // h <- bf16(h + sum_c part[c]) in chunk order, x <- bf16(x - dt h) when x is
-// set, with the residual epilogue's arithmetic. One thread per element.
+// set, with the residual epilogue's arithmetic. One thread per element. KC:
+// chunk slots (kc <= KC). Every load is issued before the first add, with no
+// branch around it (a slot past kc re-reads chunk 0 and is not added), so
+// the partials cost one memory round trip.
+template <int KC>
 __global__ __launch_bounds__(256) void residual_reduce(const float* __restrict__ part, int kc, int rows, int N,
                                                        GemmOut out) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)rows * N;
-    bool bad = false;
-    if (i < total) {
-        // every load issued before the first add
-        constexpr int MAXC = 8192 / SPLITK_CHUNK;
-        float p[MAXC];
+    const bool in = i < total;
+    const long long ii = in ? i : 0;
+    float p[KC];
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c) p[c] = c < kc ? part[c * total + i] : 0.f;
-        const float h0 = bf2f(out.h[i]);
-        const float x0 = out.x ? bf2f(out.x[i]) : 0.f;
+    for (int c = 0; c < KC; ++c) p[c] = part[(c < kc ? c : 0) * total + ii];
+    const float h0 = bf2f(out.h[ii]);
+    const float x0 = out.x ? bf2f(out.x[ii]) : 0.f;
+    bool bad = false;
+    if (in) {
         float v = 0.f;
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c)
+        for (int c = 0; c < KC; ++c)
             if (c < kc) v += p[c];
         const float hn = bf2f(f2bf(h0 + v));
         out.h[i] = f2bf(hn);
@@ -219,6 +223,12 @@ __global__ __launch_bounds__(256) void residual_reduce(const float* __restrict__
 // FP32, each thread's four in order, then the wave sum, then the waves in
 // order. With a packed y, workgroups past `rows` write the padding rows of
 // its 64 row slots as zeros. Reports a non-finite h, x or y element.
+// KC: chunk slots (kc <= KC). Every operand (the partials, h, x and gamma)
+// is loaded up front with no branch around the loads (a slot past kc
+// re-reads chunk 0 and is not added; a thread past N / 4 reads the row's
+// first elements and stores nothing), so the row costs one memory round
+// trip before its sum of squares.
+template <int KC>
 __global__ __launch_bounds__(512) void residual_norm_rows(const float* __restrict__ part, int kc,
                                                           const uint16_t* h_in, uint16_t* h_out, int rows, int N,
                                                           uint16_t* __restrict__ x, float dt, NormNext nn,
@@ -232,14 +242,14 @@ __global__ __launch_bounds__(512) void residual_norm_rows(const float* __restric
         if (own) *reinterpret_cast<uint2*>(y + apack_index(m, k0)) = make_uint2(0, 0);
         return;
     }
-    const long long off = (long long)m * N + k0, total = (long long)rows * N;
-    constexpr int MAXC = 8192 / SPLITK_CHUNK;
-    float4 p[MAXC];
+    const int kl = own ? k0 : 0;         // this thread's load column (in the row)
+    const long long off = (long long)m * N + k0, loff = (long long)m * N + kl, total = (long long)rows * N;
+    float4 p[KC > 0 ? KC : 1];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c)
-        p[c] = own && c < kc ? *reinterpret_cast<const float4*>(part + c * total + off) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint2 hr = own ? *reinterpret_cast<const uint2*>(h_in + off) : make_uint2(0, 0);
-    const uint2 xr = own && x ? *reinterpret_cast<const uint2*>(x + off) : make_uint2(0, 0);
+    for (int c = 0; c < KC; ++c) p[c] = *reinterpret_cast<const float4*>(part + (c < kc ? c : 0) * total + loff);
+    const uint2 hr = *reinterpret_cast<const uint2*>(h_in + loff);
+    const uint2 xr = x ? *reinterpret_cast<const uint2*>(x + loff) : make_uint2(0, 0);
+    const float4 g = nn.gamma ? *reinterpret_cast<const float4*>(nn.gamma + kl) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float h0[4] = {__uint_as_float(hr.x << 16), __uint_as_float(hr.x & 0xffff0000u),
                          __uint_as_float(hr.y << 16), __uint_as_float(hr.y & 0xffff0000u)};
     const float x0[4] = {__uint_as_float(xr.x << 16), __uint_as_float(xr.x & 0xffff0000u),
@@ -250,9 +260,9 @@ __global__ __launch_bounds__(512) void residual_norm_rows(const float* __restric
     for (int e = 0; e < 4; ++e) {
         float v = 0.f;
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c)
+        for (int c = 0; c < KC; ++c)
             if (c < kc) v += (e == 0 ? p[c].x : e == 1 ? p[c].y : e == 2 ? p[c].z : p[c].w);
-        hn[e] = bf2f(f2bf(h0[e] + v));
+        hn[e] = own ? bf2f(f2bf(h0[e] + v)) : 0.f;
         bad |= !finite_f(hn[e]);
     }
     if (own) *reinterpret_cast<uint2*>(h_out + off) = make_uint2(pack2_bf16(hn[0], hn[1]), pack2_bf16(hn[2], hn[3]));
@@ -276,7 +286,6 @@ __global__ __launch_bounds__(512) void residual_norm_rows(const float* __restric
         for (int w = 0; w < nw; ++w) tot += wsums[w];
         const float rinv = 1.f / sqrtf(tot / (float)N + nn.eps);
         if (own) {
-            const float4 g = *reinterpret_cast<const float4*>(nn.gamma + k0);
             const uint32_t y01 = pack2_bf16(hn[0] * rinv * g.x, hn[1] * rinv * g.y);
             const uint32_t y23 = pack2_bf16(hn[2] * rinv * g.z, hn[3] * rinv * g.w);
             bad |= nonfinite_seen(nonfinite_bits(y01) | nonfinite_bits(y23)) != 0;
@@ -291,9 +300,19 @@ static void launch_norm_rows(const float* part, int kc, const void* h_in, void* 
                              float dt, const NormNext& nn, uint32_t* nonfinite, hipStream_t s) {
     const int threads = ((N / 4 + 63) / 64) * 64;
     const int grid = nn.gamma && nn.packed ? 64 : rows;
-    residual_norm_rows<<<grid, threads, 0, s>>>(part, kc, static_cast<const uint16_t*>(h_in),
-                                                static_cast<uint16_t*>(h_out), rows, N, static_cast<uint16_t*>(x),
-                                                dt, nn, nonfinite);
+#define PA_NORM_ROWS(KC)                                                                                     \
+    residual_norm_rows<KC><<<grid, threads, 0, s>>>(part, kc, static_cast<const uint16_t*>(h_in),              \
+                                                    static_cast<uint16_t*>(h_out), rows, N,                    \
+                                                    static_cast<uint16_t*>(x), dt, nn, nonfinite)
+    if (kc == 0)
+        PA_NORM_ROWS(0);
+    else if (kc <= 4)
+        PA_NORM_ROWS(4);
+    else if (kc <= 8)
+        PA_NORM_ROWS(8);
+    else
+        PA_NORM_ROWS(16);
+#undef PA_NORM_ROWS
 }
 
 pa_status norm_rows(const void* h_in, void* h_out, int rows, int N, const NormNext& nn, uint32_t* nonfinite,
@@ -331,7 +350,13 @@ pa_status residual_splitk(const void* a, const void* w, bool packed, void* h, in
     o.dt = dt;
     o.nonfinite = nonfinite;
     const long long total = (long long)rows * N;
-    residual_reduce<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, kc, rows, N, o);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (kc <= 4)
+        residual_reduce<4><<<blocks, 256, 0, s>>>(part, kc, rows, N, o);
+    else if (kc <= 8)
+        residual_reduce<8><<<blocks, 256, 0, s>>>(part, kc, rows, N, o);
+    else
+        residual_reduce<16><<<blocks, 256, 0, s>>>(part, kc, rows, N, o);
     PA_LAUNCHED();
     return PA_OK;
 }
