@@ -232,15 +232,33 @@ __device__ __forceinline__ void norm_fragments(const uint16_t* __restrict__ a, c
     const bool r0 = base + l32 < rows, r1 = !HALVES && 32 + l32 < rows;
     constexpr int RPW = (HALVES ? 32 : 64) / GEMM_WAVES;        // rows per wave
     constexpr int LPR = (K + 511) / 512;        // 16-byte loads per lane and row
+    // Every load leaves before the first is used. Up to K = 1024 (KS <= 8) a
+    // row past `rows` or a chunk past K re-reads row 0's first chunk (in
+    // bounds) and is zeroed after the load, so that no branch sits around a
+    // load; wider rows keep the guarded loads (their registers are full).
     uint4 raw[RPW][LPR];
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
         const int r = base + wave + rr * GEMM_WAVES;
 #pragma unroll
-        for (int c = 0; c < LPR; ++c)
-            raw[rr][c] = (r < rows && c * 512 + lane * 8 < K)
-                             ? *reinterpret_cast<const uint4*>(a + (long long)r * K + c * 512 + lane * 8)
-                             : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < LPR; ++c) {
+            const bool in = r < rows && c * 512 + lane * 8 < K;
+            if constexpr (KS <= 8)
+                raw[rr][c] = *reinterpret_cast<const uint4*>(a + (in ? (long long)r * K + c * 512 + lane * 8 : 0));
+            else
+                raw[rr][c] = in ? *reinterpret_cast<const uint4*>(a + (long long)r * K + c * 512 + lane * 8)
+                                : make_uint4(0, 0, 0, 0);
+        }
+    }
+    if constexpr (KS <= 8) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int r = base + wave + rr * GEMM_WAVES;
+#pragma unroll
+            for (int c = 0; c < LPR; ++c)
+                if (!(r < rows && c * 512 + lane * 8 < K)) raw[rr][c] = make_uint4(0, 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
@@ -260,21 +278,53 @@ __device__ __forceinline__ void norm_fragments(const uint16_t* __restrict__ a, c
     }
     __syncthreads();
     const float ri0 = r0 ? rinv_s[base + l32] : 0.f, ri1 = r1 ? rinv_s[32 + l32] : 0.f;
+    if constexpr (KS <= 8) {
+        // Every fragment and gamma load leaves before the first is used (one
+        // memory round trip, not one per k-step); a row past `rows` reads row
+        // `base` (in bounds) and is scaled by 0. Without HALVES the second
+        // rows' loads exist only when a second 32-row block does.
+        const uint16_t* p0 = a + (long long)(r0 ? base + l32 : base) * K + k0;
+        const uint16_t* p1 = a + (long long)(r1 ? 32 + l32 : 0) * K + k0;
+        uint4 x0[KS], x1[KS];
+        float4 g[KS][2];
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-        const int k = k0 + 16 * i;
-        const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
-        const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
-        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-        if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)(base + l32) * K + k);
-        if (r1) x1 = *reinterpret_cast<const uint4*>(a + (long long)(32 + l32) * K + k);
-        const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
-        const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
+        for (int i = 0; i < KS; ++i) {
+            x0[i] = *reinterpret_cast<const uint4*>(p0 + 16 * i);
+            if (!HALVES) x1[i] = *reinterpret_cast<const uint4*>(p1 + 16 * i);
+            g[i][0] = *reinterpret_cast<const float4*>(gamma + k0 + 16 * i);
+            g[i][1] = *reinterpret_cast<const float4*>(gamma + k0 + 16 * i + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            a0[i][u] = (__bf16)(bf2f(e0[u]) * ri0 * gg[u]);
-            a1[i][u] = (__bf16)(bf2f(e1[u]) * ri1 * gg[u]);
+        for (int i = 0; i < KS; ++i) {
+            const float gg[8] = {g[i][0].x, g[i][0].y, g[i][0].z, g[i][0].w,
+                                 g[i][1].x, g[i][1].y, g[i][1].z, g[i][1].w};
+            const uint4 xa = x0[i], xb = HALVES ? make_uint4(0, 0, 0, 0) : x1[i];
+            const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&xa);
+            const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&xb);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a0[i][u] = (__bf16)(bf2f(e0[u]) * ri0 * gg[u]);
+                a1[i][u] = (__bf16)(bf2f(e1[u]) * ri1 * gg[u]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            const int k = k0 + 16 * i;
+            const float4 g0 = *reinterpret_cast<const float4*>(gamma + k);
+            const float4 g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
+            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+            if (r0) x0 = *reinterpret_cast<const uint4*>(a + (long long)(base + l32) * K + k);
+            if (r1) x1 = *reinterpret_cast<const uint4*>(a + (long long)(32 + l32) * K + k);
+            const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
+            const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a0[i][u] = (__bf16)(bf2f(e0[u]) * ri0 * gg[u]);
+                a1[i][u] = (__bf16)(bf2f(e1[u]) * ri1 * gg[u]);
+            }
         }
     }
 }

@@ -72,6 +72,10 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 1) void gemm_packed(const uint16_t
         w1[i] = *reinterpret_cast<const bf16x8*>(wp1 + wb + i * 512);
         if (MODE == PK_GATEUP) w2[i] = *reinterpret_cast<const bf16x8*>(wp2 + wb + i * 512);
     }
+    // every fragment load leaves before the first product (the scheduler
+    // would otherwise hold later loads behind waits for earlier ones: one
+    // memory round trip per few steps instead of one in all)
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 c0 = f32x16{}, u0 = f32x16{};
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
