@@ -115,6 +115,9 @@ __device__ __forceinline__ void valu_row(const float* qrow, int k_begin, int k_e
             float4 kv[EG / 4];
 #pragma unroll
             for (int i = 0; i < EG / 4; ++i) kv[i] = ld4f<T>(kp + g0 + 4 * i);
+            // the group's loads all leave before the first is used (the
+            // scheduler would otherwise reuse one register: one load in flight)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < EG / 4; ++i) {
                 const float4 qq = *reinterpret_cast<const float4*>(qrow + g0 + 4 * i);
@@ -134,13 +137,20 @@ __device__ __forceinline__ void valu_row(const float* qrow, int k_begin, int k_e
         for (int j0 = 0; j0 < nvalid; j0 += 8) {
             float4 v[8];
             float pj[8];
+            // lanes past D / 4 re-read the row's first four elements (no
+            // branch around the loads) and are zeroed below
+            const int dl = 4 * lane < D ? 4 * lane : 0;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int jj = j0 + u;                      // < 64; p is 0 past nvalid
                 pj[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), jj));
                 const T* vp = row_of(base + min(jj, nvalid - 1), true);
-                v[u] = 4 * lane < D ? ld4f<T>(vp + 4 * lane) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[u] = ld4f<T>(vp + dl);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (4 * lane >= D)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 o.x = fmaf(pj[u], v[u].x, o.x); o.y = fmaf(pj[u], v[u].y, o.y);
