@@ -358,6 +358,9 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
     }
     const int n0 = nb * 32;
     const int k0 = wave * KS * 16 + 8 * hi;
+    // the out-projection's residual rows, loaded with the operands
+    ResidualRows rres{};
+    if constexpr (MODE == GEMM_OPROJ) rres = residual_rows(n0, rows, N, out);
 
     bf16x8 wf[KS];
     const uint16_t* wp = w + (long long)(n0 + l32) * K + k0;
@@ -367,11 +370,20 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
     const bool r0 = 32 * half + l32 < rows, r1 = !HALVES && 32 + l32 < rows;
     bf16x8 a0[KS], a1[KS];
     if (!NORM) {
+        // rows past `rows` re-read row 0 (in bounds) and are zeroed after the
+        // loads, which all leave before the first product
+        const uint16_t* p0 = a + (long long)(r0 ? 32 * half + l32 : 0) * K + k0;
+        const uint16_t* p1 = a + (long long)(r1 ? 32 + l32 : 0) * K + k0;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-            a0[i] = r0 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 * half + l32) * K + k0 + 16 * i)
-                       : bf16x8{};
-            a1[i] = r1 ? *reinterpret_cast<const bf16x8*>(a + (long long)(32 + l32) * K + k0 + 16 * i) : bf16x8{};
+            a0[i] = *reinterpret_cast<const bf16x8*>(p0 + 16 * i);
+            if (!HALVES) a1[i] = *reinterpret_cast<const bf16x8*>(p1 + 16 * i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            if (!r0) a0[i] = bf16x8{};
+            if (HALVES || !r1) a1[i] = bf16x8{};
         }
     } else {
         norm_fragments<KS, HALVES>(a, gamma, eps, rows, rinv_s, a0, a1, half);
@@ -414,7 +426,7 @@ __global__ __launch_bounds__(GEMM_WAVES * 64, 2) void gemm_skinny(const uint16_t
                 out.v[(long long)m * out.nk + (n - out.nq - out.nk)] = f2bf(v);
         }
     } else {
-        residual_epilogue(red, n0, rows, N, out);
+        residual_epilogue(red, rres, out);
     }
 }
 

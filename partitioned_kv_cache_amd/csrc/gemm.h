@@ -68,37 +68,55 @@ struct GemmOut {
 // h <- bf16(h + C) and, when x is set, x <- bf16(x - dt h), for the 4 of the
 // 32 (row block, register) pairs wave w finishes; C's partial sums per wave
 // are in red. Every load of h and x is issued before the first store.
-__device__ __forceinline__ void residual_epilogue(const float (&red)[GEMM_WAVES][2][16][64], int n0, int rows, int N,
-                                                  const GemmOut& out) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int n = n0 + l32;
+// The h (and x) elements of the (block, register) pairs a wave finishes,
+// loaded up front: every load is issued (a row past `rows` reads row 0, in
+// bounds, and is zeroed), so they share the operand loads' round trip.
+struct ResidualRows {
     long long off[4];
     bool ok[4];
     float hv[4], xv[4];
+};
+__device__ __forceinline__ ResidualRows residual_rows(int n0, int rows, int N, const GemmOut& out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const int n = n0 + l32;
+    ResidualRows rr;
+    uint16_t hb[4], xb[4];
+    const uint16_t* xs = out.x ? out.x : out.h;     // no x: a second read of h, unused
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
         const int m = 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
-        ok[u] = m < rows;
-        off[u] = (long long)(ok[u] ? m : 0) * N + n;
-        hv[u] = ok[u] ? bf2f(out.h[off[u]]) : 0.f;
-        xv[u] = ok[u] && out.x ? bf2f(out.x[off[u]]) : 0.f;
+        rr.ok[u] = m < rows;
+        rr.off[u] = (long long)(rr.ok[u] ? m : 0) * N + n;
+        hb[u] = out.h[rr.off[u]];
+        xb[u] = xs[rr.off[u]];
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        rr.hv[u] = rr.ok[u] ? bf2f(hb[u]) : 0.f;
+        rr.xv[u] = rr.ok[u] && out.x ? bf2f(xb[u]) : 0.f;
+    }
+    return rr;
+}
+
+__device__ __forceinline__ void residual_epilogue(const float (&red)[GEMM_WAVES][2][16][64], const ResidualRows& rr,
+                                                  const GemmOut& out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     bool bad = false;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        if (!ok[u]) continue;
+        if (!rr.ok[u]) continue;
         const int idx = wave * 4 + u, blk = idx >> 4, r = idx & 15;
         float v = 0.f;
 #pragma unroll
         for (int ww = 0; ww < GEMM_WAVES; ++ww) v += red[ww][blk][r][lane];
-        const float hn = bf2f(f2bf(hv[u] + v));
-        out.h[off[u]] = f2bf(hn);
+        const float hn = bf2f(f2bf(rr.hv[u] + v));
+        out.h[rr.off[u]] = f2bf(hn);
         bad |= !finite_f(hn);
         if (out.x) {
-            const float xn = xv[u] - out.dt * hn;
+            const float xn = rr.xv[u] - out.dt * hn;
             bad |= !finite_f(xn);
-            out.x[off[u]] = f2bf(xn);
+            out.x[rr.off[u]] = f2bf(xn);
         }
     }
     if (out.nonfinite && __any(bad) && lane == 0) atomicOr(out.nonfinite, 1u);
