@@ -157,6 +157,37 @@ def test_single_layer_long_history_many_splits(splits, f32p):
     assert err <= BF16_REL
 
 
+# (layers, splits, fp32 partials): split counts at the edges of the combine's
+# choices on the long-history cache (6451 keys, where each count here is the
+# number of parts the call makes). bf16 partials: a wave merges up to 8
+# splits in a batch of 8, up to 16 in a batch of 16; past 16 two waves share
+# a slice, past 32 four; 68 splits leave 17 per wave, a second batch with one
+# real split. FP32 partials: batches of 8, two waves past 8, four past 16.
+# One layer merges in quarter-slices (a small launch), three in whole blocks.
+COMBINE_EDGES = [(1, 8, 0), (1, 9, 0), (1, 16, 0), (1, 17, 0), (1, 29, 0), (1, 34, 0), (1, 68, 0),
+                 (3, 9, 0), (3, 17, 0), (3, 68, 0),
+                 (1, 9, 1), (1, 16, 1), (1, 17, 1), (1, 34, 1), (3, 34, 1)]
+
+
+@pytest.mark.parametrize("layers,splits,f32p", COMBINE_EDGES)
+def test_combine_split_count_edges(layers, splits, f32p):
+    s = configs.LONG_18L.with_(name="lh_3L", cfg_id=49, num_layers=3)
+    _banner(f"combine edges: layers={layers} splits={splits} f32 partials={f32p}")
+    sc = Scenario(s)
+    for f in range(s.num_slots + 1):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s.with_(num_layers=layers), 1, 5)
+    out = sc.run_step(q, kd, vd, num_splits=splits, layer_begin=3 - layers, num_layers=layers, partials_f32=f32p)
+    worst = 0.0
+    for i in range(layers):
+        ck, cv = sc.cached_context(3 - layers + i)
+        ref = full_attention(synth.widen(q[i]), np.concatenate([ck, synth.widen(kd[i])]),
+                             np.concatenate([cv, synth.widen(vd[i])]), s.scale)
+        worst = max(worst, rel_err(out[i], ref))
+    _banner(f"  rel {worst:.3e}")
+    assert worst <= BF16_REL
+
+
 def test_attention_bf16_output_dtype():
     s = configs.PI05_1L
     sc = Scenario(s)
