@@ -304,8 +304,12 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int 
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = FUSED && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
+        // a row whose reference is still -inf has accumulated nothing (O = 0):
+        // on a wave's first tile the 128 accumulator products are skipped
+        if (!__all(m_run == -INFINITY)) {
 #pragma unroll
-        for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+            for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+        }
         m_run = m_new;
     }
     // p = 2^(scale log2e s - m): one FMA and the hardware exp2 (v_exp_f32);
