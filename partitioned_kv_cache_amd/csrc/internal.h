@@ -94,6 +94,18 @@ __device__ __forceinline__ bool finite_f(float x) { return (__float_as_uint(x) &
 // so the window is the leading `count` slots, except that a ring with a
 // spare slot (S = W + 1) leaves out slot `head`, the one a push may be
 // filling (physical slot order; softmax does not depend on key order).
+// One launch that copies both tensors' per-layer runs of a frame (or of the
+// pinned prefix) into the ring: for tensor t and layer l, `run` 16-byte
+// words from src[t] + l * run to dst[t] + l * dst_stride (ring.hip).
+typedef unsigned int word16 __attribute__((ext_vector_type(4)));   // one 16-byte word
+struct RunCopy {
+    const word16* src[2];
+    word16* dst[2];
+    long long run;          // 16-byte words per layer (a contiguous run in the source)
+    long long dst_stride;   // 16-byte words from one layer's run to the next in the ring
+};
+__global__ void copy_kv_runs(RunCopy c);
+
 struct KvSource {
     const void* ring_k;        // element 0 of layer `layer_begin`
     const void* ring_v;

@@ -19,6 +19,7 @@
 
 #include <stdarg.h>
 
+#include <algorithm>
 #include <new>
 
 #include "internal.h"
@@ -153,6 +154,57 @@ static pa_status copy_tokens(Ring* r, void* dst_base, const void* src, int64_t t
     return PA_OK;
 }
 
+// Workgroup (x, 2 l + t) of copy_kv_runs moves words [x * 1024, x * 1024 +
+// 1024) of tensor t's run in layer l, four per thread, all four loaded before
+// any is stored (a word past the run re-reads word 0 and is not stored). The
+// source is read once, so its loads are non-temporal; the stores stay cached
+// for the steps that read them next.
+constexpr int COPY_THREADS = 256, COPY_WORDS = 4;
+
+__global__ __launch_bounds__(COPY_THREADS) void pa::copy_kv_runs(RunCopy c) {
+    const int t = blockIdx.y & 1, l = blockIdx.y >> 1;
+    const word16* src = (t ? c.src[1] : c.src[0]) + (long long)l * c.run;
+    word16* dst = (t ? c.dst[1] : c.dst[0]) + (long long)l * c.dst_stride;
+    const long long base = (long long)blockIdx.x * (COPY_THREADS * COPY_WORDS) + threadIdx.x;
+    word16 w[COPY_WORDS];
+#pragma unroll
+    for (int u = 0; u < COPY_WORDS; ++u) {
+        const long long i = base + u * COPY_THREADS;
+        w[u] = __builtin_nontemporal_load(src + (i < c.run ? i : 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < COPY_WORDS; ++u) {
+        const long long i = base + u * COPY_THREADS;
+        if (i < c.run) dst[i] = w[u];
+    }
+}
+
+// tokens [tok0, tok0 + n) of every layer of both tensors from contiguous
+// [L][n][Hkv][D] sources; the 2-D copy engine path when a source is not
+// 16-byte aligned
+static pa_status copy_kv_tokens(Ring* r, const void* k, const void* v, int64_t tok0, int64_t n, hipStream_t s) {
+    const int64_t tok_bytes = (int64_t)r->cfg.num_kv_heads * r->cfg.head_dim * r->elem_bytes();
+    if (!aligned16(k) || !aligned16(v) || (n * tok_bytes) % 16 != 0 || tok_bytes % 16 != 0 ||
+        !aligned16(r->k) || !aligned16(r->v)) {
+        pa_status st = copy_tokens(r, r->k, k, tok0, n, s);
+        if (st != PA_OK) return st;
+        return copy_tokens(r, r->v, v, tok0, n, s);
+    }
+    RunCopy c;
+    c.src[0] = static_cast<const word16*>(k);
+    c.src[1] = static_cast<const word16*>(v);
+    c.dst[0] = reinterpret_cast<word16*>(static_cast<char*>(r->k) + tok0 * tok_bytes);
+    c.dst[1] = reinterpret_cast<word16*>(static_cast<char*>(r->v) + tok0 * tok_bytes);
+    c.run = n * tok_bytes / 16;
+    c.dst_stride = r->seq_len() * tok_bytes / 16;
+    const long long per_block = (long long)COPY_THREADS * COPY_WORDS;
+    const dim3 grid((unsigned)((c.run + per_block - 1) / per_block), 2u * (unsigned)r->cfg.num_layers);
+    copy_kv_runs<<<grid, COPY_THREADS, 0, s>>>(c);
+    PA_LAUNCHED();
+    return PA_OK;
+}
+
 extern "C" pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, int32_t n_tokens, void* stream) {
     clear_error();
     Ring* r = reinterpret_cast<Ring*>(ring);
@@ -163,9 +215,7 @@ extern "C" pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     pa_status st = refuse_capture(s, "rb_pin_prefix");
     if (st != PA_OK) return st;
-    st = copy_tokens(r, r->k, k, 0, n_tokens, s);
-    if (st != PA_OK) return st;
-    st = copy_tokens(r, r->v, v, 0, n_tokens, s);
+    st = copy_kv_tokens(r, k, v, 0, n_tokens, s);
     if (st != PA_OK) return st;
     r->pinned = n_tokens;
     return publish_state(r, s);
@@ -174,9 +224,7 @@ extern "C" pa_status rb_pin_prefix(rb_ring* ring, const void* k, const void* v, 
 // Copy a frame into slot `head` of every layer.
 static pa_status write_head_slot(Ring* r, const void* k, const void* v, hipStream_t s) {
     const int64_t tok0 = (int64_t)r->cfg.pin_capacity + (int64_t)r->head * r->cfg.tokens_per_frame;
-    pa_status st = copy_tokens(r, r->k, k, tok0, r->cfg.tokens_per_frame, s);
-    if (st != PA_OK) return st;
-    return copy_tokens(r, r->v, v, tok0, r->cfg.tokens_per_frame, s);
+    return copy_kv_tokens(r, k, v, tok0, r->cfg.tokens_per_frame, s);
 }
 
 // The frame in slot `head` joins the window; the oldest leaves it.

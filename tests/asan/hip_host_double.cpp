@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include "hip_host_double.h"
+#include "internal.h"       // the ring's run-copy kernel, which the double performs
 
 namespace dbl {
 HostDouble g;
@@ -52,7 +53,7 @@ hipError_t __hipPopCallConfiguration(dim3* grid, dim3* block, size_t* shmem, hip
     return hipSuccess;
 }
 
-hipError_t hipLaunchKernel(const void*, dim3 grid, dim3 block, void** args, size_t shmem, hipStream_t) {
+hipError_t hipLaunchKernel(const void* fn, dim3 grid, dim3 block, void** args, size_t shmem, hipStream_t) {
     g.launches += 1;
     g.last_grid = grid.x * (long long)grid.y * grid.z;
     g.last_block = block.x * (long long)block.y * block.z;
@@ -65,6 +66,16 @@ hipError_t hipLaunchKernel(const void*, dim3 grid, dim3 block, void** args, size
         g.last_ptr = *static_cast<void**>(args[0]);
         for (int i = 0; i < 3; ++i) g.last_int[i] = *static_cast<int*>(args[i + 1]);
         g.state_writes += 1;
+    }
+    // The ring's frame and prefix copies move bytes the driver checks: the
+    // double performs them, one run per (tensor, layer) the grid covers.
+    if (fn == reinterpret_cast<const void*>(&pa::copy_kv_runs) && args) {
+        const pa::RunCopy& c = *static_cast<const pa::RunCopy*>(args[0]);
+        for (unsigned y = 0; y < grid.y; ++y) {
+            const int t = y & 1, l = y >> 1;
+            memcpy(c.dst[t] + (long long)l * c.dst_stride, c.src[t] + (long long)l * c.run, (size_t)c.run * 16);
+        }
+        g.copies += 1;
     }
     return hipSuccess;
 }

@@ -53,7 +53,7 @@ def _build():
     for f in ("hip_host_double.cpp", "host_check.cpp"):
         o = os.path.join(OUT, f[:-4] + ".o")
         _run([HIPCC, "-x", "hip", "--cuda-host-only", "-O1", "-g", "-std=c++17", "-fPIC", *SAN,
-              "-I", os.path.join(ROOT, "include"), "-I", HERE, "-c", os.path.join(HERE, f), "-o", o])
+              "-I", os.path.join(ROOT, "include"), "-I", HERE, "-I", CSRC, "-c", os.path.join(HERE, f), "-o", o])
         objs.append(o)
     # each HIP translation unit names its (absent) device code object; point them all at the double's
     fatbins = sorted({l.split()[-1] for l in _run(["nm", "-u", *objs]).splitlines() if "__hip_fatbin_" in l})
