@@ -58,6 +58,36 @@ def test_ring_500_frames_wraps_and_counts():
                                "frames_pushed": 500}
 
 
+def _unaligned(a: np.ndarray, shift: int) -> torch.Tensor:
+    """A device view of `a` whose first element sits `shift` elements past a
+    16-byte boundary (the frame copy then takes the 2-D copy path)."""
+    t = dev(a).reshape(-1)
+    buf = torch.empty(t.numel() + shift, dtype=t.dtype, device="cuda")
+    buf[shift:].copy_(t)
+    return buf[shift:].view(a.shape)
+
+
+@pytest.mark.parametrize("shape", [configs.PI05_1L, configs.TINY], ids=lambda s: s.name)
+def test_push_and_pin_from_unaligned_sources(shape):
+    """Sources off a 16-byte boundary: ring bytes stay bit-exact (pin and
+    pushes past a wrap), alternating with aligned pushes."""
+    _banner(f"unaligned sources {shape.name}")
+    sc = Scenario(shape, pin_tokens=0)
+    if shape.pin_tokens:
+        pk, pv = synth.pin_kv(shape)
+        sc.ring.pin_prefix(_unaligned(pk, 1), _unaligned(pv, 1), shape.pin_tokens)
+        sc.model.pin(sc._words(pk), sc._words(pv))
+        sc.pin_k, sc.pin_v = pk, pv
+        sc.check_bytes()
+    for f in range(shape.num_slots + 3):
+        k, v = sc.frame_fn(f)
+        shift = f % 3          # 0: aligned (the kernel path), 1 and 2: not
+        ev = sc.ring.push_frame(_unaligned(k, shift) if shift else dev(k), _unaligned(v, shift) if shift else dev(v))
+        assert ev == sc.model.push(sc._words(k), sc._words(v))
+        sc._enter(f, k, v)
+        sc.check_bytes()
+
+
 # ------------------------------------------------------------- attention ----
 
 def test_attention_tiny_fp32_every_frame_and_step():
