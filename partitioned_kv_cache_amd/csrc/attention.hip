@@ -36,6 +36,20 @@ constexpr int N_XCD = 8;         // accelerator complex dies, one L2 each
 constexpr int ROWS_PER_WG = MFMA_WAVES * 32;
 constexpr float RESCALE_SLACK = 8.f;   // log2 units the running max may lag the true max
 constexpr int VALU_ROWS = 4;     // query rows per workgroup of the vector kernels
+// Launch shapes of the matrix-core partial kernel. The throughput form is 8
+// waves over 256 query rows. A launch that would leave CUs idle with it (a
+// single layer) runs 128-row workgroups instead, more of them, if they still
+// fit the chip at once (at most HALVES_MAX_WGS): with splits of at least
+// HALVES_MIN_TILES tiles, 8 waves as four row blocks x two key halves, each
+// half walking every other tile, merged through LDS; with shorter splits (in
+// launches of at most NARROW_MAX_WGS 256-row workgroups), 4 waves, one per
+// SIMD, since with one tile per wave the merge would cost more than the tile
+// it saves. The halves pay only through the extra workgroups: on a grid of
+// the same size (the 128 rows of the decode readers) the merge made the
+// launch slower.
+constexpr int HALVES_MIN_TILES = 4;
+constexpr int HALVES_MAX_WGS = 256;
+constexpr int NARROW_MAX_WGS = 64;
 
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -369,7 +383,12 @@ __device__ __forceinline__ void wait_vmem() {
 // WAVES: 8 (two per SIMD, the throughput form) or 4 (one per SIMD, for
 // launches too small to fill the chip: each wave's key loop then runs at the
 // single-wave rate).
-template <int D, bool FUSED = false, bool QPK = false, int WAVES = MFMA_WAVES, bool F32P = false>
+// KH: key halves per workgroup. With KH = 2 the waves form two groups of
+// WAVES / 2 over the same query rows; group h takes tiles h, h + 2, ... of
+// the split, and group 1 hands its (m, l, O) to group 0 through LDS at the
+// end, which merges the two and stores one partial. Each wave then walks half
+// the split's tiles, two waves per SIMD, without more partials to combine.
+template <int D, bool FUSED = false, bool QPK = false, int WAVES = MFMA_WAVES, bool F32P = false, int KH = 1>
 __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint16_t* __restrict__ q,
                                                                           long long q_layer, int hq, int group,
                                                                           int m_rows, KvSource src, int chunk,
@@ -382,11 +401,17 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     constexpr int PLANE = KT * 64;           // bytes per plane (KT keys x 32 dims x 2 B)
     constexpr int TILE = DB * PLANE;         // bytes per K or V tile
     constexpr int NBLK = TILE / 1024;        // 1 KB direct-to-LDS loads per tile and tensor
-    constexpr int DPW = (NBLK + WAVES - 1) / WAVES;   // loads per wave, per tile and tensor
-    constexpr int RPW = WAVES * 32;                   // query rows per workgroup
-    static_assert(NBLK % 2 == 0 && (NBLK <= WAVES || NBLK % WAVES == 0) && WAVES % 2 == 0, "tile / wave split");
+    constexpr int WR = WAVES / KH;                    // waves per key half, one 32-row block each
+    constexpr int DPW = (NBLK + WR - 1) / WR;         // loads per wave, per tile and tensor
+    constexpr int RPW = WR * 32;                      // query rows per workgroup
+    static_assert(NBLK % 2 == 0 && (NBLK <= WR || NBLK % WR == 0) && WR % 2 == 0, "tile / wave split");
+    static_assert(KH == 1 || (KH == 2 && !FUSED && D == 256 && WR * 32 * D * 4 <= 2 * NBUF * KH * TILE),
+                  "key halves: single-reader bf16 step, exchange fits the tile buffers");
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = KH == 1 ? 0 : wave / WR;     // key half (wave-uniform)
+    const int wr = KH == 1 ? wave : wave % WR;  // row block within the workgroup
     // XCD-aware placement. Workgroups go to the 8 XCDs round-robin by id, and
     // each XCD has its own L2. All row blocks of one (layer, split) read the
     // same keys, so they are given ids congruent mod 8: same XCD, same L2,
@@ -396,7 +421,7 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     if (unit >= parts * part.lg_count) return;                 // id padding, whole workgroup
     const int split = unit % parts, lg = unit / parts, rblk = slot % row_blocks;
     const int lb = lg / src.hkv, g = lg % src.hkv;
-    const int row0 = rblk * RPW + wave * 32;
+    const int row0 = rblk * RPW + wr * 32;
     const int row = row0 + l32;
     const bool active = row0 < m_rows;       // wave-uniform
 
@@ -442,19 +467,19 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     const int skip_at = pinned + src.window_skip(), skip_len = src.skip_len;   // in context-key units
 
     // Direct-to-LDS loads: one 1 KB load = 16 keys x 64 B of one plane, lane
-    // -> (key, 16-byte chunk). Wave w loads blocks w, w + WAVES, ... of a
-    // tile; block b is plane b / 2, keys 16 (b % 2) .. + 15. With an even wave
-    // count every block a wave loads has the same keys, so one address per
-    // tile serves.
+    // -> (key, 16-byte chunk). Wave w of a key half loads blocks w, w + WR,
+    // ... of that half's tile; block b is plane b / 2, keys 16 (b % 2) .. + 15.
+    // With an even wave count every block a wave loads has the same keys, so
+    // one address per tile serves.
     const int dma_key = lane >> 2, dma_pos = lane & 3;
-    const int kq = wave & 1;
+    const int kq = wr & 1;
     const int key_in_tile = kq * 16 + dma_key;
     const int kchunk = (dma_pos ^ ((key_in_tile >> 2) & 3)) << 3;   // K plane rotation
     // this lane's element offsets inside a tile whose keys are consecutive tokens
-    const int lane_k = key_in_tile * stride + (wave >> 1) * 32 + kchunk;
-    const int lane_v = key_in_tile * stride + (wave >> 1) * 32 + (dma_pos << 3);
+    const int lane_k = key_in_tile * stride + (wr >> 1) * 32 + kchunk;
+    const int lane_v = key_in_tile * stride + (wr >> 1) * 32 + (dma_pos << 3);
     auto issue_tile = [&](int t, char* kbuf, char* vbuf) {
-        if (DPW * WAVES > NBLK && wave >= NBLK) return;               // fewer blocks than waves
+        if (DPW * WR > NBLK && wr >= NBLK) return;                     // fewer blocks than waves
         const int j0 = k_begin + t * KT;                               // the tile's first key (uniform)
         const uint16_t* kp;
         const uint16_t* vp;
@@ -475,16 +500,16 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
             const int j = min(j0 + key_in_tile, k_end - 1);            // ragged tail: a valid key, masked later
             const bool dyn = j >= n_cached;
             const int tok = dyn ? j - n_cached : (j < pinned ? j : j + gap + (j >= skip_at ? skip_len : 0));
-            const int off = tok * stride + (wave >> 1) * 32;
+            const int off = tok * stride + (wr >> 1) * 32;
             kp = (dyn ? dk : rk) + off + kchunk;
             vp = (dyn ? dv : rv) + off + (dma_pos << 3);
         }
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
-            const int blk = __builtin_amdgcn_readfirstlane(wave + i * WAVES);
-            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(kp + i * (WAVES / 2) * 32),
+            const int blk = __builtin_amdgcn_readfirstlane(wr + i * WR);
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(kp + i * (WR / 2) * 32),
                                              (LDS_AS void*)(kbuf + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(vp + i * (WAVES / 2) * 32),
+            __builtin_amdgcn_global_load_lds((const GLB_AS void*)(vp + i * (WR / 2) * 32),
                                              (LDS_AS void*)(vbuf + blk * 1024), 16, 0, 0);
         }
     };
@@ -502,40 +527,82 @@ __global__ __launch_bounds__(WAVES * 64, MFMA_OCC) void partial_mfma(const uint1
     float m_run = -INFINITY, l_run = 0.f;
 
     const int n_tiles = (k_end - k_begin + KT - 1) / KT;
-    // Step through tile t held in ring buffer J: wait for its loads, meet at
-    // the barrier (which also frees buffer J - 1 for reuse), refill that
-    // buffer with tile t + NBUF - 1, then S = K Q^T, softmax, O += V P.
+    // Key half kh walks the split's tiles kh, kh + KH, ...: n_mine of them,
+    // in n_steps steps, the same count for every wave of the workgroup (the
+    // barriers below are met by all of them).
+    const int n_steps = (n_tiles + KH - 1) / KH;
+    const int n_mine = (n_tiles - kh + KH - 1) / KH;
+    // this half's region of each tile buffer
+    const int hoff = kh * TILE;
+    // Step through local tile t held in ring buffer J: wait for its loads,
+    // meet at the barrier (which also frees buffer J - 1 for reuse), refill
+    // that buffer with local tile t + NBUF - 1, then S = K Q^T, softmax, O += V P.
     auto step = [&](auto J_, int t) {
         constexpr int J = decltype(J_)::value;
         constexpr int JN = (J + NBUF - 1) % NBUF;
-        if (t >= n_tiles) return;
-        const int after = min(NBUF - 2, n_tiles - 1 - t);   // tiles issued after t
-        if (after >= 2)
-            wait_vmem<2 * 2 * DPW>();
-        else if (after == 1)
-            wait_vmem<2 * DPW>();
-        else
-            wait_vmem<0>();
+        if (t >= n_steps) return;
+        wait_vmem<0>();    // with two buffers no later tile of this wave is in flight yet
         __syncthreads();
-        if (t + NBUF - 1 < n_tiles) issue_tile(t + NBUF - 1, lds_buffer<JN, TILE>(), lds_buffer<NBUF + JN, TILE>());
-        if (active) {
+        if (t + NBUF - 1 < n_mine)
+            issue_tile((t + NBUF - 1) * KH + kh, lds_buffer<JN, KH * TILE>() + hoff,
+                       lds_buffer<NBUF + JN, KH * TILE>() + hoff);
+        if (active && t < n_mine) {
             bf16x8 pf[2];
-            const f32x16 sc = qk_scores<D>(lds_buffer<J, TILE>(), koff0, koff1, qf);
-            softmax_tile<D, FUSED>(sc, k_begin + t * KT, k_lim, hi, scale_log2, acc, m_run, l_run, pf, k_lim_wave);
-            pv_tile<D>(lds_buffer<NBUF + J, TILE>(), voff, pf, acc);
+            const f32x16 sc = qk_scores<D>(lds_buffer<J, KH * TILE>() + hoff, koff0, koff1, qf);
+            softmax_tile<D, FUSED>(sc, k_begin + (t * KH + kh) * KT, k_lim, hi, scale_log2, acc, m_run, l_run, pf,
+                                   k_lim_wave);
+            pv_tile<D>(lds_buffer<NBUF + J, KH * TILE>() + hoff, voff, pf, acc);
         }
     };
     // One tile in flight while one is consumed: two buffers measured faster
     // than three or four (fewer loads outstanding per CU) on every launch
     // shape here.
     static_assert(NBUF == 2, "the prologue and the unrolled loop below assume two buffers");
-    issue_tile(0, lds_buffer<0, TILE>(), lds_buffer<NBUF + 0, TILE>());
-    for (int t = 0; t < n_tiles; t += NBUF) {
+    if (n_mine > 0) issue_tile(kh, lds_buffer<0, KH * TILE>() + hoff, lds_buffer<NBUF + 0, KH * TILE>() + hoff);
+    for (int t = 0; t < n_steps; t += NBUF) {
         step(std::integral_constant<int, 0>{}, t);
         step(std::integral_constant<int, 1>{}, t + 1);
     }
 
     l_run += __shfl_xor(l_run, 32);
+    if constexpr (KH == 2) {
+        // Merge the two halves: half 1 writes its running (m, l) and its FP32
+        // accumulators into the (now idle) tile buffers, half 0 rescales both
+        // to the larger reference max and adds. 32 KB per wave: one whole
+        // K/V buffer object per row block.
+        __syncthreads();    // every wave is past its last tile
+        char* xb = wr == 0 ? lds_buffer<0, KH * TILE>()
+                 : wr == 1 ? lds_buffer<1, KH * TILE>()
+                 : wr == 2 ? lds_buffer<NBUF, KH * TILE>() : lds_buffer<NBUF + 1, KH * TILE>();
+        f32x4* xo = reinterpret_cast<f32x4*>(xb) + lane;
+        float2* xml = reinterpret_cast<float2*>(lds_buffer<2 * NBUF, WR * 64 * 8>()) + wr * 64 + lane;
+        if (kh == 1 && active) {
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xo[(b * 4 + j) * 64] = f32x4{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]};
+            *xml = make_float2(m_run, l_run);
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        if (active) {
+            const float2 ml1 = *xml;
+            const float mm = fmaxf(m_run, ml1.x);
+            const float mref = mm == -INFINITY ? 0.f : mm;     // neither half saw a key
+            const float a0 = __builtin_amdgcn_exp2f(m_run - mref), a1 = __builtin_amdgcn_exp2f(ml1.x - mref);
+            l_run = l_run * a0 + ml1.y * a1;
+            m_run = mm;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 x = xo[(b * 4 + j) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[b][4 * j + e] = acc[b][4 * j + e] * a0 + x[e] * a1;
+                }
+        }
+    }
     if (active) {       // whole 32-row block, fragment order: each store is contiguous across the wave
         // Non-temporal: the partials are read once, by the combine kernel,
         // which runs on other CUs (measured 1.5% faster than plain stores).
@@ -1031,25 +1098,33 @@ static pa_status launch_partials(const Ring* r, const Plan& p, const void* q, lo
     const float scale_log2 = scale * 1.4426950408889634f;
     const int d = r->cfg.head_dim;
     if (p.mfma) {
-        // A launch that leaves most CUs idle with 8-wave workgroups (the
-        // single-layer calls of the stack) runs 4-wave ones: one wave per
-        // SIMD, twice the workgroups, each key loop at the single-wave rate.
         const int units = p.parts * p.lg_count;
-        const bool narrow = d == 256 && !q2 && units * ((p.m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG) <= 64;
-        const int rpw = narrow ? ROWS_PER_WG / 2 : ROWS_PER_WG;
+        const int wide_wgs = units * ((p.m_rows + ROWS_PER_WG - 1) / ROWS_PER_WG);
+        const int half_wgs = units * ((p.m_rows + ROWS_PER_WG / 2 - 1) / (ROWS_PER_WG / 2));
+        const bool halves = d == 256 && !q2 && p.chunk >= HALVES_MIN_TILES * KT && half_wgs > wide_wgs &&
+                            half_wgs <= HALVES_MAX_WGS;
+        const bool narrow = d == 256 && !q2 && !halves && wide_wgs <= NARROW_MAX_WGS;
+        const int rpw = halves || narrow ? ROWS_PER_WG / 2 : ROWS_PER_WG;
+        const int threads = halves ? rpw * 4 : rpw * 2;
         const int row_blocks = (p.m_rows + rpw - 1) / rpw;
         const dim3 grid(((units + N_XCD - 1) / N_XCD) * N_XCD * row_blocks);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         const uint16_t* qq2 = static_cast<const uint16_t*>(q2);
 #define PA_MFMA_(DD, FU, QP, WV, FP, ...)                                                                     \
-    partial_mfma<DD, FU, QP, WV, FP, ##__VA_ARGS__><<<grid, rpw * 2, 0, stream>>>(                            \
+    partial_mfma<DD, FU, QP, WV, FP, ##__VA_ARGS__><<<grid, threads, 0, stream>>>(                            \
         qq, q_layer, hq, p.group, p.m_rows, src, p.chunk, scale_log2, part, p.parts, row_blocks, qq2, q2_layer, m1)
 #define PA_MFMA(DD, FU, QP, ...) PA_MFMA_(DD, FU, QP, ##__VA_ARGS__)
         // FP32 partial O (optional, single-reader steps): the same kernels
         // with wider partial stores; the combine reads FP32 partials
         const bool f32p = p.o_bytes == 4;
         if (f32p && q2) return fail(PA_EINVAL, "FP32 partials are for the single-reader step");
-        if (narrow) {
+        if (halves) {
+            if (f32p) {
+                if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES, true, 2);
+                else PA_MFMA(256, false, false, MFMA_WAVES, true, 2);
+            } else if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES, false, 2);
+            else PA_MFMA(256, false, false, MFMA_WAVES, false, 2);
+        } else if (narrow) {
             if (f32p) {
                 if (q_packed) PA_MFMA(256, false, true, MFMA_WAVES / 2, true);
                 else PA_MFMA(256, false, false, MFMA_WAVES / 2, true);

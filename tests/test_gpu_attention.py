@@ -187,6 +187,32 @@ def test_single_layer_long_history_many_splits(splits, f32p):
     assert err <= BF16_REL
 
 
+@pytest.mark.parametrize("frames,splits,f32p", [(4, 22, 0), (4, 22, 1), (3, 10, 0)])
+def test_single_layer_key_halves_ragged_splits(frames, splits, f32p):
+    """A single layer of the long-history cache runs 128-row workgroups in
+    two key halves that take alternate tiles and merge through LDS. These
+    fills and split counts give every split an odd tile count (5 or 9: the
+    halves walk 3 and 2, or 5 and 4 tiles) and leave a last split of 19 keys,
+    one ragged tile, so that its second half sees no key at all."""
+    s = configs.LONG_18L.with_(name="lh_1L", cfg_id=48, num_layers=3)
+    total = s.pin_tokens + frames * s.tokens_per_frame + s.n_dyn
+    chunk = -(-(-(-total // splits)) // 32) * 32
+    parts = -(-total // chunk)
+    assert chunk // 32 in (5, 9) and total - (parts - 1) * chunk == 19      # the shapes named above
+    _banner(f"key halves: frames={frames} splits={splits} ({parts} parts of {chunk} keys) f32 partials={f32p}")
+    sc = Scenario(s)
+    for f in range(frames):
+        sc.push(f)
+    q, kd, vd = synth.suffix_qkv(s.with_(num_layers=1), frames, 1)
+    out = sc.run_step(q, kd, vd, num_splits=splits, layer_begin=1, num_layers=1, partials_f32=f32p)
+    ck, cv = sc.cached_context(1)
+    ref = full_attention(synth.widen(q[0]), np.concatenate([ck, synth.widen(kd[0])]),
+                         np.concatenate([cv, synth.widen(vd[0])]), s.scale)
+    err = rel_err(out[0], ref)
+    _banner(f"  rel {err:.3e}")
+    assert err <= BF16_REL
+
+
 # (layers, splits, fp32 partials): split counts at the edges of the combine's
 # choices on the long-history cache (6451 keys, where each count here is the
 # number of parts the call makes). bf16 partials: a wave merges up to 8
