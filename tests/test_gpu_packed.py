@@ -141,6 +141,10 @@ CASES = {
     "full_51x1024_ffn4096": (configs.PI05_18L_FFN.with_(name="pk_d", cfg_id=913, num_layers=3), 3, True, True),
     "full_33x512_ffn3072": (configs.PI05_18L_FFN.with_(name="pk_e", cfg_id=914, num_layers=2, n_dyn=33,
                                                        model_dim=512, ffn_dim=3072), 2, True, False),
+    # the long-history cache (6,400 cached keys per layer, wrapped once): each
+    # layer's attention runs the key-halves launch, with Q in operand order
+    # (packed) and token-major (unpacked)
+    "long_51x1024": (configs.LONG_18L_FULL.with_(name="pk_f", cfg_id=915, num_layers=2), 9, False, True),
 }
 
 
