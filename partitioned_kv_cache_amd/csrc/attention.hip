@@ -329,14 +329,19 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int base, int k_end, int 
     // p = 2^(scale log2e s - m): one FMA and the hardware exp2 (v_exp_f32);
     // results below 2^-126 flush to zero, far below what a bf16 P can carry.
     const float m_e = FUSED ? fmaxf(m_run, -3.0e38f) : m_run;   // a row with nothing yet: p = 0
-    float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_e));
-        psum += p;
-        pf[r >> 3][r & 7] = (__bf16)p;
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_e));
+    // The row sum is taken over the rounded P that the P.V product uses, two
+    // values per instruction (a bf16 dot product against (1, 1), FP32 sum),
+    // in two chains.
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[0][2 * i], pf[0][2 * i + 1]}, one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[1][2 * i], pf[1][2 * i + 1]}, one, ps1, false);
     }
-    l_run += psum;
+    l_run += ps0 + ps1;
 }
 
 // O^T += V^T P^T for one tile (16 MFMAs; V^T straight from the token-major
